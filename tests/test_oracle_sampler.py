@@ -1,0 +1,175 @@
+"""Pins for the oracle's sampler: schedule closed form, exact stop steps, invariants, statistics."""
+import math
+
+import numpy as np
+import pytest
+from scipy import special
+
+from oracle import philox, sampler
+
+
+def cfg(**kw):
+    base = dict(max_steps=48, temp_start=0.8, temp_end=0.4, commit_per_step=16, renoise_conf=0.1,
+                stable_steps=2, entropy_stop=-1.0, renoise_committed=True, seed=1234)
+    base.update(kw)
+    return sampler.SamplerConfig(**base)
+
+
+def test_temperature_schedule_closed_form():
+    c = cfg()
+    T = [sampler.temperature(c, s) for s in range(48)]
+    assert T[0] == np.float32(0.8) and T[47] == np.float32(0.4)
+    assert all(a > b for a, b in zip(T, T[1:]))
+    for s in (1, 10, 23, 46):
+        assert T[s] == np.float32(0.8 - 0.4 * s / 47)
+    assert all(t.dtype == np.float32 for t in T)
+
+
+def test_row_stats_against_library_and_bruteforce():
+    V, n = 37, 5
+    r = np.random.default_rng(0)
+    z = r.standard_normal((n, V)) * 3
+    x = r.integers(0, V, n)
+    T = np.float32(0.65)
+    pos = np.arange(100, 100 + n)
+    st = sampler.row_stats(z, x, T, 42, 1, pos, 3)
+    t = z.astype(np.float32) / T
+    lse = special.logsumexp(t.astype(np.float64), axis=1)
+    p = special.softmax(t.astype(np.float64), axis=1)
+    ent = -(p * np.log(p)).sum(1)
+    assert np.allclose(st["lse"], lse, rtol=1e-6)
+    assert np.allclose(st["entropy"], ent, atol=1e-5)
+    for i in range(n):
+        g = philox.gumbel_row(42, 1, int(pos[i]), 3, V)
+        sc = [float(np.float32(t[i, v]) + np.float32(g[v])) for v in range(V)]
+        best = max(range(V), key=lambda v: (sc[v], -v))
+        assert st["cand"][i] == best
+        assert st["t_cand"][i] == t[i, best] and st["t_cur"][i] == t[i, x[i]]
+        s2 = sorted(sc)
+        assert np.isclose(st["margin"][i], s2[-1] - s2[-2], atol=1e-6)
+
+
+def _run(z_fn, c, C=256, V=1024, L=64, x0=None):
+    pos = L + np.arange(C)
+    x = sampler.canvas_init(c.seed, 0, pos, V) if x0 is None else x0.copy()
+    com = np.zeros(C, bool)
+    sr = 0
+    hist = []
+    for s in range(c.max_steps):
+        st = sampler.row_stats(z_fn(s, x), x, sampler.temperature(c, s), c.seed, 0, pos, s)
+        x_new, com_new, sr, status = sampler.sample_commit(st, x, com, sr, c, s, 0, pos, V)
+        hist.append((x.copy(), com.copy(), x_new.copy(), com_new.copy(), status, st))
+        x, com = x_new, com_new
+        if status["stop"]:
+            break
+    return x, com, hist
+
+
+def test_peaked_logits_stop_after_three_steps():
+    """z = 50 * onehot(target): every draw is the target, confidence ~1, the canvas changes only
+    at step 0, so the run stops after step 2 with 48 committed and canvas == targets."""
+    V = 1024
+    target = np.random.default_rng(1).integers(0, V, 256)
+    z = np.zeros((256, V))
+    z[np.arange(256), target] = 50.0
+    x, com, hist = _run(lambda s, x: z, cfg(), V=V)
+    assert len(hist) == 3
+    assert np.array_equal(x, target)
+    assert com.sum() == 48
+    assert [h[4]["changed"] for h in hist] == [1, 0, 0]
+    assert np.array_equal(np.nonzero(hist[0][3])[0], np.arange(16))  # ties → lowest index
+
+
+def test_fixed_commit_schedule_without_renoise_of_committed():
+    """Random logits, committed tokens never re-noised: 16 commits per step, all 256 committed
+    after step 15, then two unchanged steps → 18 steps."""
+    V = 1024
+    r = np.random.default_rng(2)
+    zs = r.standard_normal((48, 256, V))
+    x, com, hist = _run(lambda s, x: zs[s], cfg(renoise_committed=False), V=V)
+    assert len(hist) == 18
+    assert [int(h[3].sum()) for h in hist[:16]] == [16 * (i + 1) for i in range(16)]
+    assert com.all()
+    assert [h[4]["changed"] for h in hist[-3:]] == [1, 0, 0]
+
+
+def test_commit_count_and_fixed_committed_invariants():
+    V = 1024
+    r = np.random.default_rng(3)
+    target = r.integers(0, V, 256)
+
+    def z_fn(s, x):  # mixed: half the rows peaked, half random → some keep, some re-noise
+        z = r.standard_normal((256, V))
+        z[np.arange(0, 256, 2), target[::2]] = 12.0
+        return z
+
+    c = cfg()
+    _, _, hist = _run(z_fn, c, V=V)
+    for x0, c0, x1, c1, status, st in hist:
+        U = int((~c0).sum())
+        renoised_committed = int((c0 & ~c1).sum())
+        assert c1.sum() == c0.sum() - renoised_committed + min(16, U)
+        # a committed position keeps its token unless it was re-noised (then it is uncommitted)
+        kept = c0 & c1
+        assert np.array_equal(x0[kept], x1[kept])
+        # re-noised committed positions got the step's fresh token
+        drop = c0 & ~c1
+        if drop.any():
+            s = status
+        # newly committed positions hold their candidate
+        new = ~c0 & c1
+        assert np.array_equal(x1[new], st["cand"][new])
+        assert new.sum() == min(16, U)
+
+
+def test_selection_is_topm_by_confidence():
+    V, C = 64, 40
+    r = np.random.default_rng(4)
+    st = {"cand": r.integers(0, V, C).astype(np.int32),
+          "t_cand": np.round(r.standard_normal(C), 1).astype(np.float32),  # ties
+          "t_cur": r.standard_normal(C).astype(np.float32),
+          "lse": np.zeros(C, np.float32), "entropy": np.ones(C, np.float32),
+          "margin": np.ones(C, np.float32)}
+    com = np.zeros(C, bool)
+    com[::3] = True
+    x = r.integers(0, V, C).astype(np.int32)
+    c = cfg(commit_per_step=5)
+    _, _, _, status = sampler.sample_commit(st, x, com, 0, c, 0, 0, np.arange(C), V)
+    U = [i for i in range(C) if not com[i]]
+    want = sorted(U, key=lambda i: (-float(st["t_cand"][i]), i))[:5]
+    assert list(status["selected"]) == want
+
+
+def test_same_seed_same_trajectory_and_seed_matters():
+    V = 1024
+    zs = np.random.default_rng(5).standard_normal((48, 256, V))
+    a = _run(lambda s, x: zs[s], cfg(max_steps=6), V=V)
+    b = _run(lambda s, x: zs[s], cfg(max_steps=6), V=V)
+    c = _run(lambda s, x: zs[s], cfg(max_steps=6, seed=99), V=V)
+    assert np.array_equal(a[0], b[0]) and len(a[2]) == len(b[2]) == 6
+    assert not np.array_equal(a[0], c[0])
+
+
+def test_step_cap_stops():
+    V = 1024
+    zs = np.random.default_rng(6).standard_normal((5, 256, V))
+    _, _, hist = _run(lambda s, x: zs[s], cfg(max_steps=5), V=V)
+    assert len(hist) == 5 and hist[-1][4]["stop"] == 1
+
+
+def test_entropy_stop_optional():
+    V = 1024
+    target = np.random.default_rng(7).integers(0, V, 256)
+    z = np.zeros((256, V))
+    z[np.arange(256), target] = 50.0
+    # entropy ~0 and unchanged at step 1 → stops one step earlier than the stable-run rule
+    _, _, hist = _run(lambda s, x: z, cfg(entropy_stop=0.005), V=V)
+    assert len(hist) == 2
+    _, _, hist = _run(lambda s, x: z, cfg(entropy_stop=0.005, stable_steps=5), V=V)
+    assert len(hist) == 2
+
+
+def test_canvas_init_is_uniform_and_positional():
+    a = sampler.canvas_init(3, 0, np.arange(256), 1024)
+    b = sampler.canvas_init(3, 0, np.arange(256, 512), 1024)
+    assert a.min() >= 0 and a.max() < 1024 and (a != b).mean() > 0.9
