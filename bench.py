@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the denoise step: canvas positions/s and ms per step on one MI355X.
+
+Workload (default "full_canvas_loop"): the 12-layer MoE model (d 2048, 16 q / 8 kv heads,
+head_dim 128, 64 experts top-4, d_ff 768, shared SwiGLU FFN 4096, vocab 65536), a prefix of 2048
+random tokens prefilled causally (untimed), and one 256-token canvas run through the sampling
+schedule (48-step cap, temperature 0.8 -> 0.4, commit 16, re-noise below 0.1).  A step is one
+dg_denoise_step (embedding, 12 layers, final norm, fused vocab head) plus one dg_sample_commit;
+steps cycle through the 48-step schedule (the canvas restarts after the cap).  Weights and
+tokens are seeded synthetic data (no checkpoint exists), drawn on the device.
+
+Output: one JSON line with the metric, a roofline entry for the dominant kernel (the expert
+gate/up grouped GEMM, measured live with HIP events on its launch stream) and the CPU oracle
+timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+SEED = 20260610
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def expert_gemm1_bytes(shape, routes: int, experts_touched: int) -> float:
+    """Algorithmic HBM bytes of one gate/up expert GEMM launch: each touched expert's gate and up
+    matrices once, each routed row's activations once, the SwiGLU output once."""
+    w = experts_touched * 2 * shape.d_ff_expert * shape.d_model * 2
+    x = routes * shape.d_model * 2
+    out = routes * shape.d_ff_expert * 2
+    return float(w + x + out)
+
+
+def _host(t):
+    import torch
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def cpu_baseline(shape, weights, prefix_len: int, sample_rows: int):
+    """The CPU oracle, as it stands, on a bounded sample of one step: layer 0 over the 256 canvas
+    rows (synthetic residual state and random bf16 prefix K/V), the fused head on `sample_rows`
+    rows, and the sampler on 256 positions; scaled to a full step (n_layers layers, 256 head rows).
+    The oracle gets the same synthetic weights the GPU uses (copied from the device RNG draw)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from block_discrete_diffusion_amd import synth
+    from oracle import model as om
+    from oracle import sampler as osm
+
+    d, D, V = shape.d_model, shape.head_dim, shape.vocab
+    lw = {k: _host(v) for k, v in weights["layers"][0].items()}
+    k = synth.bf16_normal((shape.n_kv_heads, prefix_len, D), SEED, 101)
+    v = synth.bf16_normal((shape.n_kv_heads, prefix_len, D), SEED, 102)
+    h = synth.hidden(256, d, SEED, 103)
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        om.layer(h, lw, shape, prefix_len + np.arange(256), k, v, None)
+    t_layer = (time.perf_counter() - t0) / reps
+    del lw
+    head = _host(weights["lm_head"])
+    f = synth.bf16_normal((sample_rows, d), SEED, 104)
+    x = synth.tokens(sample_rows, V, SEED, 105)
+    cfg = osm.SamplerConfig(seed=1)
+    t0 = time.perf_counter()
+    z = om.head_logits(f, head)
+    st = osm.row_stats(z, x, osm.temperature(cfg, 0), cfg.seed, 0, prefix_len + np.arange(sample_rows), 0)
+    t_head = (time.perf_counter() - t0) * 256 / sample_rows
+    full = {kk: np.resize(vv, 256) for kk, vv in st.items()}
+    t0 = time.perf_counter()
+    osm.sample_commit(full, synth.tokens(256, V, SEED, 106), np.zeros(256, bool), 0, cfg, 0, 0,
+                      prefix_len + np.arange(256), V)
+    t_samp = time.perf_counter() - t0
+    t_step = shape.n_layers * t_layer + t_head + t_samp
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": 256.0 / t_step, "unit": "canvas positions/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle: 1 layer x 256 canvas rows (prefix {prefix_len}, mean of {reps}) "
+                   f"scaled x{shape.n_layers}, "
+                   f"head + Gumbel row stats on {sample_rows} rows scaled x{256 // sample_rows}, sampler on 256; "
+                   f"est. {t_step * 1e3:.0f} ms/step (layer {t_layer * 1e3:.0f} ms, head {t_head * 1e3:.0f} ms, "
+                   f"sampler {t_samp * 1e3:.1f} ms); host affinity {len(os.sched_getaffinity(0))} cpus"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="skip the HIP-event per-kernel pass (e.g. under a profiler)")
+    ap.add_argument("--cpu-sample-rows", type=int, default=64)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}). "
+              "Requests shard across GPUs with no exchange; see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_discrete_diffusion_amd import dg, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    shape = synth.FULL
+    prefix_len = 2048
+    log("drawing weights on the device")
+    w = synth.torch_model_weights(shape, "cuda", SEED)
+    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=2048)
+    kv = dg.KV(shape, 1, prefix_len + shape.canvas)
+    prefix = torch.from_numpy(synth.tokens(prefix_len, shape.vocab, SEED, 1)).cuda()
+    log("prefill")
+    m.prefill(prefix, [prefix_len], kv)
+    torch.cuda.synchronize()
+    cfg = dg.sampler_cfg(seed=SEED)
+    st = dg.Canvas(1, shape.canvas)
+    stats = dg.Stats(1, shape.canvas)
+    status = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    m.canvas_init(st, kv, cfg)
+    counter = {"s": 0}
+
+    def step():
+        s = counter["s"]
+        if s == cfg.max_steps:
+            m.canvas_init(st, kv, cfg)
+            s = 0
+        m.denoise_step(st.tokens, kv, cfg, s, stats)
+        m.sample_commit(st, stats, cfg, s, kv, status)
+        counter["s"] = s + 1
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    value = shape.canvas / (ms * 1e-3)
+
+    roofline = None
+    kernels = None
+    if not args.no_kernel_timing:
+        m.timing(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        kt = m.timing_read()
+        m.timing(False)
+        kernels = {k: round(v["total_ms"] / args.steps * 1e3, 2) for k, v in kt.items()}  # us per step
+        g1 = kt["moe_gemm1_swiglu"]
+        routes = shape.canvas * shape.top_k
+        nbytes = expert_gemm1_bytes(shape, routes, shape.n_experts)
+        ach = nbytes / (g1["avg_ms"] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "moe_gemm1_swiglu", "achieved": round(ach, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": None, "avg_launch_us": round(g1["avg_ms"] * 1e3, 2),
+                    "algorithmic_bytes_per_launch": nbytes}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline (bounded sample)")
+        cpu = cpu_baseline(shape, w, prefix_len, args.cpu_sample_rows)
+    out = {
+        "metric": "canvas positions/s (denoise step, 1 GPU)", "value": round(value, 1),
+        "unit": "canvas positions/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded device RNG weights, uniform random tokens)",
+        "config": {"workload": "full_canvas_loop: 12 layers d2048 16q/8kv hd128, 64 experts top-4 "
+                               "d_ff 768 + shared FFN 4096, vocab 65536, prefix 2048, canvas 256, "
+                               "sampler 48 steps 0.8->0.4 commit 16",
+                   "global_batch": 1, "seq_len": prefix_len + shape.canvas, "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernel_us_per_step": kernels,
+        "wall_s_timed": round(t_wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+    m.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,599 @@
+// libdg C ABI: argument validation, workspace, and the launch sequence of each entry point.
+// See include/dg.h for the contract of every function.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dg.h"
+#include "dg_kernels.h"
+
+using namespace dg;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct Buf {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+}  // namespace
+
+struct dg_ctx {
+  dg_model_desc m{};
+  dg_weights w{};
+  std::vector<dg_layer_weights> layers;
+  int max_batch = 0, max_prefill = 0;
+  int r_canvas = 0;  // max_batch * canvas
+  int r_max = 0;     // max(r_canvas, max_prefill)
+  int part_cap = 0;  // (row, head, split) slots of the attention partial buffers
+  std::string err;
+  std::vector<void*> allocs;
+
+  // measurement: HIP events around launches (dg_timing_enable)
+  struct Rec {
+    const char* name;
+    hipEvent_t a, b;
+  };
+  bool timing = false;
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t event() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    (void)hipEventCreate(&e);
+    return e;
+  }
+
+  // workspace
+  float* h = nullptr;          // [r_max][d]
+  uint16_t* a = nullptr;       // [r_max][d]
+  float* qkv = nullptr;        // [r_max][(Hq+2Hkv)D]
+  uint16_t* q = nullptr;       // [r_max][Hq D]
+  uint16_t* attn = nullptr;    // [r_max][Hq D]
+  float* part_o = nullptr;     // [part_cap][D]
+  float* part_ml = nullptr;    // [part_cap][2]
+  int32_t* eidx = nullptr;     // [r_max][k]
+  float* gates = nullptr;      // [r_max][k]
+  int32_t* offs = nullptr;     // [E+1]
+  int32_t* perm = nullptr;     // [r_max*k]
+  int32_t* inv = nullptr;      // [r_max*k]
+  uint16_t* act = nullptr;     // [r_max*k][F]
+  float* y = nullptr;          // [r_max*k][d]
+  uint16_t* sact = nullptr;    // [r_max][Fs]
+  uint16_t* f = nullptr;       // [r_canvas][d]
+  float* head_part = nullptr;  // [r_canvas][V/64][8]
+  uint16_t* ck = nullptr;      // [L][max_batch][Hkv][C][D]
+  uint16_t* cv = nullptr;
+
+  int fail(int code, const std::string& msg) {
+    err = msg;
+    return code;
+  }
+  template <typename T>
+  bool alloc(T** out, size_t count) {
+    void* p = nullptr;
+    if (count == 0) count = 1;
+    if (hipMalloc(&p, count * sizeof(T)) != hipSuccess) return false;
+    allocs.push_back(p);
+    *out = static_cast<T*>(p);
+    return true;
+  }
+  ~dg_ctx() {
+    for (auto& r : recs) {
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
+    }
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+    for (void* p : allocs) (void)hipFree(p);
+  }
+};
+
+namespace {
+
+constexpr int kMaxSplit = 16;
+constexpr int kHeadSlice = 64;  // vocab entries per head partial (half the 128-wide tile)
+
+// Run `launch` (one or more kernel launches on stream s); with timing on, bracket it by events.
+template <typename F>
+void timed(dg_ctx* c, const char* name, hipStream_t s, F&& launch) {
+  if (!c->timing) {
+    launch();
+    return;
+  }
+  hipEvent_t a = c->event(), b = c->event();
+  (void)hipEventRecord(a, s);
+  launch();
+  (void)hipEventRecord(b, s);
+  c->recs.push_back({name, a, b});
+}
+
+long kv_layer_stride(const dg_model_desc& m, int batch, int cap) {
+  return static_cast<long>(batch) * m.n_kv_heads * cap * m.head_dim;
+}
+
+int check_hip(dg_ctx* c, const char* where) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    return c->fail(DG_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+  }
+  return DG_OK;
+}
+
+std::string validate_desc(const dg_model_desc& m) {
+  char buf[256];
+  auto bad = [&](const char* what) {
+    snprintf(buf, sizeof buf, "unsupported model shape: %s", what);
+    return std::string(buf);
+  };
+  if (m.n_layers < 1) return bad("n_layers < 1");
+  if (m.head_dim != 64 && m.head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (m.n_q_heads < 1 || m.n_kv_heads < 1 || m.n_q_heads % m.n_kv_heads) return bad("n_q_heads % n_kv_heads");
+  if (m.d_model < 64 || m.d_model % 64 || m.d_model > 4096) return bad("d_model: multiple of 64, <= 4096");
+  if ((m.n_q_heads * m.head_dim) % 64) return bad("n_q_heads*head_dim % 64");
+  if (m.n_experts < 1 || m.n_experts > 64) return bad("n_experts in [1, 64]");
+  if (m.top_k < 1 || m.top_k > m.n_experts) return bad("top_k in [1, n_experts]");
+  if (m.d_ff_expert < 64 || m.d_ff_expert % 64) return bad("d_ff_expert % 64");
+  if (m.d_ff_shared < 0 || m.d_ff_shared % 64) return bad("d_ff_shared % 64");
+  if (m.vocab < 128 || m.vocab % 128) return bad("vocab % 128");
+  if (m.canvas != 256) return bad("canvas must be 256");
+  if (!(m.rms_eps > 0.f) || !(m.rope_theta >= 0.f)) return bad("rms_eps > 0, rope_theta >= 0");
+  return "";
+}
+
+RowMap make_map(int rows_per_req, int n_req, const int32_t* pos0) {
+  RowMap r{};
+  r.rows_per_req = rows_per_req;
+  r.n_req = n_req;
+  for (int b = 0; b < n_req; ++b) r.pos0[b] = pos0 ? pos0[b] : 0;
+  return r;
+}
+
+int choose_split(const dg_ctx* c, int base_wgs, int n_keys, int rows) {
+  int ns = std::max(1, std::min(kMaxSplit, (1024 + base_wgs - 1) / base_wgs));
+  ns = std::min(ns, std::max(1, (n_keys + 63) / 64));
+  ns = std::min(ns, std::max(1, c->part_cap / std::max(1, rows * c->m.n_q_heads)));
+  return ns;
+}
+
+// One decoder layer over `rows` rows (n_req requests of rows_per_req rows each).
+// Denoise mode: K/V of the rows go to the canvas scratch; keys = cache[0:len) + canvas.
+// Prefill mode (one request): K/V go to the cache at len..; keys = cache[0:len+rows), causal.
+void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len, bool prefill,
+               uint16_t* kc_l, uint16_t* vc_l, int cap, const dg_debug* dbg, hipStream_t s) {
+  const dg_model_desc& m = c->m;
+  const dg_layer_weights& lw = c->layers[l];
+  const int rows = n_req * rows_per_req;
+  const int d = m.d_model, Hq = m.n_q_heads, Hkv = m.n_kv_heads, D = m.head_dim;
+  const int nqkv = (Hq + 2 * Hkv) * D;
+  const RowMap map = make_map(rows_per_req, n_req, len);
+
+  timed(c, "rmsnorm", s, [&] { launch_rmsnorm(c->h, lw.attn_norm, m.rms_eps, c->a, rows, d, s); });
+
+  GemmArgs g{};
+  g.x = c->a; g.ldx = d; g.n_tok = rows;
+  g.seg_w[0] = lw.wq; g.seg_w[1] = lw.wk; g.seg_w[2] = lw.wv;
+  g.seg_start[0] = 0; g.seg_start[1] = Hq * D; g.seg_start[2] = (Hq + Hkv) * D; g.seg_start[3] = nqkv;
+  g.n_seg = 3; g.K = d; g.N = nqkv; g.out_f32 = c->qkv; g.ldo = nqkv;
+  timed(c, "gemm_qkv", s, [&] { launch_gemm(g, EPI_STORE_F32, s); });
+
+  RopeArgs ra{};
+  ra.qkv = c->qkv; ra.rows = rows; ra.Hq = Hq; ra.Hkv = Hkv; ra.D = D; ra.theta = m.rope_theta;
+  ra.q = c->q; ra.map = map;
+  const long ck_layer = static_cast<long>(l) * c->max_batch * Hkv * m.canvas * D;
+  if (prefill) {
+    ra.k_dst = kc_l; ra.v_dst = vc_l; ra.kv_cap = cap;
+    for (int b = 0; b < n_req; ++b) ra.slot0[b] = len[b];
+  } else {
+    ra.k_dst = c->ck + ck_layer; ra.v_dst = c->cv + ck_layer; ra.kv_cap = m.canvas;
+    for (int b = 0; b < n_req; ++b) ra.slot0[b] = 0;
+  }
+  timed(c, "rope_scatter", s, [&] { launch_rope_scatter(ra, s); });
+
+  AttnArgs at{};
+  at.q = c->q; at.out = c->attn; at.kc = kc_l; at.vc = vc_l; at.cap = cap;
+  at.kx = c->ck + ck_layer; at.vx = c->cv + ck_layer; at.xcap = m.canvas;
+  at.Hq = Hq; at.Hkv = Hkv; at.D = D; at.rows_per_req = rows_per_req; at.n_req = n_req;
+  int max_keys = 0;
+  for (int b = 0; b < n_req; ++b) {
+    at.n_cache[b] = prefill ? len[b] + rows_per_req : len[b];
+    at.q_pos0[b] = len[b];
+    max_keys = std::max(max_keys, at.n_cache[b] + (prefill ? 0 : m.canvas));
+  }
+  at.n_extra = prefill ? 0 : m.canvas;
+  at.causal = prefill ? 1 : 0;
+  at.scale = 1.0f / std::sqrt(static_cast<float>(D));
+  const int tasks = (Hq / Hkv) * ((rows_per_req + 31) / 32);
+  const int base = ((tasks + 3) / 4) * n_req * Hkv;
+  at.n_split = choose_split(c, base, max_keys, rows);
+  at.split_keys = (((max_keys + at.n_split - 1) / at.n_split + 63) / 64) * 64;
+  at.n_split = (max_keys + at.split_keys - 1) / at.split_keys;
+  at.part_o = c->part_o; at.part_ml = c->part_ml;
+  timed(c, "attention", s, [&] { launch_attention(at, s); });
+  if (dbg && dbg->attn_out)
+    (void)hipMemcpyAsync(dbg->attn_out + static_cast<long>(l) * rows * Hq * D, c->attn,
+                         sizeof(uint16_t) * rows * Hq * D, hipMemcpyDeviceToDevice, s);
+
+  GemmArgs go{};
+  go.x = c->attn; go.ldx = Hq * D; go.n_tok = rows; go.w0 = lw.wo; go.K = Hq * D; go.N = d;
+  go.out_f32 = c->h; go.ldo = d;
+  timed(c, "gemm_o_residual", s, [&] { launch_gemm(go, EPI_ADD_F32, s); });
+  if (dbg && dbg->h_mid)
+    (void)hipMemcpyAsync(dbg->h_mid + static_cast<long>(l) * rows * d, c->h,
+                         sizeof(float) * rows * d, hipMemcpyDeviceToDevice, s);
+
+  timed(c, "norm_router_topk", s, [&] { launch_norm_router(c->h, lw.ffn_norm, m.rms_eps, lw.w_router, rows, d, m.n_experts, m.top_k,
+                     c->a, c->eidx, c->gates, s); });
+  if (dbg && dbg->expert_idx)
+    (void)hipMemcpyAsync(dbg->expert_idx + static_cast<long>(l) * rows * m.top_k, c->eidx,
+                         sizeof(int32_t) * rows * m.top_k, hipMemcpyDeviceToDevice, s);
+  if (dbg && dbg->gates)
+    (void)hipMemcpyAsync(dbg->gates + static_cast<long>(l) * rows * m.top_k, c->gates,
+                         sizeof(float) * rows * m.top_k, hipMemcpyDeviceToDevice, s);
+
+  const int routes = rows * m.top_k;
+  timed(c, "moe_permute", s, [&] { launch_moe_permute(c->eidx, routes, m.n_experts, c->offs, c->perm, c->inv, s); });
+  MoeArgs g1{};
+  g1.x = c->a; g1.ldx = d; g1.perm = c->perm; g1.top_k = m.top_k; g1.offs = c->offs;
+  g1.w0 = lw.w_gate; g1.w1 = lw.w_up; g1.K = d; g1.N = m.d_ff_expert;
+  g1.out_bf16 = c->act; g1.ldo = m.d_ff_expert; g1.n_exp = m.n_experts;
+  timed(c, "moe_gemm1_swiglu", s, [&] { launch_moe_gemm1(g1, s); });
+  MoeArgs g2{};
+  g2.x = c->act; g2.ldx = m.d_ff_expert; g2.perm = c->perm; g2.top_k = m.top_k; g2.offs = c->offs;
+  g2.w0 = lw.w_down; g2.K = m.d_ff_expert; g2.N = d; g2.out_f32 = c->y; g2.ldo = d;
+  g2.n_exp = m.n_experts;
+  timed(c, "moe_gemm2", s, [&] { launch_moe_gemm2(g2, s); });
+
+  if (m.d_ff_shared > 0) {
+    GemmArgs gs{};
+    gs.x = c->a; gs.ldx = d; gs.n_tok = rows; gs.w0 = lw.ws_gate; gs.w1 = lw.ws_up; gs.K = d;
+    gs.N = m.d_ff_shared; gs.out_bf16 = c->sact; gs.ldo = m.d_ff_shared;
+    timed(c, "shared_gate_up_swiglu", s, [&] { launch_gemm(gs, EPI_SWIGLU_BF16, s); });
+    GemmArgs gd{};
+    gd.x = c->sact; gd.ldx = m.d_ff_shared; gd.n_tok = rows; gd.w0 = lw.ws_down;
+    gd.K = m.d_ff_shared; gd.N = d; gd.out_f32 = c->h; gd.ldo = d;
+    timed(c, "shared_down_residual", s, [&] { launch_gemm(gd, EPI_ADD_F32, s); });
+  }
+  timed(c, "moe_combine", s, [&] { launch_moe_combine(c->h, c->y, c->inv, c->gates, rows, d, m.top_k, s); });
+}
+
+int check_kv(dg_ctx* c, const dg_kv_cache* kv) {
+  if (!kv || !kv->k || !kv->v || !kv->len) return c->fail(DG_ERR_ARG, "kv cache: null pointer");
+  if (kv->batch < 1 || kv->batch > c->max_batch)
+    return c->fail(DG_ERR_CAPACITY, "kv->batch must be in [1, max_batch]");
+  if (kv->cap < 1) return c->fail(DG_ERR_ARG, "kv->cap < 1");
+  for (int b = 0; b < kv->batch; ++b)
+    if (kv->len[b] < 0 || kv->len[b] > kv->cap) return c->fail(DG_ERR_ARG, "kv->len out of [0, cap]");
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_batch,
+              int32_t max_prefill_rows, dg_ctx** out) {
+  g_create_error.clear();
+  if (!desc || !weights || !out) { g_create_error = "dg_create: null argument"; return DG_ERR_ARG; }
+  *out = nullptr;
+  const std::string bad = validate_desc(*desc);
+  if (!bad.empty()) { g_create_error = bad; return DG_ERR_SHAPE; }
+  if (max_batch < 1 || max_batch > kMaxBatch) {
+    g_create_error = "max_batch must be in [1, 64]";
+    return DG_ERR_ARG;
+  }
+  if (max_prefill_rows < 1 || max_prefill_rows > (1 << 16)) {
+    g_create_error = "max_prefill_rows must be in [1, 65536]";
+    return DG_ERR_ARG;
+  }
+  if (!weights->embed || !weights->final_norm || !weights->lm_head || !weights->layers) {
+    g_create_error = "dg_create: null weight pointer";
+    return DG_ERR_ARG;
+  }
+  for (int l = 0; l < desc->n_layers; ++l) {
+    const dg_layer_weights& lw = weights->layers[l];
+    if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_router ||
+        !lw.w_gate || !lw.w_up || !lw.w_down ||
+        (desc->d_ff_shared > 0 && (!lw.ws_gate || !lw.ws_up || !lw.ws_down))) {
+      g_create_error = "dg_create: null weight pointer in layer " + std::to_string(l);
+      return DG_ERR_ARG;
+    }
+  }
+  dg_ctx* c = new (std::nothrow) dg_ctx();
+  if (!c) { g_create_error = "out of host memory"; return DG_ERR_ARG; }
+  c->m = *desc;
+  c->w = *weights;
+  c->layers.assign(weights->layers, weights->layers + desc->n_layers);
+  c->w.layers = nullptr;
+  c->max_batch = max_batch;
+  c->max_prefill = max_prefill_rows;
+  c->r_canvas = max_batch * desc->canvas;
+  c->r_max = std::max(c->r_canvas, max_prefill_rows);
+  c->part_cap = c->r_canvas * desc->n_q_heads * kMaxSplit;
+  const dg_model_desc& m = c->m;
+  const long R = c->r_max, d = m.d_model, HD = m.n_q_heads * m.head_dim;
+  const long nqkv = (m.n_q_heads + 2L * m.n_kv_heads) * m.head_dim;
+  const long ckv = static_cast<long>(m.n_layers) * max_batch * m.n_kv_heads * m.canvas * m.head_dim;
+  bool ok = c->alloc(&c->h, R * d) && c->alloc(&c->a, R * d) && c->alloc(&c->qkv, R * nqkv) &&
+            c->alloc(&c->q, R * HD) && c->alloc(&c->attn, R * HD) &&
+            c->alloc(&c->part_o, static_cast<long>(c->part_cap) * m.head_dim) &&
+            c->alloc(&c->part_ml, static_cast<long>(c->part_cap) * 2) &&
+            c->alloc(&c->eidx, R * m.top_k) && c->alloc(&c->gates, R * m.top_k) &&
+            c->alloc(&c->offs, m.n_experts + 1) && c->alloc(&c->perm, R * m.top_k) &&
+            c->alloc(&c->inv, R * m.top_k) && c->alloc(&c->act, R * m.top_k * m.d_ff_expert) &&
+            c->alloc(&c->y, R * m.top_k * d) &&
+            c->alloc(&c->sact, R * std::max(1, m.d_ff_shared)) &&
+            c->alloc(&c->f, static_cast<long>(c->r_canvas) * d) &&
+            c->alloc(&c->head_part, static_cast<long>(c->r_canvas) * (m.vocab / kHeadSlice) * 8) &&
+            c->alloc(&c->ck, ckv) && c->alloc(&c->cv, ckv);
+  if (!ok) {
+    g_create_error = "workspace allocation failed";
+    delete c;
+    return DG_ERR_HIP;
+  }
+  *out = c;
+  return DG_OK;
+}
+
+void dg_destroy(dg_ctx* ctx) { delete ctx; }
+
+const char* dg_last_error(const dg_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_create_error.c_str();
+}
+
+float dg_temperature(const dg_sampler_cfg* cfg, int32_t step) {
+  if (!cfg) return 0.f;
+  if (cfg->max_steps <= 1) return cfg->temp_start;
+  const double t = static_cast<double>(cfg->temp_start) +
+                   (static_cast<double>(cfg->temp_end) - static_cast<double>(cfg->temp_start)) *
+                       step / (cfg->max_steps - 1);
+  return static_cast<float>(t);
+}
+
+int dg_prefill_causal(dg_ctx* c, const int32_t* tokens, const int32_t* n_new, int32_t batch,
+                      dg_kv_cache* kv, hipStream_t s) {
+  if (!c) return DG_ERR_ARG;
+  if (!tokens || !n_new) return c->fail(DG_ERR_ARG, "prefill: null pointer");
+  int rc = check_kv(c, kv);
+  if (rc) return rc;
+  if (batch != kv->batch) return c->fail(DG_ERR_ARG, "prefill: batch != kv->batch");
+  for (int b = 0; b < batch; ++b) {
+    if (n_new[b] < 0) return c->fail(DG_ERR_ARG, "prefill: n_new < 0");
+    if (static_cast<long>(kv->len[b]) + n_new[b] > kv->cap)
+      return c->fail(DG_ERR_CAPACITY, "prefill: len + n_new > cap");
+  }
+  const dg_model_desc& m = c->m;
+  long tok_ofs = 0;
+  for (int b = 0; b < batch; ++b) {
+    for (int done = 0; done < n_new[b];) {
+      const int n = std::min(c->max_prefill, n_new[b] - done);
+      launch_embed(tokens + tok_ofs + done, c->w.embed, c->h, n, m.d_model, s);
+      const int32_t len_b = kv->len[b] + done;
+      for (int l = 0; l < m.n_layers; ++l) {
+        const long base = l * kv_layer_stride(m, kv->batch, kv->cap) +
+                          static_cast<long>(b) * m.n_kv_heads * kv->cap * m.head_dim;
+        run_layer(c, l, 1, n, &len_b, true, kv->k + base, kv->v + base, kv->cap, nullptr, s);
+      }
+      done += n;
+    }
+    tok_ofs += n_new[b];
+  }
+  rc = check_hip(c, "prefill");
+  if (rc) return rc;
+  for (int b = 0; b < batch; ++b) kv->len[b] += n_new[b];
+  return DG_OK;
+}
+
+int dg_canvas_init(dg_ctx* c, dg_canvas_state* st, const dg_kv_cache* kv,
+                   const dg_sampler_cfg* cfg, hipStream_t s) {
+  if (!c) return DG_ERR_ARG;
+  if (!st || !st->tokens || !st->committed || !st->stable_run || !st->stopped || !cfg)
+    return c->fail(DG_ERR_ARG, "canvas_init: null pointer");
+  int rc = check_kv(c, kv);
+  if (rc) return rc;
+  const RowMap map = make_map(c->m.canvas, kv->batch, kv->len);
+  launch_canvas_init(st->tokens, st->committed, st->stable_run, st->stopped, c->m.canvas, c->m.vocab,
+                     static_cast<uint32_t>(cfg->seed), static_cast<uint32_t>(cfg->seed >> 32), map, s);
+  return check_hip(c, "canvas_init");
+}
+
+static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
+                        const dg_sampler_cfg* cfg, const dg_step_params* p, dg_row_stats* out,
+                        hipStream_t s) {
+  const dg_model_desc& m = c->m;
+  const int B = kv->batch, C = m.canvas, rows = B * C, d = m.d_model;
+  const uint32_t flags = p ? p->flags : 0u;
+  const dg_debug* dbg = p ? p->debug : nullptr;
+  const bool head_only = flags & DG_STEP_HEAD_ONLY;
+  const bool no_head = flags & DG_STEP_NO_HEAD;
+
+  if (!head_only) {
+    if (flags & DG_STEP_HIDDEN_IN)
+      (void)hipMemcpyAsync(c->h, p->hidden_in, sizeof(float) * rows * d, hipMemcpyDeviceToDevice, s);
+    else
+      timed(c, "embed", s, [&] { launch_embed(canvas, c->w.embed, c->h, rows, d, s); });
+    for (int l = 0; l < m.n_layers; ++l)
+      run_layer(c, l, B, C, kv->len, false, kv->k + l * kv_layer_stride(m, B, kv->cap),
+                kv->v + l * kv_layer_stride(m, B, kv->cap), kv->cap, dbg, s);
+    if (dbg && dbg->hidden_out)
+      (void)hipMemcpyAsync(dbg->hidden_out, c->h, sizeof(float) * rows * d, hipMemcpyDeviceToDevice, s);
+    if (dbg && (dbg->canvas_k || dbg->canvas_v)) {
+      // workspace canvas K/V is [L][max_batch][Hkv][C][D]; dump [L][B][Hkv][C][D]
+      const long per_b = static_cast<long>(m.n_kv_heads) * C * m.head_dim;
+      for (int l = 0; l < m.n_layers; ++l) {
+        const long src = static_cast<long>(l) * c->max_batch * per_b, dst = static_cast<long>(l) * B * per_b;
+        if (dbg->canvas_k)
+          (void)hipMemcpyAsync(dbg->canvas_k + dst, c->ck + src, 2 * B * per_b, hipMemcpyDeviceToDevice, s);
+        if (dbg->canvas_v)
+          (void)hipMemcpyAsync(dbg->canvas_v + dst, c->cv + src, 2 * B * per_b, hipMemcpyDeviceToDevice, s);
+      }
+    }
+  }
+  if (no_head) return DG_OK;
+  const uint16_t* f = c->f;
+  if (head_only) {
+    f = static_cast<const uint16_t*>(p->hidden_in);
+  } else {
+    timed(c, "final_norm", s, [&] { launch_rmsnorm(c->h, c->w.final_norm, m.rms_eps, c->f, rows, d, s); });
+  }
+  HeadArgs ha{};
+  ha.f = f; ha.n_rows = rows; ha.w = c->w.lm_head; ha.K = d; ha.V = m.vocab;
+  ha.temp = dg_temperature(cfg, p ? p->step : 0);
+  ha.k0 = static_cast<uint32_t>(cfg->seed); ha.k1 = static_cast<uint32_t>(cfg->seed >> 32);
+  ha.step = p ? p->step : 0;
+  ha.cur_tok = canvas;
+  ha.map = make_map(C, B, kv->len);
+  ha.part = c->head_part;
+  ha.dbg_logits = dbg ? dbg->logits : nullptr;
+  timed(c, "head_lse_gumbel", s, [&] { launch_head(ha, s); });
+  timed(c, "head_merge", s, [&] { launch_head_merge(c->head_part, rows, m.vocab / kHeadSlice, kHeadSlice, canvas, out->cand,
+                    out->t_cand, out->t_cur, out->lse, out->entropy, s); });
+  return DG_OK;
+}
+
+int dg_denoise_step(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
+                    const dg_sampler_cfg* cfg, const dg_step_params* p, dg_row_stats* out,
+                    hipStream_t s) {
+  if (!c) return DG_ERR_ARG;
+  int rc = check_kv(c, kv);
+  if (rc) return rc;
+  const uint32_t flags = p ? p->flags : 0u;
+  if (flags & ~(DG_STEP_HIDDEN_IN | DG_STEP_NO_HEAD | DG_STEP_HEAD_ONLY))
+    return c->fail(DG_ERR_UNSUPPORTED, "denoise: unknown flag");
+  if ((flags & DG_STEP_HEAD_ONLY) && (flags & (DG_STEP_NO_HEAD | DG_STEP_HIDDEN_IN)))
+    return c->fail(DG_ERR_UNSUPPORTED, "denoise: HEAD_ONLY excludes NO_HEAD and HIDDEN_IN");
+  if ((flags & (DG_STEP_HIDDEN_IN | DG_STEP_HEAD_ONLY)) && !p->hidden_in)
+    return c->fail(DG_ERR_ARG, "denoise: hidden_in is null");
+  const bool head = !(flags & DG_STEP_NO_HEAD);
+  if (!canvas && (head || !(flags & DG_STEP_HIDDEN_IN)))
+    return c->fail(DG_ERR_ARG, "denoise: canvas is null");
+  if (head) {
+    if (!cfg) return c->fail(DG_ERR_ARG, "denoise: sampler cfg is null");
+    if (!out || !out->cand || !out->t_cand || !out->t_cur || !out->lse || !out->entropy)
+      return c->fail(DG_ERR_ARG, "denoise: row stats pointer is null");
+    if (cfg->max_steps < 1) return c->fail(DG_ERR_ARG, "denoise: max_steps < 1");
+    const int step = p ? p->step : 0;
+    if (step < 0 || step >= cfg->max_steps) return c->fail(DG_ERR_ARG, "denoise: step out of [0, max_steps)");
+    if (!(cfg->temp_start > 0.f) || !(cfg->temp_end > 0.f))
+      return c->fail(DG_ERR_ARG, "denoise: temperatures must be > 0");
+  }
+  rc = denoise_impl(c, canvas, kv, cfg, p, out, s);
+  if (rc) return rc;
+  return check_hip(c, "denoise_step");
+}
+
+int dg_sample_commit(dg_ctx* c, dg_canvas_state* st, const dg_row_stats* rs,
+                     const dg_sampler_cfg* cfg, int32_t step, const dg_kv_cache* kv,
+                     dg_step_status* status, hipStream_t s) {
+  if (!c) return DG_ERR_ARG;
+  if (!st || !st->tokens || !st->committed || !st->stable_run || !st->stopped || !rs || !rs->cand ||
+      !rs->t_cand ||
+      !rs->t_cur || !rs->lse || !rs->entropy || !cfg || !status)
+    return c->fail(DG_ERR_ARG, "sample_commit: null pointer");
+  int rc = check_kv(c, kv);
+  if (rc) return rc;
+  if (cfg->max_steps < 1 || step < 0 || step >= cfg->max_steps)
+    return c->fail(DG_ERR_ARG, "sample_commit: step out of [0, max_steps)");
+  if (cfg->commit_per_step < 0 || cfg->stable_steps < 1 || !(cfg->renoise_conf >= 0.f))
+    return c->fail(DG_ERR_ARG, "sample_commit: bad sampler config");
+  SamplerArgs a{};
+  a.tokens = st->tokens; a.committed = st->committed; a.stable_run = st->stable_run;
+  a.stopped = st->stopped;
+  a.cand = rs->cand; a.t_cand = rs->t_cand; a.t_cur = rs->t_cur; a.lse = rs->lse; a.ent = rs->entropy;
+  a.status = status;
+  a.C = c->m.canvas; a.V = c->m.vocab; a.step = step; a.max_steps = cfg->max_steps;
+  a.commit_m = cfg->commit_per_step;
+  a.log_tau = cfg->renoise_conf > 0.f ? static_cast<float>(std::log(static_cast<double>(cfg->renoise_conf)))
+                                      : -INFINITY;
+  a.stable_steps = cfg->stable_steps; a.entropy_stop = cfg->entropy_stop;
+  a.renoise_committed = cfg->renoise_committed;
+  a.k0 = static_cast<uint32_t>(cfg->seed); a.k1 = static_cast<uint32_t>(cfg->seed >> 32);
+  for (int b = 0; b < kv->batch; ++b) a.pos0[b] = kv->len[b];
+  timed(c, "sample_commit", s, [&] { launch_sample_commit(a, kv->batch, s); });
+  return check_hip(c, "sample_commit");
+}
+
+int dg_commit_block(dg_ctx* c, const int32_t* canvas, dg_kv_cache* kv, int32_t refresh,
+                    hipStream_t s) {
+  if (!c) return DG_ERR_ARG;
+  int rc = check_kv(c, kv);
+  if (rc) return rc;
+  if (refresh && !canvas) return c->fail(DG_ERR_ARG, "commit_block: refresh needs the canvas");
+  const dg_model_desc& m = c->m;
+  for (int b = 0; b < kv->batch; ++b)
+    if (static_cast<long>(kv->len[b]) + m.canvas > kv->cap)
+      return c->fail(DG_ERR_CAPACITY, "commit_block: len + canvas > cap");
+  if (refresh) {
+    dg_step_params p{};
+    p.flags = DG_STEP_NO_HEAD;
+    rc = denoise_impl(c, canvas, kv, nullptr, &p, nullptr, s);
+    if (rc) return rc;
+  }
+  const RowMap map = make_map(m.canvas, kv->batch, kv->len);
+  const long per_layer_ws = static_cast<long>(c->max_batch) * m.n_kv_heads * m.canvas * m.head_dim;
+  for (int l = 0; l < m.n_layers; ++l) {
+    const long dst = l * kv_layer_stride(m, kv->batch, kv->cap);
+    timed(c, "kv_append", s, [&] {
+      launch_kv_append(c->ck + l * per_layer_ws, c->cv + l * per_layer_ws, kv->k + dst, kv->v + dst,
+                       kv->batch, m.n_kv_heads, m.canvas, m.head_dim, kv->cap, map, s);
+    });
+  }
+  rc = check_hip(c, "commit_block");
+  if (rc) return rc;
+  for (int b = 0; b < kv->batch; ++b) kv->len[b] += m.canvas;
+  return DG_OK;
+}
+
+int dg_timing_enable(dg_ctx* c, int32_t enable) {
+  if (!c) return DG_ERR_ARG;
+  c->timing = enable != 0;
+  return DG_OK;
+}
+
+int dg_timing_read(dg_ctx* c, dg_kernel_time* out, int32_t max) {
+  if (!c) return DG_ERR_ARG;
+  if (!out || max < 0) return c->fail(DG_ERR_ARG, "timing_read: bad output buffer");
+  std::vector<dg_kernel_time> acc;
+  for (auto& r : c->recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      return c->fail(DG_ERR_HIP, "timing_read: event query failed");
+    auto it = std::find_if(acc.begin(), acc.end(),
+                           [&](const dg_kernel_time& k) { return std::strcmp(k.name, r.name) == 0; });
+    if (it == acc.end()) acc.push_back({r.name, 1, ms});
+    else { it->launches += 1; it->total_ms += ms; }
+    c->pool.push_back(r.a);
+    c->pool.push_back(r.b);
+  }
+  c->recs.clear();
+  const int n = std::min<int>(max, static_cast<int>(acc.size()));
+  for (int i = 0; i < n; ++i) out[i] = acc[i];
+  return n;
+}
+
+int dg_debug_set_canvas_kv(dg_ctx* c, const uint16_t* k, const uint16_t* v, int32_t batch,
+                           hipStream_t s) {
+  if (!c) return DG_ERR_ARG;
+  if (!k || !v) return c->fail(DG_ERR_ARG, "set_canvas_kv: null pointer");
+  if (batch < 1 || batch > c->max_batch) return c->fail(DG_ERR_ARG, "set_canvas_kv: bad batch");
+  const dg_model_desc& m = c->m;
+  const long per_b = static_cast<long>(m.n_kv_heads) * m.canvas * m.head_dim;
+  for (int l = 0; l < m.n_layers; ++l) {
+    const long dst = static_cast<long>(l) * c->max_batch * per_b, src = static_cast<long>(l) * batch * per_b;
+    (void)hipMemcpyAsync(c->ck + dst, k + src, 2 * batch * per_b, hipMemcpyDeviceToDevice, s);
+    (void)hipMemcpyAsync(c->cv + dst, v + src, 2 * batch * per_b, hipMemcpyDeviceToDevice, s);
+  }
+  return check_hip(c, "set_canvas_kv");
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// Host-side launch interface of the libdg kernels (one family per source file).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+constexpr int kMaxBatch = 64;
+
+// Per-request row bookkeeping passed by value to kernels: request b owns rows
+// [b*rows_per_req, (b+1)*rows_per_req) and row i of it sits at position pos0[b] + i.
+struct RowMap {
+  int32_t rows_per_req;
+  int32_t n_req;
+  int32_t pos0[kMaxBatch];
+};
+
+// ---- k_norm.hip
+void launch_embed(const int32_t* tok, const uint16_t* embed, float* h, int rows, int d,
+                  hipStream_t s);
+void launch_rmsnorm(const float* h, const float* gain, float eps, uint16_t* out, int rows, int d,
+                    hipStream_t s);
+void launch_f32_to_bf16(const float* in, uint16_t* out, long n, hipStream_t s);
+// ffn norm + router: b = bf16(rms(h)*gain); logits in fp32 from the fp32 normed row;
+// top-k (value desc, index asc); softmax gates over the k picks.
+void launch_norm_router(const float* h, const float* gain, float eps, const uint16_t* w_router,
+                        int rows, int d, int n_exp, int top_k, uint16_t* b_out, int32_t* idx,
+                        float* gates, hipStream_t s);
+
+// ---- k_gemm.hip : C[t][f] = sum_k X[t][k] * W[f][k]
+enum GemmEpi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU_BF16 = 2, EPI_STORE_BF16 = 3 };
+struct GemmArgs {
+  const uint16_t* x; int ldx; int n_tok;
+  const uint16_t* w0; const uint16_t* w1;  // w1: up matrix for SwiGLU
+  // optional segmented W (QKV): rows [seg_start[s], seg_start[s+1]) come from seg_w[s]
+  const uint16_t* seg_w[3]; int seg_start[4]; int n_seg;
+  int K; int N;
+  float* out_f32; uint16_t* out_bf16; int ldo;
+};
+void launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
+
+// Fused vocab head: logits never leave registers.  Writes per (row, 64-wide vocab slice)
+// partial statistics; launch_head_merge reduces them into row statistics.
+struct HeadArgs {
+  const uint16_t* f; int n_rows;      // bf16 [rows][d] final normed state
+  const uint16_t* w; int K; int V;    // lm_head [V][d]
+  float inv_dummy; float temp;        // temperature T (t = z / T)
+  uint32_t k0, k1; int32_t step;      // Philox key (seed) and step
+  const int32_t* cur_tok;             // [rows] current canvas token
+  RowMap map;
+  float* part;                        // [rows][n_slices][8]
+  float* dbg_logits;                  // optional [rows][V]
+};
+void launch_head(const HeadArgs& a, hipStream_t s);
+void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
+                       const int32_t* cur_tok, int32_t* cand, float* t_cand, float* t_cur,
+                       float* lse, float* ent, hipStream_t s);
+
+// ---- k_attn.hip
+// Split qkv fp32 [rows][(Hq+2Hkv)*D] into rotated bf16 q [rows][Hq*D] and rotated k / v written
+// at kv_dst + ((b*Hkv + g)*kv_cap + slot0[b] + i)*D.
+struct RopeArgs {
+  const float* qkv; int rows; int Hq; int Hkv; int D; float theta;
+  uint16_t* q; uint16_t* k_dst; uint16_t* v_dst; int kv_cap;  // per-layer base
+  RowMap map; int32_t slot0[kMaxBatch];
+};
+void launch_rope_scatter(const RopeArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const uint16_t* q;       // [rows][Hq*D]
+  uint16_t* out;           // [rows][Hq*D]
+  const uint16_t* kc; const uint16_t* vc; int cap;   // cache base of the layer [B][Hkv][cap][D]
+  const uint16_t* kx; const uint16_t* vx; int xcap;  // extra keys (canvas) [B][Hkv][xcap][D]
+  int Hq, Hkv, D;
+  int rows_per_req; int n_req;
+  int32_t n_cache[kMaxBatch];   // keys read from the cache per request
+  int32_t n_extra;              // canvas keys (0 in prefill)
+  int32_t q_pos0[kMaxBatch];    // position of the first query row of each request
+  int causal;                   // key position <= query position
+  float scale;                  // 1/sqrt(D)
+  int n_split; int split_keys;  // split-KV: each split covers split_keys keys
+  float* part_o; float* part_ml;  // partials when n_split > 1
+};
+void launch_attention(const AttnArgs& a, hipStream_t s);
+
+// ---- k_moe.hip
+void launch_moe_permute(const int32_t* idx, int n_routes, int n_exp, int32_t* offs,
+                        int32_t* perm, int32_t* inv, hipStream_t s);
+struct MoeArgs {
+  const uint16_t* x; int ldx;       // GEMM1: normed rows b [rows][d]; GEMM2: act [routes][F]
+  const int32_t* perm; int top_k;   // GEMM1 gathers row perm[p]/top_k; GEMM2 reads row p
+  const int32_t* offs;              // [E+1]
+  const uint16_t* w0; const uint16_t* w1;  // GEMM1: gate, up [E][F][d]; GEMM2: down [E][d][F]
+  int K; int N;                     // reduction length and output features per expert
+  uint16_t* out_bf16; float* out_f32; int ldo;
+  int n_exp;
+};
+void launch_moe_gemm1(const MoeArgs& a, hipStream_t s);
+void launch_moe_gemm2(const MoeArgs& a, hipStream_t s);
+void launch_moe_combine(float* h, const float* y, const int32_t* inv, const float* gates,
+                        int rows, int d, int top_k, hipStream_t s);
+
+// ---- k_sampler.hip
+struct SamplerArgs {
+  int32_t* tokens; uint8_t* committed; int32_t* stable_run; int32_t* stopped;
+  const int32_t* cand; const float* t_cand; const float* t_cur; const float* lse;
+  const float* ent;
+  void* status;  // dg_step_status[B]
+  int C; int V; int step; int max_steps; int commit_m; float log_tau; int stable_steps;
+  float entropy_stop; int renoise_committed; uint32_t k0, k1;
+  int32_t pos0[kMaxBatch];
+};
+void launch_sample_commit(const SamplerArgs& a, int n_req, hipStream_t s);
+void launch_canvas_init(int32_t* tokens, uint8_t* committed, int32_t* stable_run,
+                        int32_t* stopped, int C, int V,
+                        uint32_t k0, uint32_t k1, const RowMap& map, hipStream_t s);
+// Copy canvas K/V [B][Hkv][C][D] of one layer into the cache at [len[b], len[b]+C).
+void launch_kv_append(const uint16_t* src_k, const uint16_t* src_v, uint16_t* dst_k,
+                      uint16_t* dst_v, int B, int Hkv, int C, int D, int cap,
+                      const RowMap& map, hipStream_t s);
+
+}  // namespace dg

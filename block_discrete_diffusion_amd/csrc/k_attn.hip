@@ -1,0 +1,347 @@
+// Canvas attention (bidirectional, no mask) and causal prefill attention on MFMA, plus the
+// RoPE/scatter step that turns the QKV projection into rotated bf16 Q and K/V rows.
+//
+// Each work-group serves one (request, KV head) and up to four (query head, 32-row) tasks of
+// that head's query group, so every K/V tile staged in LDS is reused by all of them (GQA).
+// Keys are the request's cached prefix followed by the canvas keys; the key range can be split
+// across work-groups (split-KV) so that a 256-row canvas still fills the chip; the splits are
+// merged in a fixed order afterwards (deterministic).
+//
+// Lane layout: per 64-key block a wave computes S^T = K Q^T with 16x16x32 MFMAs (A = K rows
+// from LDS, B = its 32 queries from registers).  The accumulator gives each lane one query
+// (lane % 16) and four keys, which is exactly the B-operand layout of the next MFMA,
+// O^T += V^T P^T, if the 32 keys of one MFMA are taken as {4j..4j+3} of two 16-key sub-blocks
+// (the k order inside an MFMA only has to agree between A and B).  V is stored transposed in
+// LDS so the A operand V^T[d][keys] is two 8-byte reads.  The online-softmax state (max, sum)
+// is per query = per lane, so rescaling O^T needs no cross-lane traffic.
+#include "dg_common.h"
+#include "dg_kernels.h"
+
+namespace dg {
+namespace {
+
+// ---------------------------------------------------------------------------------- RoPE
+__global__ __launch_bounds__(256) void rope_scatter_kernel(RopeArgs a) {
+  const int r = blockIdx.x;
+  const int b = r / a.map.rows_per_req, i = r - b * a.map.rows_per_req;
+  const double pos = static_cast<double>(a.map.pos0[b] + i);
+  const int D = a.D, half = D / 2;
+  const int nqk = (a.Hq + a.Hkv) * half;  // rotated pairs
+  const float* row = a.qkv + static_cast<long>(r) * (a.Hq + 2 * a.Hkv) * D;
+  const long slot = a.slot0[b] + i;
+  for (int p = threadIdx.x; p < nqk; p += 256) {
+    const int h = p / half, j = p - h * half;
+    const float x1 = row[h * D + j], x2 = row[h * D + j + half];
+    float y1 = x1, y2 = x2;
+    if (a.theta != 0.f) {
+      const double inv_freq = pow(static_cast<double>(a.theta), -2.0 * j / D);
+      double sn, cs;
+      sincos(pos * inv_freq, &sn, &cs);
+      const double d1 = static_cast<double>(x1), d2 = static_cast<double>(x2);
+      y1 = static_cast<float>(d1 * cs - d2 * sn);
+      y2 = static_cast<float>(d2 * cs + d1 * sn);
+    }
+    if (h < a.Hq) {
+      uint16_t* q = a.q + static_cast<long>(r) * a.Hq * D + h * D;
+      q[j] = f2bf(y1);
+      q[j + half] = f2bf(y2);
+    } else {
+      const int g = h - a.Hq;
+      uint16_t* k = a.k_dst + ((static_cast<long>(b) * a.Hkv + g) * a.kv_cap + slot) * D;
+      k[j] = f2bf(y1);
+      k[j + half] = f2bf(y2);
+    }
+  }
+  // V: no rotation
+  const float* vrow = row + (a.Hq + a.Hkv) * D;
+  for (int p = threadIdx.x; p < a.Hkv * D; p += 256) {
+    const int g = p / D, dd = p - g * D;
+    a.v_dst[((static_cast<long>(b) * a.Hkv + g) * a.kv_cap + slot) * D + dd] = f2bf(vrow[p]);
+  }
+}
+
+// ---------------------------------------------------------------------------- attention
+constexpr int KB = 64;       // keys per block
+constexpr int VPAD = 4;      // V^T row padding (bf16)
+
+template <int D>
+struct AttnSmem {
+  uint16_t k[KB][D + 8];
+  uint16_t vt[D][KB + VPAD];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+  constexpr int NKS = D / 32;   // MFMA k-steps over the head dimension
+  constexpr int NDT = D / 16;   // 16-row tiles of O^T
+  constexpr int KCH = KB * D / 8 / 256;      // 16-byte K chunks per thread
+  constexpr int VTASK = (KB / 4) * (D / 8);  // (key quad, d octet) tasks
+  constexpr int VPT = (VTASK + 255) / 256;
+  __shared__ AttnSmem<D> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j4 = lane >> 4, l16 = lane & 15;
+  const int bg = blockIdx.z;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int group = a.Hq / a.Hkv;
+  const int rows = a.rows_per_req;
+  const int n_rb = (rows + 31) / 32;
+  const int task = blockIdx.x * 4 + wave;
+  const bool active = task < group * n_rb;
+  const int hq = g * group + (active ? task % group : 0);
+  const int rb = active ? task / group : 0;
+  const int row0 = rb * 32;  // first query row (within the request) of this wave
+
+  const int n_cache = a.n_cache[b];
+  const int n_keys = n_cache + a.n_extra;
+  // key range of this split; with a causal mask it ends after the last query of the group
+  int k_lo = blockIdx.y * a.split_keys;
+  int k_hi = min(n_keys, k_lo + a.split_keys);
+  if (a.causal) {
+    const int last_task = min(blockIdx.x * 4 + 3, group * n_rb - 1);
+    const int last_row = min(rows - 1, (last_task / group) * 32 + 31);
+    k_hi = min(k_hi, a.q_pos0[b] + last_row + 1);
+  }
+  const long qrow_base = static_cast<long>(b) * rows;
+
+  // queries (B operand): lane holds Q[qt*16 + l16][ks*32 + 8*j4 .. +8]
+  u32x4_t qf[2][NKS];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qr = row0 + qt * 16 + l16;
+    const bool ok = active && qr < rows;
+    const uint16_t* qp = a.q + (qrow_base + qr) * a.Hq * D + hq * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[qt][ks] = ok ? ld16(qp + ks * 32 + 8 * j4) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  int qpos[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) qpos[qt] = a.q_pos0[b] + row0 + qt * 16 + l16;
+
+  floatx4_t o[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  const float sl2 = a.scale * 1.4426950408889634f;
+
+  const long kv_head = static_cast<long>(b) * a.Hkv + g;
+  auto key_ptr_k = [&](int kk) -> const uint16_t* {
+    return kk < n_cache ? a.kc + (kv_head * a.cap + kk) * D
+                        : a.kx + (kv_head * a.xcap + (kk - n_cache)) * D;
+  };
+  auto key_ptr_v = [&](int kk) -> const uint16_t* {
+    return kk < n_cache ? a.vc + (kv_head * a.cap + kk) * D
+                        : a.vx + (kv_head * a.xcap + (kk - n_cache)) * D;
+  };
+
+  u32x4_t rk[KCH], rv[VPT][4];
+  auto gload = [&](int kb0) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int kk = kb0 + key;
+      rk[i] = (kk < k_hi) ? ld16(key_ptr_k(kk) + col) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int t = tid + 256 * i;
+      const int kq = t % (KB / 4), dq = t / (KB / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = kb0 + kq * 4 + r;
+        rv[i][r] = (t < VTASK && kk < k_hi) ? ld16(key_ptr_v(kk) + dq * 8) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
+      st16(&sm.k[key][col], rk[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int t = tid + 256 * i;
+      if (t >= VTASK) continue;
+      const int kq = t % (KB / 4), dq = t / (KB / 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // element e of each of the 4 keys -> V^T[dq*8+e][kq*4 .. +4]
+        const int w = e >> 1;
+        const bool hi = e & 1;
+        uint32_t h4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h4[r] = hi ? (rv[i][r][w] >> 16) : (rv[i][r][w] & 0xffffu);
+        *reinterpret_cast<u32x2_t*>(&sm.vt[dq * 8 + e][kq * 4]) =
+            u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
+      }
+    }
+  };
+
+  const int n_blk = (k_hi > k_lo) ? (k_hi - k_lo + KB - 1) / KB : 0;
+  if (n_blk > 0) gload(k_lo);
+  for (int blk = 0; blk < n_blk; ++blk) {
+    const int kb0 = k_lo + blk * KB;
+    __syncthreads();  // previous block's LDS reads are done
+    sstore();
+    __syncthreads();
+    if (blk + 1 < n_blk) gload(kb0 + KB);
+    if (!active) continue;
+
+    // S^T for 4 key sub-blocks x 2 query tiles
+    floatx4_t s[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const u32x4_t kf = ld16(&sm.k[kt * 16 + l16][ks * 32 + 8 * j4]);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
+      }
+    }
+    // scale, mask, online softmax (per lane = per query)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = kb0 + kt * 16 + 4 * j4 + i;
+          float v = s[kt][qt][i] * sl2;
+          if (kk >= k_hi || (a.causal && kk > qpos[qt])) v = -INFINITY;
+          s[kt][qt][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[qt], mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[qt] - m_new);
+      float sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = (m_new == -INFINITY) ? 0.f : exp2f(s[kt][qt][i] - m_new);
+          s[kt][qt][i] = p;
+          sum += p;
+        }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      l_run[qt] = l_run[qt] * alpha + sum;
+      m_run[qt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha;
+    }
+    // O^T += V^T P^T over two 32-key steps
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      u32x4_t pf[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const floatx4_t p0 = s[2 * kk2][qt], p1 = s[2 * kk2 + 1][qt];
+        pf[qt] = u32x4_t{pack_bf2(p0[0], p0[1]), pack_bf2(p0[2], p0[3]), pack_bf2(p1[0], p1[1]),
+                         pack_bf2(p1[2], p1[3])};
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint16_t* vr = &sm.vt[dt * 16 + l16][kk2 * 32 + 4 * j4];
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16);
+        const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma16(vf, pf[qt], o[dt][qt]);
+      }
+    }
+  }
+
+  if (!active) return;
+  // write: lane owns query qt*16+l16, dims dt*16 + 4*j4 + i
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qr = row0 + qt * 16 + l16;
+    if (qr >= rows) continue;
+    const long orow = qrow_base + qr;
+    if (a.n_split == 1) {
+      const float inv = (l_run[qt] > 0.f) ? 1.0f / l_run[qt] : 0.f;
+      uint16_t* op = a.out + orow * a.Hq * D + hq * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const floatx4_t v = o[dt][qt];
+        *reinterpret_cast<u32x2_t*>(op + dt * 16 + 4 * j4) =
+            u32x2_t{pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv)};
+      }
+    } else {
+      const long slot = (orow * a.Hq + hq) * a.n_split + blockIdx.y;
+      float* po = a.part_o + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<floatx4_t*>(po + dt * 16 + 4 * j4) = o[dt][qt];
+      if (j4 == 0) {
+        a.part_ml[slot * 2] = m_run[qt];
+        a.part_ml[slot * 2 + 1] = l_run[qt];
+      }
+    }
+  }
+}
+
+// Merge split partials in split order: O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           uint16_t* __restrict__ out, int n_rh,
+                                                           int n_split) {
+  constexpr int TPR = D / 4;  // threads per (row, head): 4 dims each
+  const int rh = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  if (rh >= n_rh) return;
+  const int d0 = (threadIdx.x % TPR) * 4;
+  float m = -INFINITY;
+  for (int s = 0; s < n_split; ++s) m = fmaxf(m, part_ml[(static_cast<long>(rh) * n_split + s) * 2]);
+  floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    const long slot = static_cast<long>(rh) * n_split + s;
+    const float ms = part_ml[slot * 2];
+    if (ms == -INFINITY) continue;
+    const float w = exp2f(ms - m);
+    l += w * part_ml[slot * 2 + 1];
+    acc += w * *reinterpret_cast<const floatx4_t*>(part_o + slot * D + d0);
+  }
+  const float inv = (l > 0.f) ? 1.0f / l : 0.f;
+  *reinterpret_cast<u32x2_t*>(out + static_cast<long>(rh) * D + d0) =
+      u32x2_t{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
+}
+
+template <int D>
+void launch_attn_d(const AttnArgs& a, hipStream_t s) {
+  const int group = a.Hq / a.Hkv;
+  const int tasks = group * ((a.rows_per_req + 31) / 32);
+  dim3 grid((tasks + 3) / 4, a.n_split, a.n_req * a.Hkv);
+  hipLaunchKernelGGL((attention_kernel<D>), grid, dim3(256), 0, s, a);
+  if (a.n_split > 1) {
+    const int n_rh = a.n_req * a.rows_per_req * a.Hq;
+    const int per = 256 / (D / 4);
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((n_rh + per - 1) / per), dim3(256), 0, s,
+                       a.part_o, a.part_ml, a.out, n_rh, a.n_split);
+  }
+}
+
+}  // namespace
+
+void launch_rope_scatter(const RopeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(rope_scatter_kernel, dim3(a.rows), dim3(256), 0, s, a);
+}
+
+void launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.D == 128) launch_attn_d<128>(a, s);
+  else launch_attn_d<64>(a, s);
+}
+
+}  // namespace dg

@@ -1,0 +1,350 @@
+// Dense projections on MFMA (QKV, O-proj + residual, shared SwiGLU FFN) and the fused vocab
+// head (projection + temperature + log-sum-exp + entropy + Gumbel-max; logits stay on chip).
+//
+// C[t][f] = sum_k X[t][k] * W[f][k]: both operands are k-contiguous ("NT"), which is the
+// natural MFMA operand layout.  The weight tile is the A operand (rows = output features) and
+// the activation tile the B operand (columns = tokens), so a lane's accumulator holds four
+// consecutive output features of one token: one Philox call covers exactly the four vocab
+// entries a lane owns, and stores are 16-byte (fp32) or 8-byte (bf16) per lane.
+//
+// Work-group tile BF features x BT tokens, 4 waves in a 2x2 grid, k-tile 64 double-buffered in
+// LDS with rows padded to 144 B (16-lane ds_read_b128 phases hit distinct banks).  The tile ->
+// work-group mapping keeps all token tiles of one weight tile on the same XCD so the weight
+// tile is fetched from HBM once and re-read from that XCD's L2.
+#include "dg_common.h"
+#include "dg_kernels.h"
+
+namespace dg {
+namespace {
+
+constexpr int BK = 64;
+constexpr int LDK = BK + 8;
+
+template <int BF, int BT, bool DUAL>
+struct Smem {
+  uint16_t w[2][DUAL ? 2 : 1][BF][LDK];
+  uint16_t x[2][BT][LDK];
+};
+
+// XCD-aware tile index: hardware hands consecutive work-group ids to the 8 XCDs round-robin;
+// this makes consecutive logical tiles land on one XCD.
+DG_DEVICE int xcd_remap(int bid, int G) {
+  return (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+}
+
+template <int BF, int BT, bool DUAL>
+struct Mainloop {
+  static constexpr int WF = BF / 2, WT = BT / 2, FM = WF / 16, TN = WT / 16;
+  static constexpr int CW = BF * (BK / 8) / 256;  // 16-byte chunks per thread (weights)
+  static constexpr int CX = BT * (BK / 8) / 256;  // 16-byte chunks per thread (activations)
+  static_assert(CW >= 1 && CX >= 1, "tile too small for 256 threads");
+
+  floatx4_t acc[FM][TN];
+  floatx4_t acc1[DUAL ? FM : 1][DUAL ? TN : 1];
+
+  DG_DEVICE void run(Smem<BF, BT, DUAL>& sm, const uint16_t* w0, const uint16_t* w1,
+                     const uint16_t* x, int ldx, int n_tok, int t0, int K) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wf = wave & 1, wt = wave >> 1;
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (DUAL) acc1[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    u32x4_t rw[CW], rw1[DUAL ? CW : 1], rx[CX];
+    const int nk = K / BK;
+
+    auto gload = [&](int kt) {
+      const int kof = kt * BK;
+#pragma unroll
+      for (int i = 0; i < CW; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
+        rw[i] = ld16(w0 + static_cast<long>(r) * K + kof + col);
+        if constexpr (DUAL) rw1[i] = ld16(w1 + static_cast<long>(r) * K + kof + col);
+      }
+#pragma unroll
+      for (int i = 0; i < CX; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
+        const int t = t0 + r;
+        rx[i] = (t < n_tok) ? ld16(x + static_cast<long>(t) * ldx + kof + col)
+                            : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < CW; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
+        st16(&sm.w[buf][0][r][col], rw[i]);
+        if constexpr (DUAL) st16(&sm.w[buf][DUAL ? 1 : 0][r][col], rw1[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < CX; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
+        st16(&sm.x[buf][r][col], rx[i]);
+      }
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        const int kk = ks * 32 + 8 * (lane >> 4);
+        u32x4_t af[FM], af1[DUAL ? FM : 1], bx[TN];
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+          af[a] = ld16(&sm.w[buf][0][wf * WF + a * 16 + (lane & 15)][kk]);
+          if constexpr (DUAL) af1[a] = ld16(&sm.w[buf][DUAL ? 1 : 0][wf * WF + a * 16 + (lane & 15)][kk]);
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) bx[b] = ld16(&sm.x[buf][wt * WT + b * 16 + (lane & 15)][kk]);
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+          for (int b = 0; b < TN; ++b) {
+            acc[a][b] = mfma16(af[a], bx[b], acc[a][b]);
+            if constexpr (DUAL) acc1[a][b] = mfma16(af1[a], bx[b], acc1[a][b]);
+          }
+      }
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) gload(kt + 1);
+      compute(kt & 1);
+      if (kt + 1 < nk) sstore((kt + 1) & 1);
+      __syncthreads();
+    }
+  }
+};
+
+template <int BF, int BT, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+  constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
+  using ML = Mainloop<BF, BT, DUAL>;
+  __shared__ Smem<BF, BT, DUAL> sm;
+  const int n_tt = (a.n_tok + BT - 1) / BT, n_ft = a.N / BF;
+  const int L = xcd_remap(blockIdx.x, n_tt * n_ft);
+  const int ft = L / n_tt, tt = L % n_tt;
+  const int f0 = ft * BF, t0 = tt * BT;
+  const uint16_t* w0;
+  const uint16_t* w1 = nullptr;
+  if (a.n_seg > 0) {
+    int s = 0;
+    while (s + 1 < a.n_seg && f0 >= a.seg_start[s + 1]) ++s;
+    w0 = a.seg_w[s] + static_cast<long>(f0 - a.seg_start[s]) * a.K;
+  } else {
+    w0 = a.w0 + static_cast<long>(f0) * a.K;
+    if (DUAL) w1 = a.w1 + static_cast<long>(f0) * a.K;
+  }
+  ML ml;
+  ml.run(sm, w0, w1, a.x, a.ldx, a.n_tok, t0, a.K);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wf = wave & 1, wt = wave >> 1;
+#pragma unroll
+  for (int fm = 0; fm < ML::FM; ++fm)
+#pragma unroll
+    for (int tn = 0; tn < ML::TN; ++tn) {
+      const int t = t0 + wt * ML::WT + tn * 16 + (lane & 15);
+      const int f = f0 + wf * ML::WF + fm * 16 + 4 * (lane >> 4);
+      if (t >= a.n_tok) continue;
+      const floatx4_t v = ml.acc[fm][tn];
+      if constexpr (EPI == EPI_STORE_F32) {
+        *reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(t) * a.ldo + f) = v;
+      } else if constexpr (EPI == EPI_ADD_F32) {
+        floatx4_t* p = reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(t) * a.ldo + f);
+        floatx4_t o = *p;
+        o += v;
+        *p = o;
+      } else if constexpr (EPI == EPI_SWIGLU_BF16) {
+        const floatx4_t u = ml.acc1[DUAL ? fm : 0][DUAL ? tn : 0];
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = v[i] / (1.0f + expf(-v[i])) * u[i];
+        *reinterpret_cast<u32x2_t*>(a.out_bf16 + static_cast<long>(t) * a.ldo + f) =
+            u32x2_t{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
+      } else {
+        *reinterpret_cast<u32x2_t*>(a.out_bf16 + static_cast<long>(t) * a.ldo + f) =
+            u32x2_t{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Fused vocab head.  Per lane and token: the four logits z of vocab entries v0..v0+3 (v0 a
+// multiple of 4) give t = z / T, Gumbel noise from one Philox call (counter v0>>2, position,
+// step, request), and running max / sum(exp) / sum(exp*t) / best (score, index, t).  Lanes of
+// the same token merge with two butterfly steps; one record per (token, wave slice of BF/2
+// vocab entries) goes to `part`.
+// ------------------------------------------------------------------------------------------
+struct Stat {
+  float m, s, st, bs, bt, tc;
+  int bi;
+};
+
+DG_DEVICE Stat merge_stat(const Stat& a, const Stat& b) {
+  Stat r;
+  if (a.m == -INFINITY) {
+    r = b;
+  } else if (b.m == -INFINITY) {
+    r = a;
+  } else {
+    r.m = fmaxf(a.m, b.m);
+    const float ea = expf(a.m - r.m), eb = expf(b.m - r.m);
+    r.s = a.s * ea + b.s * eb;
+    r.st = a.st * ea + b.st * eb;
+  }
+  const bool take_b = (b.bs > a.bs) || (b.bs == a.bs && b.bi < a.bi);
+  r.bs = take_b ? b.bs : a.bs;
+  r.bi = take_b ? b.bi : a.bi;
+  r.bt = take_b ? b.bt : a.bt;
+  r.tc = (a.tc == a.tc) ? a.tc : b.tc;  // NaN = current token not in this range
+  return r;
+}
+
+DG_DEVICE Stat shfl_stat(const Stat& a, int o) {
+  Stat r;
+  r.m = __shfl_xor(a.m, o, 64);
+  r.s = __shfl_xor(a.s, o, 64);
+  r.st = __shfl_xor(a.st, o, 64);
+  r.bs = __shfl_xor(a.bs, o, 64);
+  r.bt = __shfl_xor(a.bt, o, 64);
+  r.tc = __shfl_xor(a.tc, o, 64);
+  r.bi = __shfl_xor(a.bi, o, 64);
+  return r;
+}
+
+template <int BF, int BT>
+__global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
+  using ML = Mainloop<BF, BT, false>;
+  __shared__ Smem<BF, BT, false> sm;
+  const int n_tt = (a.n_rows + BT - 1) / BT, n_ft = a.V / BF;
+  const int L = xcd_remap(blockIdx.x, n_tt * n_ft);
+  const int ft = L / n_tt, tt = L % n_tt;
+  const int f0 = ft * BF, t0 = tt * BT;
+  ML ml;
+  ml.run(sm, a.w + static_cast<long>(f0) * a.K, nullptr, a.f, a.K, a.n_rows, t0, a.K);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wf = wave & 1, wt = wave >> 1;
+  const int n_slices = a.V / ML::WF;
+  const int slice = (f0 + wf * ML::WF) / ML::WF;
+#pragma unroll
+  for (int tn = 0; tn < ML::TN; ++tn) {
+    const int t = t0 + wt * ML::WT + tn * 16 + (lane & 15);
+    const bool ok = t < a.n_rows;
+    const int tc = ok ? t : 0;
+    const int b = tc / a.map.rows_per_req;
+    const int pos = a.map.pos0[b] + (tc - b * a.map.rows_per_req);
+    const int cur = ok ? a.cur_tok[tc] : -1;
+    float tv[ML::FM][4];
+    Stat st;
+    st.m = -INFINITY; st.s = 0.f; st.st = 0.f; st.bs = -INFINITY; st.bt = 0.f; st.tc = NAN;
+    st.bi = 0x7fffffff;
+#pragma unroll
+    for (int fm = 0; fm < ML::FM; ++fm) {
+      const int v0 = f0 + wf * ML::WF + fm * 16 + 4 * (lane >> 4);
+      const philox_out rnd = philox4x32_10(static_cast<uint32_t>(v0 >> 2), static_cast<uint32_t>(pos),
+                                           static_cast<uint32_t>(a.step),
+                                           (static_cast<uint32_t>(b) << 8) | kStreamGumbel, a.k0, a.k1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float z = ml.acc[fm][tn][i];
+        const float t_ = z / a.temp;
+        tv[fm][i] = t_;
+        const float sc = t_ + gumbel(rnd.x[i]);
+        if (sc > st.bs) { st.bs = sc; st.bi = v0 + i; st.bt = t_; }
+        st.m = fmaxf(st.m, t_);
+        if (v0 + i == cur) st.tc = t_;
+        if (a.dbg_logits && ok) a.dbg_logits[static_cast<long>(t) * a.V + v0 + i] = z;
+      }
+    }
+#pragma unroll
+    for (int fm = 0; fm < ML::FM; ++fm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = expf(tv[fm][i] - st.m);
+        st.s += e;
+        st.st += e * tv[fm][i];
+      }
+    st = merge_stat(st, shfl_stat(st, 16));
+    st = merge_stat(st, shfl_stat(st, 32));
+    if (ok && (lane >> 4) == 0) {
+      float* p = a.part + (static_cast<long>(t) * n_slices + slice) * 8;
+      *reinterpret_cast<floatx4_t*>(p) = floatx4_t{st.m, st.s, st.st, st.bs};
+      *reinterpret_cast<floatx4_t*>(p + 4) = floatx4_t{__int_as_float(st.bi), st.bt, st.tc, 0.f};
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void head_merge_kernel(const float* __restrict__ part, int n_rows,
+                                                        int n_slices, int slice_w,
+                                                        const int32_t* __restrict__ cur_tok,
+                                                        int32_t* cand, float* t_cand, float* t_cur,
+                                                        float* lse, float* ent) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  Stat st;
+  st.m = -INFINITY; st.s = 0.f; st.st = 0.f; st.bs = -INFINITY; st.bt = 0.f; st.tc = NAN;
+  st.bi = 0x7fffffff;
+  for (int j = lane; j < n_slices; j += 64) {
+    const float* p = part + (static_cast<long>(row) * n_slices + j) * 8;
+    Stat o;
+    o.m = p[0]; o.s = p[1]; o.st = p[2]; o.bs = p[3]; o.bi = __float_as_int(p[4]); o.bt = p[5];
+    o.tc = NAN;
+    st = merge_stat(st, o);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) st = merge_stat(st, shfl_stat(st, o));
+  if (lane == 0) {
+    const float l = st.m + logf(st.s);
+    lse[row] = l;
+    ent[row] = l - st.st / st.s;
+    cand[row] = st.bi;
+    t_cand[row] = st.bt;
+    const int x = cur_tok[row];
+    t_cur[row] = part[(static_cast<long>(row) * n_slices + x / slice_w) * 8 + 6];
+  }
+}
+
+template <int BF, int BT, int EPI>
+void launch_cfg(const GemmArgs& a, hipStream_t s) {
+  const int G = ((a.n_tok + BT - 1) / BT) * (a.N / BF);
+  hipLaunchKernelGGL((gemm_kernel<BF, BT, EPI>), dim3(G), dim3(256), 0, s, a);
+}
+
+template <int EPI>
+void launch_epi(const GemmArgs& a, hipStream_t s) {
+  // Pick the tile so the grid still covers the 256 CUs: wide token tiles only when there are
+  // enough feature tiles.
+  const int tiles128 = (a.N / 64) * ((a.n_tok + 127) / 128);
+  if (a.n_tok >= 128 && tiles128 >= 512) launch_cfg<64, 128, EPI>(a, s);
+  else launch_cfg<64, 64, EPI>(a, s);
+}
+
+}  // namespace
+
+void launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE_F32: launch_epi<EPI_STORE_F32>(a, s); break;
+    case EPI_ADD_F32: launch_epi<EPI_ADD_F32>(a, s); break;
+    case EPI_SWIGLU_BF16: launch_cfg<64, 64, EPI_SWIGLU_BF16>(a, s); break;
+    default: launch_epi<EPI_STORE_BF16>(a, s); break;
+  }
+}
+
+void launch_head(const HeadArgs& a, hipStream_t s) {
+  constexpr int BF = 128, BT = 64;
+  const int G = ((a.n_rows + BT - 1) / BT) * (a.V / BF);
+  hipLaunchKernelGGL((head_kernel<BF, BT>), dim3(G), dim3(256), 0, s, a);
+}
+
+void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
+                       const int32_t* cur_tok, int32_t* cand, float* t_cand, float* t_cur,
+                       float* lse, float* ent, hipStream_t s) {
+  hipLaunchKernelGGL(head_merge_kernel, dim3(n_rows), dim3(64), 0, s, part, n_rows, n_slices,
+                     slice_w, cur_tok, cand, t_cand, t_cur, lse, ent);
+}
+
+}  // namespace dg

@@ -1,0 +1,320 @@
+"""ctypes binding of libdg (include/dg.h).  Argument marshalling only: every step of the denoise
+path runs in the HIP kernels of libdg.so.  PyTorch supplies device memory and the stream.
+
+Loading fails loudly (ImportError) when libdg.so has not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m block_discrete_diffusion_amd.build_lib` (hipcc, gfx950)")
+_lib = C.CDLL(LIB_PATH)
+
+DG_OK, DG_ERR_ARG, DG_ERR_SHAPE, DG_ERR_CAPACITY, DG_ERR_HIP, DG_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+DG_STEP_HIDDEN_IN, DG_STEP_NO_HEAD, DG_STEP_HEAD_ONLY = 1, 2, 4
+
+EXPORTS = ["dg_create", "dg_destroy", "dg_last_error", "dg_temperature", "dg_prefill_causal",
+           "dg_canvas_init", "dg_denoise_step", "dg_sample_commit", "dg_commit_block",
+           "dg_timing_enable", "dg_timing_read", "dg_debug_set_canvas_kv"]
+
+vp = C.c_void_p
+
+
+class ModelDesc(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim",
+                                         "n_experts", "top_k", "d_ff_expert", "d_ff_shared", "vocab",
+                                         "canvas")] + [("rms_eps", C.c_float), ("rope_theta", C.c_float)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(n, vp) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_router", "w_gate",
+                                  "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
+
+
+class Weights(C.Structure):
+    _fields_ = [("embed", vp), ("final_norm", vp), ("lm_head", vp), ("layers", C.POINTER(LayerWeights))]
+
+
+class KVCache(C.Structure):
+    _fields_ = [("k", vp), ("v", vp), ("cap", C.c_int32), ("batch", C.c_int32), ("len", C.POINTER(C.c_int32))]
+
+
+class CanvasState(C.Structure):
+    _fields_ = [("tokens", vp), ("committed", vp), ("stable_run", vp), ("stopped", vp)]
+
+
+class RowStats(C.Structure):
+    _fields_ = [("cand", vp), ("t_cand", vp), ("t_cur", vp), ("lse", vp), ("entropy", vp)]
+
+
+class SamplerCfg(C.Structure):
+    _fields_ = [("max_steps", C.c_int32), ("temp_start", C.c_float), ("temp_end", C.c_float),
+                ("commit_per_step", C.c_int32), ("renoise_conf", C.c_float), ("stable_steps", C.c_int32),
+                ("entropy_stop", C.c_float), ("renoise_committed", C.c_int32), ("seed", C.c_uint64)]
+
+
+class Debug(C.Structure):
+    _fields_ = [(n, vp) for n in ("hidden_out", "attn_out", "h_mid", "expert_idx", "gates", "logits",
+                                  "canvas_k", "canvas_v")]
+
+
+class StepParams(C.Structure):
+    _fields_ = [("step", C.c_int32), ("flags", C.c_uint32), ("hidden_in", vp), ("debug", C.POINTER(Debug))]
+
+
+class KernelTime(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("launches", C.c_int32), ("total_ms", C.c_float)]
+
+
+STATUS_FIELDS = ("changed", "n_committed", "n_new", "n_renoised", "stable_run", "stop", "nonfinite")
+
+_lib.dg_create.argtypes = [C.POINTER(ModelDesc), C.POINTER(Weights), C.c_int32, C.c_int32, C.POINTER(vp)]
+_lib.dg_create.restype = C.c_int
+_lib.dg_destroy.argtypes = [vp]
+_lib.dg_destroy.restype = None
+_lib.dg_last_error.argtypes = [vp]
+_lib.dg_last_error.restype = C.c_char_p
+_lib.dg_temperature.argtypes = [C.POINTER(SamplerCfg), C.c_int32]
+_lib.dg_temperature.restype = C.c_float
+_lib.dg_prefill_causal.argtypes = [vp, vp, C.POINTER(C.c_int32), C.c_int32, C.POINTER(KVCache), vp]
+_lib.dg_canvas_init.argtypes = [vp, C.POINTER(CanvasState), C.POINTER(KVCache), C.POINTER(SamplerCfg), vp]
+_lib.dg_denoise_step.argtypes = [vp, vp, C.POINTER(KVCache), C.POINTER(SamplerCfg), C.POINTER(StepParams),
+                                 C.POINTER(RowStats), vp]
+_lib.dg_sample_commit.argtypes = [vp, C.POINTER(CanvasState), C.POINTER(RowStats), C.POINTER(SamplerCfg),
+                                  C.c_int32, C.POINTER(KVCache), vp, vp]
+_lib.dg_commit_block.argtypes = [vp, vp, C.POINTER(KVCache), C.c_int32, vp]
+_lib.dg_debug_set_canvas_kv.argtypes = [vp, vp, vp, C.c_int32, vp]
+_lib.dg_timing_enable.argtypes = [vp, C.c_int32]
+_lib.dg_timing_read.argtypes = [vp, C.POINTER(KernelTime), C.c_int32]
+for _n in ("dg_timing_enable", "dg_timing_read", "dg_prefill_causal", "dg_canvas_init", "dg_denoise_step", "dg_sample_commit",
+           "dg_commit_block", "dg_debug_set_canvas_kv"):
+    getattr(_lib, _n).restype = C.c_int
+
+
+class DGError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libdg error {code}: {msg}")
+        self.code = code
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def to_device_bf16(x, device) -> torch.Tensor:
+    """float32 array of bf16-exact values (or a bf16 tensor) → contiguous bf16 device tensor."""
+    if isinstance(x, torch.Tensor):
+        return x.to(device=device, dtype=torch.bfloat16).contiguous()
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    bits = (a.view(np.uint32) >> 16).astype(np.uint16)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device).contiguous()
+
+
+def sampler_cfg(max_steps=48, temp_start=0.8, temp_end=0.4, commit_per_step=16, renoise_conf=0.1,
+                stable_steps=2, entropy_stop=-1.0, renoise_committed=True, seed=0) -> SamplerCfg:
+    return SamplerCfg(int(max_steps), float(temp_start), float(temp_end), int(commit_per_step),
+                      float(renoise_conf), int(stable_steps), float(entropy_stop),
+                      int(bool(renoise_committed)), int(seed) & ((1 << 64) - 1))
+
+
+def temperature(cfg: SamplerCfg, step: int) -> float:
+    return float(_lib.dg_temperature(C.byref(cfg), int(step)))
+
+
+class KV:
+    """bf16 KV cache [n_layers][batch][Hkv][cap][D] on the device + host lengths."""
+
+    def __init__(self, shape, batch: int, cap: int, device="cuda", fill: Optional[float] = 0.0):
+        dims = (shape.n_layers, batch, shape.n_kv_heads, cap, shape.head_dim)
+        self.k = torch.empty(dims, dtype=torch.bfloat16, device=device)
+        self.v = torch.empty(dims, dtype=torch.bfloat16, device=device)
+        if fill is not None:
+            self.k.fill_(fill)
+            self.v.fill_(fill)
+        self.len = (C.c_int32 * batch)(*([0] * batch))
+        self.c = KVCache(_ptr(self.k), _ptr(self.v), cap, batch, C.cast(self.len, C.POINTER(C.c_int32)))
+
+    @property
+    def lengths(self) -> List[int]:
+        return list(self.len)
+
+    def set_lengths(self, lens: Sequence[int]):
+        for b, v in enumerate(lens):
+            self.len[b] = int(v)
+
+
+class Canvas:
+    def __init__(self, batch: int, canvas: int, device="cuda"):
+        self.tokens = torch.zeros((batch, canvas), dtype=torch.int32, device=device)
+        self.committed = torch.zeros((batch, canvas), dtype=torch.uint8, device=device)
+        self.stable_run = torch.zeros((batch,), dtype=torch.int32, device=device)
+        self.stopped = torch.zeros((batch,), dtype=torch.int32, device=device)
+        self.c = CanvasState(_ptr(self.tokens), _ptr(self.committed), _ptr(self.stable_run),
+                             _ptr(self.stopped))
+
+
+class Stats:
+    def __init__(self, batch: int, canvas: int, device="cuda"):
+        z = lambda dt: torch.zeros((batch, canvas), dtype=dt, device=device)
+        self.cand = z(torch.int32)
+        self.t_cand, self.t_cur, self.lse, self.entropy = (z(torch.float32) for _ in range(4))
+        self.c = RowStats(_ptr(self.cand), _ptr(self.t_cand), _ptr(self.t_cur), _ptr(self.lse),
+                          _ptr(self.entropy))
+
+
+def status_dict(raw: torch.Tensor) -> List[Dict]:
+    """Decode a [batch][8] int32 status tensor (dg_step_status) on the host."""
+    a = raw.cpu().numpy()
+    out = []
+    for row in a:
+        d = {k: int(row[i]) for i, k in enumerate(STATUS_FIELDS)}
+        d["mean_entropy"] = float(row[7:8].view(np.float32)[0])
+        out.append(d)
+    return out
+
+
+class Model:
+    """Device weights + a libdg context.
+
+    weights: dict as produced by synth.model_weights (float32 bf16-exact numpy arrays) or
+    synth.torch_model_weights (device tensors)."""
+
+    def __init__(self, shape, weights: Dict, max_batch: int = 1, max_prefill_rows: int = 2048,
+                 device="cuda"):
+        self.shape = shape
+        self.device = device
+        dev = torch.device(device)
+        f32 = lambda x: (x if isinstance(x, torch.Tensor) else torch.from_numpy(np.asarray(x, np.float32))).to(
+            dev, torch.float32).contiguous()
+        self.t = {"embed": to_device_bf16(weights["embed"], dev), "final_norm": f32(weights["final_norm"]),
+                  "lm_head": to_device_bf16(weights["lm_head"], dev), "layers": []}
+        arr = (LayerWeights * shape.n_layers)()
+        for l, lw in enumerate(weights["layers"]):
+            t = {}
+            for k, v in lw.items():
+                t[k] = f32(v) if k.endswith("norm") else to_device_bf16(v, dev)
+            self.t["layers"].append(t)
+            get = lambda k: _ptr(t.get(k))
+            arr[l] = LayerWeights(get("attn_norm"), get("wq"), get("wk"), get("wv"), get("wo"),
+                                  get("ffn_norm"), get("w_router"), get("w_gate"), get("w_up"),
+                                  get("w_down"), get("ws_gate"), get("ws_up"), get("ws_down"))
+        self._layers = arr
+        self.w = Weights(_ptr(self.t["embed"]), _ptr(self.t["final_norm"]), _ptr(self.t["lm_head"]), arr)
+        self.desc = ModelDesc(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                              shape.n_experts, shape.top_k, shape.d_ff_expert, shape.d_ff_shared, shape.vocab,
+                              shape.canvas, float(shape.rms_eps), float(shape.rope_theta))
+        h = C.c_void_p()
+        rc = _lib.dg_create(C.byref(self.desc), C.byref(self.w), int(max_batch), int(max_prefill_rows),
+                            C.byref(h))
+        if rc != DG_OK:
+            raise DGError(rc, _lib.dg_last_error(None).decode())
+        self.ctx = h
+        self.max_batch = max_batch
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            _lib.dg_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, rc: int):
+        if rc != DG_OK:
+            raise DGError(rc, _lib.dg_last_error(self.ctx).decode())
+
+    # ---------------------------------------------------------------- entry points
+    def prefill(self, tokens: torch.Tensor, n_new: Sequence[int], kv: KV):
+        n = (C.c_int32 * len(n_new))(*[int(v) for v in n_new])
+        self._check(_lib.dg_prefill_causal(self.ctx, _ptr(tokens), n, len(n_new), C.byref(kv.c), _stream()))
+
+    def canvas_init(self, state: Canvas, kv: KV, cfg: SamplerCfg):
+        self._check(_lib.dg_canvas_init(self.ctx, C.byref(state.c), C.byref(kv.c), C.byref(cfg), _stream()))
+
+    def denoise_step(self, canvas: Optional[torch.Tensor], kv: KV, cfg: Optional[SamplerCfg], step: int,
+                     out: Optional[Stats], flags: int = 0, hidden_in: Optional[torch.Tensor] = None,
+                     debug: Optional[Dict[str, torch.Tensor]] = None):
+        dbg = None
+        if debug:
+            dbg = Debug(*[_ptr(debug.get(n)) for n, _ in Debug._fields_])
+        p = StepParams(int(step), int(flags), _ptr(hidden_in), C.pointer(dbg) if dbg is not None else None)
+        self._check(_lib.dg_denoise_step(self.ctx, _ptr(canvas), C.byref(kv.c),
+                                         C.byref(cfg) if cfg is not None else None, C.byref(p),
+                                         C.byref(out.c) if out is not None else None, _stream()))
+
+    def sample_commit(self, state: Canvas, stats: Stats, cfg: SamplerCfg, step: int, kv: KV,
+                      status: torch.Tensor):
+        self._check(_lib.dg_sample_commit(self.ctx, C.byref(state.c), C.byref(stats.c), C.byref(cfg),
+                                          int(step), C.byref(kv.c), _ptr(status), _stream()))
+
+    def commit_block(self, canvas: torch.Tensor, kv: KV, refresh: bool):
+        self._check(_lib.dg_commit_block(self.ctx, _ptr(canvas), C.byref(kv.c), int(bool(refresh)), _stream()))
+
+    def timing(self, enable: bool):
+        self._check(_lib.dg_timing_enable(self.ctx, int(bool(enable))))
+
+    def timing_read(self) -> Dict[str, Dict]:
+        """{kernel family: {"launches": n, "total_ms": t, "avg_ms": t/n}} since the last read."""
+        buf = (KernelTime * 64)()
+        n = _lib.dg_timing_read(self.ctx, buf, 64)
+        if n < 0:
+            self._check(n)
+        return {buf[i].name.decode(): {"launches": buf[i].launches, "total_ms": buf[i].total_ms,
+                                       "avg_ms": buf[i].total_ms / max(1, buf[i].launches)} for i in range(n)}
+
+    def set_canvas_kv(self, k: torch.Tensor, v: torch.Tensor, batch: int):
+        self._check(_lib.dg_debug_set_canvas_kv(self.ctx, _ptr(k), _ptr(v), int(batch), _stream()))
+
+    # ---------------------------------------------------------------- block-AR driver
+    def denoise_canvas(self, state: Canvas, kv: KV, cfg: SamplerCfg, stats: Optional[Stats] = None,
+                       on_step=None) -> Dict:
+        """Run the sampling loop on every canvas of `state` until all requests stop.  One pinned
+        32-byte-per-request status read per step is the only host synchronisation."""
+        B = kv.c.batch
+        stats = stats or Stats(B, self.shape.canvas, self.device)
+        status = torch.zeros((B, 8), dtype=torch.int32, device=self.device)
+        host = torch.zeros((B, 8), dtype=torch.int32, pin_memory=True)
+        steps, last = 0, None
+        for s in range(cfg.max_steps):
+            self.denoise_step(state.tokens, kv, cfg, s, stats)
+            self.sample_commit(state, stats, cfg, s, kv, status)
+            host.copy_(status, non_blocking=True)
+            torch.cuda.current_stream().synchronize()
+            last = status_dict(host)
+            steps += 1
+            if on_step:
+                on_step(s, last)
+            if all(d["stop"] for d in last):
+                break
+        return {"steps": steps, "status": last}
+
+    def generate(self, prefix: torch.Tensor, n_prefix: Sequence[int], n_blocks: int, cfg: SamplerCfg,
+                 kv: KV) -> List[torch.Tensor]:
+        """Prefill, then denoise and commit `n_blocks` canvases ([GUIDE] block-autoregressive)."""
+        B = len(n_prefix)
+        self.prefill(prefix, n_prefix, kv)
+        blocks = []
+        for _ in range(n_blocks):
+            st = Canvas(B, self.shape.canvas, self.device)
+            self.canvas_init(st, kv, cfg)
+            res = self.denoise_canvas(st, kv, cfg)
+            refresh = any(d["changed"] for d in res["status"])
+            self.commit_block(st.tokens, kv, refresh)
+            blocks.append(st.tokens.clone())
+        return blocks

@@ -62,16 +62,15 @@ FULL = ModelShape(n_layers=12, d_model=2048, n_q_heads=16, n_kv_heads=8, head_di
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even); return float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    out = r.astype(np.uint32).view(np.float32)
-    # keep NaN payloads as NaN (none are generated, but do not turn them into inf)
-    nan = np.isnan(x)
+    """Round float32 values to the nearest bfloat16 (ties to even); return float32 (new array)."""
+    out = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = out.view(np.uint32)
+    nan = np.isnan(out)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    lsb += np.uint32(0x7FFF)
+    u += lsb          # finite values: no uint32 overflow (|x| <= max float)
+    u &= np.uint32(0xFFFF0000)
     if nan.any():
-        out = out.copy()
         out[nan] = np.nan
     return out
 

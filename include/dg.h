@@ -1,0 +1,243 @@
+/*
+ * dg.h — C ABI of libdg: the denoise step of a block-autoregressive, uniform-state
+ * discrete-diffusion language model on AMD MI355X (gfx950).
+ *
+ * The method (sources cited by tag; the pages are):
+ *   [GUIDE] "DiffusionGemma Guia do Desenvolvedor para Decodificação Paralela a 1000+ Tokens/s"
+ *           (dev.infolabhq.com), sections "Arquitetura em Detalhes" and the Sudoku demo;
+ *   [NEWS]  "Google's DiffusionGemma Atinge 1.000 Tokens por Segundo" (aiexpert.news), 2nd ¶;
+ *   [RANK]  "DiffusionGemma: geração de texto até 4x mais rápida…" (pulsar-ranking.com),
+ *           "Pontos-chave";
+ *   [DOCS]  Google's DiffusionGemma documentation (ai.google.dev/gemma/docs/diffusiongemma),
+ *           feature list and table "Configuração de exibição recomendada".
+ *
+ * A prompt is prefilled causally into a KV cache ([GUIDE] "Arquitetura em Detalhes"; [NEWS]).
+ * A canvas of 256 random tokens is then refined in parallel: each denoise step is one forward
+ * pass in which every canvas position attends, unmasked, to the cached prefix and to the whole
+ * canvas ([GUIDE] Sudoku demo; [RANK]; [DOCS] feature list), followed by a sampler that draws a
+ * candidate per position at a falling temperature, commits the most confident positions and
+ * puts random tokens back where confidence is low ([NEWS]; [DOCS] table).  A finished canvas is
+ * appended to the KV cache and the next one starts ([GUIDE]; [NEWS]; [DOCS] feature list).
+ *
+ * Conventions for every function below:
+ *  - Pointers are DEVICE memory unless marked (host).  bf16 tensors are passed as uint16_t
+ *    (the upper half of an IEEE float32); all matrices are row-major, [out][in].
+ *  - The caller owns every buffer it passes; libdg never frees caller memory.  libdg owns the
+ *    context and a workspace it allocates in dg_create (activations, per-layer canvas K/V,
+ *    split-attention partials, MoE routing tables) and frees in dg_destroy.
+ *  - Calls are asynchronous on `stream` (hipStream_t).  No call synchronizes the stream.
+ *  - Every argument and shape is validated BEFORE anything is enqueued: a non-zero return
+ *    leaves the device untouched.  dg_last_error() returns the message of the last failure.
+ *  - Device-side conditions (non-finite logits) are reported in dg_step_status, not as errors.
+ *  - A context is not thread-safe; use one context per stream.  Kernels are deterministic:
+ *    the same inputs give bit-identical outputs (no floating-point atomics).
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dg_ctx dg_ctx;
+
+enum {
+  DG_OK = 0,
+  DG_ERR_ARG = -1,         /* null pointer / bad value */
+  DG_ERR_SHAPE = -2,       /* shape not supported by the kernels (see dg_create) */
+  DG_ERR_CAPACITY = -3,    /* KV cache or workspace too small for the request */
+  DG_ERR_HIP = -4,         /* HIP runtime error (message in dg_last_error) */
+  DG_ERR_UNSUPPORTED = -5  /* flag combination not supported */
+};
+
+/* Model shape.  Supported: head_dim 64 or 128; d_model, n_q_heads*head_dim, d_ff_expert and
+ * d_ff_shared multiples of 64; n_q_heads a multiple of n_kv_heads; 1 <= top_k <= n_experts
+ * <= 64; vocab a multiple of 128; canvas == 256 ([GUIDE] "Arquitetura em Detalhes": fixed
+ * 256-token blocks).  rope_theta 0 disables RoPE (rotate-half, absolute positions). */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_experts, top_k, d_ff_expert, d_ff_shared /* 0 = no shared FFN */, vocab, canvas;
+  float rms_eps, rope_theta;
+} dg_model_desc;
+
+/* One decoder layer (pre-norm attention block, then routed MoE FFN + optional shared FFN).
+ * Norm gains are float32 [d_model]; every matrix is bf16 row-major [out][in]. */
+typedef struct {
+  const float* attn_norm;
+  const uint16_t* wq;       /* [n_q_heads*head_dim][d_model] */
+  const uint16_t* wk;       /* [n_kv_heads*head_dim][d_model] */
+  const uint16_t* wv;       /* [n_kv_heads*head_dim][d_model] */
+  const uint16_t* wo;       /* [d_model][n_q_heads*head_dim] */
+  const float* ffn_norm;
+  const uint16_t* w_router; /* [n_experts][d_model] */
+  const uint16_t* w_gate;   /* [n_experts][d_ff_expert][d_model] */
+  const uint16_t* w_up;     /* [n_experts][d_ff_expert][d_model] */
+  const uint16_t* w_down;   /* [n_experts][d_model][d_ff_expert] */
+  const uint16_t* ws_gate;  /* [d_ff_shared][d_model], NULL when d_ff_shared == 0 */
+  const uint16_t* ws_up;    /* [d_ff_shared][d_model] */
+  const uint16_t* ws_down;  /* [d_model][d_ff_shared] */
+} dg_layer_weights;
+
+typedef struct {
+  const uint16_t* embed;          /* [vocab][d_model] */
+  const float* final_norm;        /* [d_model] */
+  const uint16_t* lm_head;        /* [vocab][d_model] (untied) */
+  const dg_layer_weights* layers; /* (host) [n_layers]; copied by dg_create */
+} dg_weights;
+
+/* KV cache: bf16 K (after RoPE) and V, layout [n_layers][batch][n_kv_heads][cap][head_dim].
+ * len (host) holds each request's committed length; dg_prefill_causal and dg_commit_block
+ * advance it when they enqueue their work. */
+typedef struct {
+  uint16_t* k;
+  uint16_t* v;
+  int32_t cap;
+  int32_t batch;
+  int32_t* len; /* (host) [batch] */
+} dg_kv_cache;
+
+/* Sampler state of `batch` canvases ([NEWS] 2nd ¶: committed anchors; re-noising). */
+typedef struct {
+  int32_t* tokens;     /* [batch][canvas] current token per slot */
+  uint8_t* committed;  /* [batch][canvas] 1 = committed */
+  int32_t* stable_run; /* [batch] consecutive steps that changed no token */
+  int32_t* stopped;    /* [batch] 1 once the request's sampler has stopped; its canvas is then
+                          left untouched by further sampler steps */
+} dg_canvas_state;
+
+/* Per-position statistics written by dg_denoise_step, consumed by dg_sample_commit.
+ * With t = logits / T: cand = argmax(t + Gumbel), t_cand = t[cand], t_cur = t[current token],
+ * lse = log-sum-exp(t), entropy of softmax(t).  Each [batch][canvas]. */
+typedef struct {
+  int32_t* cand;
+  float* t_cand;
+  float* t_cur;
+  float* lse;
+  float* entropy;
+} dg_row_stats;
+
+/* Sampler parameters ([DOCS] table "Configuração de exibição recomendada": 48 steps,
+ * temperature linear 0.8 -> 0.4; commit/re-noise/stop readings documented in the oracle). */
+typedef struct {
+  int32_t max_steps;         /* 48 */
+  float temp_start;          /* 0.8 */
+  float temp_end;            /* 0.4 */
+  int32_t commit_per_step;   /* 16 */
+  float renoise_conf;        /* 0.1: re-noise when the tempered probability is below this */
+  int32_t stable_steps;      /* 2: stop after this many consecutive unchanged steps */
+  float entropy_stop;        /* < 0 off; else also stop when mean entropy < it and unchanged */
+  int32_t renoise_committed; /* 1: committed positions whose confidence drops are re-noised */
+  uint64_t seed;
+} dg_sampler_cfg;
+
+/* Per-request result of dg_sample_commit (device [batch]). */
+typedef struct {
+  int32_t changed, n_committed, n_new, n_renoised, stable_run, stop, nonfinite;
+  float mean_entropy;
+} dg_step_status;
+
+/* Optional per-step dumps (device buffers; any may be NULL).  Row index r = b*canvas + i. */
+typedef struct {
+  float* hidden_out;       /* [rows][d_model] residual stream after the last layer */
+  uint16_t* attn_out;      /* [n_layers][rows][n_q_heads*head_dim] attention output (bf16) */
+  float* h_mid;            /* [n_layers][rows][d_model] residual after the attention block */
+  int32_t* expert_idx;     /* [n_layers][rows][top_k] */
+  float* gates;            /* [n_layers][rows][top_k] */
+  float* logits;           /* [rows][vocab] raw logits (test sizes only) */
+  uint16_t* canvas_k;      /* [n_layers][batch][n_kv_heads][canvas][head_dim] */
+  uint16_t* canvas_v;      /* same */
+} dg_debug;
+
+enum {
+  DG_STEP_HIDDEN_IN = 1u << 0, /* hidden_in = float32 [rows][d_model] replaces the embedding */
+  DG_STEP_NO_HEAD = 1u << 1,   /* run the layers only (no vocab projection, no row stats) */
+  DG_STEP_HEAD_ONLY = 1u << 2  /* hidden_in = bf16 [rows][d_model] already-normed final state;
+                                  only the vocab projection + row statistics run */
+};
+
+typedef struct {
+  int32_t step;          /* denoise step s (selects the temperature and the RNG counter) */
+  uint32_t flags;        /* DG_STEP_* */
+  const void* hidden_in; /* see flags */
+  const dg_debug* debug; /* (host) optional, may be NULL */
+} dg_step_params;
+
+/* Create a context for `desc` over caller-owned device weights.  max_batch: largest batch
+ * (<= 64) of later calls; max_prefill_rows: largest prefill chunk processed at once (rows are
+ * split into chunks of this size).  Returns DG_OK and *out, or an error code. */
+int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_batch,
+              int32_t max_prefill_rows, dg_ctx** out);
+void dg_destroy(dg_ctx* ctx);
+/* Message of the last failure on ctx (or of the last dg_create failure when ctx is NULL). */
+const char* dg_last_error(const dg_ctx* ctx);
+/* The temperature of step `step`: T0 + (T1 - T0) * step / (max_steps - 1), rounded to float32
+ * once ([DOCS] table, temperature row). */
+float dg_temperature(const dg_sampler_cfg* cfg, int32_t step);
+
+/* Causal prefill ([GUIDE] "Arquitetura em Detalhes"; [NEWS] 2nd ¶; [DOCS] autoregressive
+ * encoder): request b's n_new[b] tokens (packed back to back in `tokens`, device int32) are
+ * placed at positions len[b] .. len[b]+n_new[b]-1; each attends to its cached history and to
+ * itself and earlier new tokens.  Every layer's K (after RoPE) and V are written into the cache
+ * and len[b] advances by n_new[b].  Needs len[b] + n_new[b] <= cap.  n_new: (host) [batch]. */
+int dg_prefill_causal(dg_ctx* ctx, const int32_t* tokens, const int32_t* n_new, int32_t batch,
+                      dg_kv_cache* kv, hipStream_t stream);
+
+/* Uniform-state canvas start ([GUIDE] "Arquitetura em Detalhes"): slot i of request b gets the
+ * uniform token Philox(seed; 0, len[b]+i, 0, (b<<8)|2) -> (w*V)>>32; committed = 0;
+ * stable_run = 0; stopped = 0. */
+int dg_canvas_init(dg_ctx* ctx, dg_canvas_state* state, const dg_kv_cache* kv,
+                   const dg_sampler_cfg* cfg, hipStream_t stream);
+
+/* One denoise forward pass over the canvases `canvas` ([batch][canvas] device int32) of the
+ * kv->batch requests: canvas slot i sits at position len[b]+i and attends, with no mask, to
+ * cache[0:len[b]] and to all canvas slots; top-k MoE FFN; final norm; vocab projection fused
+ * with temperature, log-sum-exp, entropy and the Gumbel-max draw (logits never reach HBM).
+ * Writes `out` (unless DG_STEP_NO_HEAD) and keeps every layer's canvas K/V in the workspace
+ * for dg_commit_block.  cfg supplies the temperature schedule and the seed. */
+int dg_denoise_step(dg_ctx* ctx, const int32_t* canvas, const dg_kv_cache* kv,
+                    const dg_sampler_cfg* cfg, const dg_step_params* params,
+                    dg_row_stats* out, hipStream_t stream);
+
+/* Sampler step `step` on every canvas ([NEWS] 2nd ¶; [GUIDE] Sudoku demo; [DOCS] table):
+ * commit the min(commit_per_step, #uncommitted) uncommitted slots with the highest candidate
+ * log-confidence t_cand - lse (lowest slot on ties); re-noise committed slots whose current
+ * log-confidence fell below log(renoise_conf) (if renoise_committed); other uncommitted slots
+ * take their candidate if its log-confidence >= log(renoise_conf), else a fresh uniform token
+ * Philox(seed; 0, pos, step, (b<<8)|1).  Updates state and writes status[batch].  A request
+ * whose `stopped` flag is already set is left unchanged (status: stop 1, changed 0). */
+int dg_sample_commit(dg_ctx* ctx, dg_canvas_state* state, const dg_row_stats* stats,
+                     const dg_sampler_cfg* cfg, int32_t step, const dg_kv_cache* kv,
+                     dg_step_status* status, hipStream_t stream);
+
+/* Append each finished canvas's K/V to the cache at [len[b], len[b]+canvas) and advance len
+ * ([GUIDE] "Arquitetura em Detalhes"; [NEWS] 2nd ¶).  The K/V are the ones the last
+ * dg_denoise_step computed; refresh != 0 first re-runs the layers (no head) on `canvas`
+ * ([batch][canvas] device int32), needed when the last sampler step changed the canvas.  The
+ * copy is bit-exact; nothing outside the appended slices is written. */
+int dg_commit_block(dg_ctx* ctx, const int32_t* canvas, dg_kv_cache* kv, int32_t refresh,
+                    hipStream_t stream);
+
+/* Per-kernel device timing for measurement runs: while enabled, every kernel launch is
+ * bracketed by HIP events recorded on its launch stream.  dg_timing_read waits for the recorded
+ * events, writes up to `max` per-kernel-family totals (name is a static string) and clears the
+ * record.  Returns the number of entries written, or a negative dg_status. */
+typedef struct {
+  const char* name;
+  int32_t launches;
+  float total_ms;
+} dg_kernel_time;
+int dg_timing_enable(dg_ctx* ctx, int32_t enable);
+int dg_timing_read(dg_ctx* ctx, dg_kernel_time* out, int32_t max);
+
+/* Test hook: load canvas K/V ([n_layers][batch][n_kv_heads][canvas][head_dim] bf16) into the
+ * workspace, as if a denoise step had produced them. */
+int dg_debug_set_canvas_kv(dg_ctx* ctx, const uint16_t* k, const uint16_t* v, int32_t batch,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H_ */

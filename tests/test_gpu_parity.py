@@ -1,0 +1,351 @@
+"""GPU vs oracle parity on the small configuration (2 layers, d 256, 4/2 heads, D 64, 8 experts
+top-2, F 512, V 1024, prefix 64, one 256-token canvas).  Every call goes through the C ABI."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from block_discrete_diffusion_amd import synth
+from oracle import model as omodel
+from oracle import sampler as osampler
+from tests.gpu_common import (MARGIN, ROUTER_BOUND, bf16_to_np, check_topk, close, load_cache,
+                              need_gpu, np_bf16_dev, oracle_cfg, random_cache, topk_margin)
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = synth.TINY
+L = 64
+SEED = 20260610
+
+
+@pytest.fixture(scope="module")
+def env():
+    dg = need_gpu()
+    w = synth.model_weights(SHAPE, SEED)
+    m = dg.Model(SHAPE, w, max_batch=2, max_prefill_rows=512)
+    yield dg, w, m
+    m.close()
+
+
+def _kv(dg, cap=L + 512, batch=1, seed=7):
+    kv = dg.KV(SHAPE, batch, cap)
+    k, v = random_cache(SHAPE, L, cap, seed, batch)
+    load_cache(kv, k, v, [L] * batch)
+    return kv, k, v
+
+
+def test_canvas_init_bitexact(env):
+    dg, w, m = env
+    kv, _, _ = _kv(dg, batch=2)
+    kv.set_lengths([L, L + 256])
+    st = dg.Canvas(2, 256)
+    cfg = dg.sampler_cfg(seed=123456789012345)
+    m.canvas_init(st, kv, cfg)
+    torch.cuda.synchronize()
+    for b, Lb in enumerate([L, L + 256]):
+        want = osampler.canvas_init(cfg.seed, b, Lb + np.arange(256), SHAPE.vocab)
+        assert np.array_equal(st.tokens[b].cpu().numpy(), want)
+    assert not st.committed.any() and not st.stable_run.any() and not st.stopped.any()
+
+
+@pytest.mark.parametrize("step", [0, 17, 47])
+def test_head_decisions_and_stats(env, step):
+    """Teacher-forced head: identical bf16 final states f and W_out on both sides."""
+    dg, w, m = env
+    kv, _, _ = _kv(dg)
+    f = synth.bf16_normal((256, SHAPE.d_model), SEED, 30 + step)
+    x = synth.tokens(256, SHAPE.vocab, SEED, 31 + step)
+    cfg = dg.sampler_cfg(seed=99 + step)
+    stats = dg.Stats(1, 256)
+    logits = torch.zeros((256, SHAPE.vocab), dtype=torch.float32, device="cuda")
+    tok = torch.from_numpy(x).cuda()
+    m.denoise_step(tok, kv, cfg, step, stats, flags=dg.DG_STEP_HEAD_ONLY, hidden_in=np_bf16_dev(f),
+                   debug={"logits": logits})
+    torch.cuda.synchronize()
+    oc = oracle_cfg(cfg)
+    z = omodel.head_logits(f, w["lm_head"])
+    close(logits.cpu().numpy(), z, what="logits")
+    T = osampler.temperature(oc, step)
+    assert np.float32(dg.temperature(cfg, step)) == T
+    want = osampler.row_stats(z, x, T, cfg.seed, 0, L + np.arange(256), step)
+    got_cand = stats.cand.cpu().numpy()[0]
+    ok = want["margin"] >= MARGIN
+    assert ok.mean() > 0.9
+    assert np.array_equal(got_cand[ok], want["cand"][ok])
+    for k in ("t_cand", "t_cur", "lse"):
+        close(getattr(stats, k).cpu().numpy()[0][ok], want[k][ok], max_abs=1e-3, rel_l2=1e-5, what=k)
+    close(stats.entropy.cpu().numpy()[0], want["entropy"], max_abs=1e-3, rel_l2=1e-4, what="entropy")
+
+
+def test_sampler_bitexact_over_steps(env):
+    """dg_sample_commit on identical float32 row statistics is bit-exact against the oracle."""
+    dg, w, m = env
+    kv, _, _ = _kv(dg, batch=2)
+    kv.set_lengths([L, 3 * L])
+    cfg = dg.sampler_cfg(seed=4242, max_steps=12, commit_per_step=16)
+    oc = oracle_cfg(cfg)
+    st = dg.Canvas(2, 256)
+    m.canvas_init(st, kv, cfg)
+    torch.cuda.synchronize()
+    o_state = []
+    for b, Lb in enumerate([L, 3 * L]):
+        o_state.append([osampler.canvas_init(cfg.seed, b, Lb + np.arange(256), SHAPE.vocab),
+                        np.zeros(256, bool), 0])
+    stats = dg.Stats(2, 256)
+    status = torch.zeros((2, 8), dtype=torch.int32, device="cuda")
+    for s in range(cfg.max_steps):
+        # confidences spread around log(0.1) so commit, keep and re-noise all occur
+        rs = {
+            "cand": synth.tokens(512, SHAPE.vocab, s, 1).reshape(2, 256),
+            "t_cand": synth.uniform((2, 256), -4.0, 0.5, s, 2),
+            "t_cur": synth.uniform((2, 256), -4.0, 0.5, s, 3),
+            "lse": synth.uniform((2, 256), 0.0, 0.5, s, 4),
+            "entropy": synth.uniform((2, 256), 0.0, 3.0, s, 5),
+        }
+        rs["t_cand"][:, ::7] = rs["t_cand"][:, 3:4]  # exact ties in the ranking
+        for k, v in rs.items():
+            getattr(stats, k).copy_(torch.from_numpy(np.ascontiguousarray(v)))
+        m.sample_commit(st, stats, cfg, s, kv, status)
+        torch.cuda.synchronize()
+        got = dg.status_dict(status)
+        for b, Lb in enumerate([L, 3 * L]):
+            ost = {k: rs[k][b] for k in rs}
+            x, com, sr, ostatus = osampler.sample_commit(ost, o_state[b][0], o_state[b][1], o_state[b][2],
+                                                        oc, s, b, Lb + np.arange(256), SHAPE.vocab)
+            o_state[b] = [x, com, sr]
+            assert np.array_equal(st.tokens[b].cpu().numpy(), x), (s, b)
+            assert np.array_equal(st.committed[b].cpu().numpy().astype(bool), com), (s, b)
+            assert int(st.stable_run[b]) == sr
+            for k in ("changed", "n_committed", "n_new", "n_renoised", "stable_run", "stop"):
+                assert got[b][k] == ostatus[k], (s, b, k)
+            assert abs(got[b]["mean_entropy"] - ostatus["mean_entropy"]) < 1e-5
+        if all(g["stop"] for g in got):
+            break
+
+
+def _layer_debug(dg, m, shape, rows, n_layers):
+    HD = shape.n_q_heads * shape.head_dim
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt, device="cuda")
+    return {
+        "hidden_out": z(rows, shape.d_model),
+        "attn_out": z(n_layers, rows, HD, dt=torch.bfloat16),
+        "h_mid": z(n_layers, rows, shape.d_model),
+        "expert_idx": z(n_layers, rows, shape.top_k, dt=torch.int32),
+        "gates": z(n_layers, rows, shape.top_k),
+        "canvas_k": z(n_layers, 1, shape.n_kv_heads, 256, shape.head_dim, dt=torch.bfloat16),
+        "canvas_v": z(n_layers, 1, shape.n_kv_heads, 256, shape.head_dim, dt=torch.bfloat16),
+    }
+
+
+def check_layer(dg, m, w, shape, Lp, seed, cap):
+    """One layer from a synthetic residual state: attention, FFN and canvas K/V vs the oracle."""
+    kv = dg.KV(shape, 1, cap)
+    k, v = random_cache(shape, Lp, cap, seed)
+    load_cache(kv, k, v, [Lp])
+    h = synth.hidden(256, shape.d_model, seed, 5)
+    dbg = _layer_debug(dg, m, shape, 256, shape.n_layers)
+    m.denoise_step(None, kv, None, 0, None, flags=dg.DG_STEP_HIDDEN_IN | dg.DG_STEP_NO_HEAD,
+                   hidden_in=torch.from_numpy(h).cuda(), debug=dbg)
+    torch.cuda.synchronize()
+    pos = Lp + np.arange(256)
+    h_out, ok_k, ok_v, od = omodel.layer(h, w["layers"][0], shape, pos, k[0, 0, :, :Lp], v[0, 0, :, :Lp], None)
+    close(bf16_to_np(dbg["attn_out"][0]), od["attn_out"], what="attention output")
+    close(dbg["h_mid"][0].cpu().numpy(), od["h_mid"], what="h after attention")
+    close(bf16_to_np(dbg["canvas_k"][0, 0]), ok_k, what="canvas K")
+    close(bf16_to_np(dbg["canvas_v"][0, 0]), ok_v, what="canvas V")
+    gi = dbg["expert_idx"][0].cpu().numpy()
+    safe = check_topk(gi, od["router_logits"], shape.top_k)
+    assert safe.mean() > 0.75, safe.mean()
+    order_ok = np.all(gi == od["expert_idx"], axis=1) & safe
+    close(dbg["gates"][0].cpu().numpy()[order_ok], od["gates"][order_ok], max_abs=1e-2, what="gates")
+    close(dbg["hidden_out"].cpu().numpy()[safe], h_out[safe], what="layer output")
+    close((dbg["hidden_out"].cpu().numpy() - dbg["h_mid"][0].cpu().numpy())[safe], od["ffn_out"][safe],
+          what="FFN output")
+
+
+def test_single_layer_parity(env):
+    dg, w, _ = env
+    shape = dataclasses.replace(SHAPE, n_layers=1)
+    w1 = dict(w)
+    w1["layers"] = w["layers"][:1]
+    m1 = dg.Model(shape, w1, max_batch=1)
+    try:
+        check_layer(dg, m1, w1, shape, L, SEED, L + 256)
+        check_layer(dg, m1, w1, shape, 0, SEED + 1, 256)       # no prefix: pure canvas attention
+        check_layer(dg, m1, w1, shape, 1000, SEED + 2, 1300)   # ragged prefix, several key tiles
+    finally:
+        m1.close()
+
+
+def test_full_step_parity(env):
+    """Tokens → 2 layers → head: continuous row statistics within the parity bar; decisions
+    compared where the oracle margin is safely away from a tie."""
+    dg, w, m = env
+    kv, k, v = _kv(dg)
+    x = synth.tokens(256, SHAPE.vocab, SEED, 40)
+    cfg = dg.sampler_cfg(seed=5)
+    stats = dg.Stats(1, 256)
+    logits = torch.zeros((256, SHAPE.vocab), dtype=torch.float32, device="cuda")
+    m.denoise_step(torch.from_numpy(x).cuda(), kv, cfg, 3, stats, debug={"logits": logits})
+    torch.cuda.synchronize()
+    fw = omodel.denoise_forward(w, SHAPE, x, [k[l, 0] for l in range(2)], [v[l, 0] for l in range(2)], L,
+                                keep_debug=True)
+    # rows whose expert choice is unique in every layer (no near-tie in the oracle's router)
+    safe = np.ones(256, bool)
+    for dl in fw["debug"]:
+        safe &= topk_margin(dl["router_logits"], SHAPE.top_k) >= ROUTER_BOUND
+    assert safe.mean() > 0.75, safe.mean()
+    # each sub-block meets the 2e-2 bar on identical inputs; end to end the per-block errors
+    # add up over the n_layers + 1 blocks on the path (rel-L2 keeps the 1e-2 bar)
+    close(logits.cpu().numpy()[safe], fw["logits"][safe], max_abs=2e-2 * (SHAPE.n_layers + 1),
+          what="logits (end to end)")
+    oc = oracle_cfg(cfg)
+    want = osampler.row_stats(fw["logits"], x, osampler.temperature(oc, 3), cfg.seed, 0, L + np.arange(256), 3)
+    close(stats.lse.cpu().numpy()[0][safe], want["lse"][safe], max_abs=2e-2, what="lse")
+    close(stats.t_cur.cpu().numpy()[0][safe], want["t_cur"][safe], max_abs=5e-2, what="t_cur")
+    agree = (stats.cand.cpu().numpy()[0] == want["cand"])
+    clear = safe & (want["margin"] >= 0.1)
+    assert agree[clear].mean() > 0.97, agree[clear].mean()
+
+
+def test_prefill_matches_oracle(env):
+    dg, w, m = env
+    toks = synth.tokens(L, SHAPE.vocab, SEED, 50)
+    kv = dg.KV(SHAPE, 1, L + 256)
+    m.prefill(torch.from_numpy(toks).cuda(), [L], kv)
+    torch.cuda.synchronize()
+    assert kv.lengths == [L]
+    ck = [np.zeros((2, L + 256, 64)) for _ in range(2)]
+    cv = [np.zeros((2, L + 256, 64)) for _ in range(2)]
+    omodel.prefill(w, SHAPE, toks, ck, cv, 0)
+    for l in range(2):
+        close(bf16_to_np(kv.k[l, 0, :, :L]), ck[l][:, :L], what=f"prefill K layer {l}")
+        close(bf16_to_np(kv.v[l, 0, :, :L]), cv[l][:, :L], what=f"prefill V layer {l}")
+
+
+def test_prefill_chunked_equals_whole(env):
+    dg, w, m = env
+    toks = synth.tokens(200, SHAPE.vocab, SEED, 51)
+    a = dg.KV(SHAPE, 1, 512)
+    m.prefill(torch.from_numpy(toks).cuda(), [200], a)
+    b = dg.KV(SHAPE, 1, 512)
+    m.prefill(torch.from_numpy(toks[:72]).cuda(), [72], b)
+    m.prefill(torch.from_numpy(toks[72:]).cuda(), [128], b)
+    torch.cuda.synchronize()
+    assert a.lengths == b.lengths == [200]
+    close(bf16_to_np(a.k[:, :, :, :200]), bf16_to_np(b.k[:, :, :, :200]), max_abs=2e-2, rel_l2=2e-3,
+          what="chunked prefill")
+
+
+def test_commit_block_bitexact_with_canaries(env):
+    dg, w, m = env
+    kv = dg.KV(SHAPE, 2, 1024, fill=None)
+    canary_k = synth.bf16_normal(tuple(kv.k.shape), 1, 60)
+    canary_v = synth.bf16_normal(tuple(kv.v.shape), 1, 61)
+    kv.k.copy_(np_bf16_dev(canary_k))
+    kv.v.copy_(np_bf16_dev(canary_v))
+    kv.set_lengths([L, 300])
+    src_k = synth.bf16_normal((2, 2, 2, 256, 64), 2, 62)
+    src_v = synth.bf16_normal((2, 2, 2, 256, 64), 2, 63)
+    m.set_canvas_kv(np_bf16_dev(src_k), np_bf16_dev(src_v), 2)
+    m.commit_block(None, kv, refresh=False)
+    torch.cuda.synchronize()
+    assert kv.lengths == [L + 256, 556]
+    want_k = [[canary_k[l, b] for b in range(2)] for l in range(2)]
+    ok = [[c.copy() for c in row] for row in want_k]
+    for l in range(2):
+        for b, Lb in enumerate([L, 300]):
+            ck = [canary_k[l, b].astype(np.float64)]
+            cv = [canary_v[l, b].astype(np.float64)]
+            omodel.commit_block(ck, cv, [src_k[l, b]], [src_v[l, b]], Lb)
+            assert np.array_equal(bf16_to_np(kv.k[l, b]), ck[0])
+            assert np.array_equal(bf16_to_np(kv.v[l, b]), cv[0])
+
+
+def test_commit_after_denoise_appends_the_step_kv(env):
+    dg, w, m = env
+    kv, k, v = _kv(dg, cap=L + 256)
+    x = torch.from_numpy(synth.tokens(256, SHAPE.vocab, SEED, 70)).cuda()
+    dbg = _layer_debug(dg, m, SHAPE, 256, 2)
+    cfg = dg.sampler_cfg(seed=1)
+    m.denoise_step(x, kv, cfg, 0, dg.Stats(1, 256), debug={"canvas_k": dbg["canvas_k"], "canvas_v": dbg["canvas_v"]})
+    m.commit_block(x, kv, refresh=False)
+    torch.cuda.synchronize()
+    assert torch.equal(kv.k[:, :, :, L:L + 256], dbg["canvas_k"])
+    assert torch.equal(kv.v[:, :, :, L:L + 256], dbg["canvas_v"])
+    assert torch.equal(kv.k[:, :, :, :L].cpu(), np_bf16_dev(k[:, :, :, :L]).cpu())
+    # the appended K/V are the oracle's canvas K/V of these tokens (parity bar)
+    fw = omodel.denoise_forward(w, SHAPE, x.cpu().numpy(), [k[l, 0] for l in range(2)],
+                                [v[l, 0] for l in range(2)], L, with_head=False)
+    for l in range(2):
+        close(bf16_to_np(kv.k[l, 0, :, L:L + 256]), fw["canvas_k"][l], what=f"appended K layer {l}")
+
+
+def test_refresh_recomputes_kv_of_final_canvas(env):
+    dg, w, m = env
+    kv, k, v = _kv(dg, cap=L + 256)
+    x0 = torch.from_numpy(synth.tokens(256, SHAPE.vocab, SEED, 71)).cuda()
+    x1 = torch.from_numpy(synth.tokens(256, SHAPE.vocab, SEED, 72)).cuda()
+    m.denoise_step(x0, kv, dg.sampler_cfg(), 0, dg.Stats(1, 256))
+    m.commit_block(x1, kv, refresh=True)
+    kv2, _, _ = _kv(dg, cap=L + 256)
+    m.denoise_step(x1, kv2, dg.sampler_cfg(), 0, dg.Stats(1, 256))
+    m.commit_block(x1, kv2, refresh=False)
+    torch.cuda.synchronize()
+    assert torch.equal(kv.k, kv2.k) and torch.equal(kv.v, kv2.v)
+
+
+def test_deterministic_bitwise(env):
+    dg, w, m = env
+    kv, _, _ = _kv(dg)
+    x = torch.from_numpy(synth.tokens(256, SHAPE.vocab, SEED, 80)).cuda()
+    cfg = dg.sampler_cfg(seed=77)
+    outs = []
+    for _ in range(2):
+        s = dg.Stats(1, 256)
+        m.denoise_step(x, kv, cfg, 5, s)
+        torch.cuda.synchronize()
+        outs.append([getattr(s, k).clone() for k in ("cand", "t_cand", "t_cur", "lse", "entropy")])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_peaked_head_stops_after_three_steps(env):
+    """End-to-end through head + sampler with the peaked fixture: f and W_out chosen so that the
+    logit of target_i is 50 and every other logit is 0 → exactly three steps."""
+    dg, w, m = env
+    d, V = SHAPE.d_model, SHAPE.vocab
+    target = synth.tokens(256, V, SEED, 90)
+    # f_i = e_{j(i)} * 1, W_out[v] = 50 * e_{j} for v == target of rows using basis j: use d >= 256
+    # distinct basis vectors, one per row, and give row i's target that vector.
+    W = np.zeros((V, d), np.float32)
+    f = np.zeros((256, d), np.float32)
+    # rows sharing a target share its basis vector
+    basis = {}
+    for i, t in enumerate(target):
+        j = basis.setdefault(int(t), len(basis))
+        f[i, j] = 1.0
+        W[t, j] = 50.0
+    m2 = dg.Model(SHAPE, {**w, "lm_head": W}, max_batch=1)
+    try:
+        kv, _, _ = _kv(dg)
+        cfg = dg.sampler_cfg(seed=3)
+        st = dg.Canvas(1, 256)
+        m2.canvas_init(st, kv, cfg)
+        stats = dg.Stats(1, 256)
+        status = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+        fdev = np_bf16_dev(f)
+        steps = 0
+        for s in range(48):
+            m2.denoise_step(st.tokens, kv, cfg, s, stats, flags=dg.DG_STEP_HEAD_ONLY, hidden_in=fdev)
+            m2.sample_commit(st, stats, cfg, s, kv, status)
+            torch.cuda.synchronize()
+            steps += 1
+            if dg.status_dict(status)[0]["stop"]:
+                break
+        assert steps == 3
+        assert np.array_equal(st.tokens[0].cpu().numpy(), target)
+        assert int(st.committed.sum()) == 48
+    finally:
+        m2.close()
