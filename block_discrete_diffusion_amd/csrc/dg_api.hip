@@ -75,6 +75,8 @@ struct dg_ctx {
   float* head_part = nullptr;  // [r_canvas][V/64][8]
   uint16_t* ck = nullptr;      // [L][max_batch][Hkv][C][D]
   uint16_t* cv = nullptr;
+  std::vector<uint16_t*> pk1;  // per layer: packed gate/up expert weights
+  std::vector<uint16_t*> pk2;  // per layer: packed down expert weights
 
   int fail(int code, const std::string& msg) {
     err = msg;
@@ -139,11 +141,12 @@ std::string validate_desc(const dg_model_desc& m) {
   if (m.n_layers < 1) return bad("n_layers < 1");
   if (m.head_dim != 64 && m.head_dim != 128) return bad("head_dim must be 64 or 128");
   if (m.n_q_heads < 1 || m.n_kv_heads < 1 || m.n_q_heads % m.n_kv_heads) return bad("n_q_heads % n_kv_heads");
-  if (m.d_model < 64 || m.d_model % 64 || m.d_model > 4096) return bad("d_model: multiple of 64, <= 4096");
+  if (m.d_model < 128 || m.d_model % 128 || m.d_model > 8192) return bad("d_model: multiple of 128, <= 8192");
   if ((m.n_q_heads * m.head_dim) % 64) return bad("n_q_heads*head_dim % 64");
   if (m.n_experts < 1 || m.n_experts > 64) return bad("n_experts in [1, 64]");
   if (m.top_k < 1 || m.top_k > m.n_experts) return bad("top_k in [1, n_experts]");
-  if (m.d_ff_expert < 64 || m.d_ff_expert % 64) return bad("d_ff_expert % 64");
+  if (m.d_ff_expert < 128 || m.d_ff_expert % 128 || m.d_ff_expert > 1024)
+    return bad("d_ff_expert: multiple of 128, <= 1024");
   if (m.d_ff_shared < 0 || m.d_ff_shared % 64) return bad("d_ff_shared % 64");
   if (m.vocab < 128 || m.vocab % 128) return bad("vocab % 128");
   if (m.canvas != 256) return bad("canvas must be 256");
@@ -160,7 +163,8 @@ RowMap make_map(int rows_per_req, int n_req, const int32_t* pos0) {
 }
 
 int choose_split(const dg_ctx* c, int base_wgs, int n_keys, int rows) {
-  int ns = std::max(1, std::min(kMaxSplit, (1024 + base_wgs - 1) / base_wgs));
+  // one work-group per CU (the attention kernel runs one 4-wave group per CU)
+  int ns = std::max(1, std::min(kMaxSplit, (256 + base_wgs - 1) / base_wgs));
   ns = std::min(ns, std::max(1, (n_keys + 63) / 64));
   ns = std::min(ns, std::max(1, c->part_cap / std::max(1, rows * c->m.n_q_heads)));
   return ns;
@@ -245,14 +249,14 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   timed(c, "moe_permute", s, [&] { launch_moe_permute(c->eidx, routes, m.n_experts, c->offs, c->perm, c->inv, s); });
   MoeArgs g1{};
   g1.x = c->a; g1.ldx = d; g1.perm = c->perm; g1.top_k = m.top_k; g1.offs = c->offs;
-  g1.w0 = lw.w_gate; g1.w1 = lw.w_up; g1.K = d; g1.N = m.d_ff_expert;
+  g1.wp = c->pk1[l]; g1.K = d; g1.N = m.d_ff_expert;
   g1.out_bf16 = c->act; g1.ldo = m.d_ff_expert; g1.n_exp = m.n_experts;
-  timed(c, "moe_gemm1_swiglu", s, [&] { launch_moe_gemm1(g1, s); });
+  timed(c, "moe_gemm1_swiglu", s, [&] { launch_moe_gemm1(g1, routes / m.n_experts, s); });
   MoeArgs g2{};
   g2.x = c->act; g2.ldx = m.d_ff_expert; g2.perm = c->perm; g2.top_k = m.top_k; g2.offs = c->offs;
-  g2.w0 = lw.w_down; g2.K = m.d_ff_expert; g2.N = d; g2.out_f32 = c->y; g2.ldo = d;
+  g2.wp = c->pk2[l]; g2.K = m.d_ff_expert; g2.N = d; g2.out_f32 = c->y; g2.ldo = d;
   g2.n_exp = m.n_experts;
-  timed(c, "moe_gemm2", s, [&] { launch_moe_gemm2(g2, s); });
+  timed(c, "moe_gemm2", s, [&] { launch_moe_gemm2(g2, routes / m.n_experts, s); });
 
   if (m.d_ff_shared > 0) {
     GemmArgs gs{};
@@ -336,8 +340,20 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
             c->alloc(&c->f, static_cast<long>(c->r_canvas) * d) &&
             c->alloc(&c->head_part, static_cast<long>(c->r_canvas) * (m.vocab / kHeadSlice) * 8) &&
             c->alloc(&c->ck, ckv) && c->alloc(&c->cv, ckv);
+  // expert banks, repacked once into the MFMA fragment order the expert GEMMs stream
+  const long ew = static_cast<long>(m.n_experts) * m.d_ff_expert * m.d_model;
+  c->pk1.assign(m.n_layers, nullptr);
+  c->pk2.assign(m.n_layers, nullptr);
+  for (int l = 0; ok && l < m.n_layers; ++l) {
+    ok = c->alloc(&c->pk1[l], 2 * ew) && c->alloc(&c->pk2[l], ew);
+    if (!ok) break;
+    const dg_layer_weights& lw = c->layers[l];
+    launch_moe_pack(lw.w_gate, lw.w_up, c->pk1[l], m.n_experts, m.d_ff_expert, m.d_model, nullptr);
+    launch_moe_pack(lw.w_down, nullptr, c->pk2[l], m.n_experts, m.d_model, m.d_ff_expert, nullptr);
+  }
+  if (ok) ok = hipDeviceSynchronize() == hipSuccess && hipGetLastError() == hipSuccess;
   if (!ok) {
-    g_create_error = "workspace allocation failed";
+    g_create_error = "workspace allocation or weight packing failed";
     delete c;
     return DG_ERR_HIP;
   }

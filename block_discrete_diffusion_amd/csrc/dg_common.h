@@ -14,16 +14,14 @@ namespace dg {
 
 constexpr int kWave = 64;
 
-// bfloat16 <-> float32 (round to nearest even; inputs are finite in this path).
+// bfloat16 <-> float32.  float -> bf16 uses the gfx950 hardware conversion
+// (v_cvt_pk_bf16_f32, round to nearest even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 DG_DEVICE float bf2f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
-DG_DEVICE uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+DG_DEVICE uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 DG_DEVICE uint32_t pack_bf2(float a, float b) {
-  return static_cast<uint32_t>(f2bf(a)) | (static_cast<uint32_t>(f2bf(b)) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // One 16x16x32 bf16 MFMA step: D(16x16, fp32) += A(16x32) * B(32x16).
@@ -34,6 +32,10 @@ DG_DEVICE floatx4_t mfma16(const u32x4_t& a, const u32x4_t& b, const floatx4_t& 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+
+// Keeps the machine scheduler from moving instructions across this point: used right after a
+// prefetch is issued so the loads stay ahead of the MFMAs that do not need them.
+DG_DEVICE void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 DG_DEVICE u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 DG_DEVICE u32x4_t ld16_nt(const void* p) {

@@ -90,13 +90,20 @@ struct MoeArgs {
   const uint16_t* x; int ldx;       // GEMM1: normed rows b [rows][d]; GEMM2: act [routes][F]
   const int32_t* perm; int top_k;   // GEMM1 gathers row perm[p]/top_k; GEMM2 reads row p
   const int32_t* offs;              // [E+1]
-  const uint16_t* w0; const uint16_t* w1;  // GEMM1: gate, up [E][F][d]; GEMM2: down [E][d][F]
+  const uint16_t* wp;               // expert weights in the packed fragment layout (below)
   int K; int N;                     // reduction length and output features per expert
   uint16_t* out_bf16; float* out_f32; int ldo;
   int n_exp;
 };
-void launch_moe_gemm1(const MoeArgs& a, hipStream_t s);
-void launch_moe_gemm2(const MoeArgs& a, hipStream_t s);
+// Packed expert weights: for expert e, 16-row tile ft and 32-wide k-step s, the MFMA A-operand
+// fragment of every matrix q (GEMM1: q = gate, up; GEMM2: q = down) is 64 lanes x 16 B, lane l
+// holding W_q[e][16 ft + l % 16][32 s + 8 (l / 16) .. + 8].  Order: [e][ft][s][q][lane], so a
+// wave streaming one tile over k reads contiguous memory.
+void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int n_exp, int N,
+                     int K, hipStream_t s);
+// mean_rows: routed rows per expert on average (selects the token-tile depth per pass)
+void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s);
+void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s);
 void launch_moe_combine(float* h, const float* y, const int32_t* inv, const float* gates,
                         int rows, int d, int top_k, hipStream_t s);
 

@@ -21,36 +21,34 @@ namespace dg {
 namespace {
 
 // ---------------------------------------------------------------------------------- RoPE
+// One work-group per row.  Thread t handles rotation pair j = t % half for the heads
+// h = t / half, t / half + 256 / half, ...; the angle pos * theta^(-2j/D) and its sine and
+// cosine are formed in float64 once per thread (positions reach 10^5 radians, where a float32
+// angle would already be off by ~1e-2).
 __global__ __launch_bounds__(256) void rope_scatter_kernel(RopeArgs a) {
   const int r = blockIdx.x;
   const int b = r / a.map.rows_per_req, i = r - b * a.map.rows_per_req;
   const double pos = static_cast<double>(a.map.pos0[b] + i);
   const int D = a.D, half = D / 2;
-  const int nqk = (a.Hq + a.Hkv) * half;  // rotated pairs
+  const int nh = a.Hq + a.Hkv;  // rotated heads: q heads then k heads
   const float* row = a.qkv + static_cast<long>(r) * (a.Hq + 2 * a.Hkv) * D;
   const long slot = a.slot0[b] + i;
-  for (int p = threadIdx.x; p < nqk; p += 256) {
-    const int h = p / half, j = p - h * half;
+  const int j = threadIdx.x % half, hstep = 256 / half;
+  double sn = 0.0, cs = 1.0;
+  if (a.theta != 0.f) sincos(pos * pow(static_cast<double>(a.theta), -2.0 * j / D), &sn, &cs);
+  for (int h = threadIdx.x / half; h < nh; h += hstep) {
     const float x1 = row[h * D + j], x2 = row[h * D + j + half];
-    float y1 = x1, y2 = x2;
-    if (a.theta != 0.f) {
-      const double inv_freq = pow(static_cast<double>(a.theta), -2.0 * j / D);
-      double sn, cs;
-      sincos(pos * inv_freq, &sn, &cs);
-      const double d1 = static_cast<double>(x1), d2 = static_cast<double>(x2);
-      y1 = static_cast<float>(d1 * cs - d2 * sn);
-      y2 = static_cast<float>(d2 * cs + d1 * sn);
-    }
+    const double d1 = static_cast<double>(x1), d2 = static_cast<double>(x2);
+    const float y1 = static_cast<float>(d1 * cs - d2 * sn);
+    const float y2 = static_cast<float>(d2 * cs + d1 * sn);
+    uint16_t* dst;
     if (h < a.Hq) {
-      uint16_t* q = a.q + static_cast<long>(r) * a.Hq * D + h * D;
-      q[j] = f2bf(y1);
-      q[j + half] = f2bf(y2);
+      dst = a.q + static_cast<long>(r) * a.Hq * D + h * D;
     } else {
-      const int g = h - a.Hq;
-      uint16_t* k = a.k_dst + ((static_cast<long>(b) * a.Hkv + g) * a.kv_cap + slot) * D;
-      k[j] = f2bf(y1);
-      k[j + half] = f2bf(y2);
+      dst = a.k_dst + ((static_cast<long>(b) * a.Hkv + (h - a.Hq)) * a.kv_cap + slot) * D;
     }
+    dst[j] = f2bf(y1);
+    dst[j + half] = f2bf(y2);
   }
   // V: no rotation
   const float* vrow = row + (a.Hq + a.Hkv) * D;
@@ -118,6 +116,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   int qpos[2];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) qpos[qt] = a.q_pos0[b] + row0 + qt * 16 + l16;
+  const int qmin = a.q_pos0[b] + row0;  // smallest query position of this wave
 
   floatx4_t o[NDT][2];
 #pragma unroll
@@ -137,22 +136,24 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
                         : a.vx + (kv_head * a.xcap + (kk - n_cache)) * D;
   };
 
+  // Keys past the range end re-read the last valid key (never uninitialised cache memory, and
+  // every load is unconditional so wait counts stay exact); their scores are masked to -inf.
   u32x4_t rk[KCH], rv[VPT][4];
   auto gload = [&](int kb0) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int kk = kb0 + key;
-      rk[i] = (kk < k_hi) ? ld16(key_ptr_k(kk) + col) : u32x4_t{0u, 0u, 0u, 0u};
+      const int kk = min(kb0 + key, k_hi - 1);
+      rk[i] = ld16(key_ptr_k(kk) + col);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int t = tid + 256 * i;
+      const int t = min(tid + 256 * i, VTASK - 1);
       const int kq = t % (KB / 4), dq = t / (KB / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kk = kb0 + kq * 4 + r;
-        rv[i][r] = (t < VTASK && kk < k_hi) ? ld16(key_ptr_v(kk) + dq * 8) : u32x4_t{0u, 0u, 0u, 0u};
+        const int kk = min(kb0 + kq * 4 + r, k_hi - 1);
+        rv[i][r] = ld16(key_ptr_v(kk) + dq * 8);
       }
     }
   };
@@ -188,7 +189,8 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
     __syncthreads();  // previous block's LDS reads are done
     sstore();
     __syncthreads();
-    if (blk + 1 < n_blk) gload(kb0 + KB);
+    gload(blk + 1 < n_blk ? kb0 + KB : kb0);  // unconditional: exact wait counts
+    sched_fence();
     if (!active) continue;
 
     // S^T for 4 key sub-blocks x 2 query tiles
@@ -206,7 +208,9 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
         for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
       }
     }
-    // scale, mask, online softmax (per lane = per query)
+    // scale, mask (only blocks that cross the key range end or the causal diagonal),
+    // online softmax (per lane = per query)
+    const bool edge = (kb0 + KB > k_hi) || (a.causal && kb0 + KB - 1 > qmin);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       float mx = -INFINITY;
@@ -214,9 +218,11 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kk = kb0 + kt * 16 + 4 * j4 + i;
           float v = s[kt][qt][i] * sl2;
-          if (kk >= k_hi || (a.causal && kk > qpos[qt])) v = -INFINITY;
+          if (edge) {
+            const int kk = kb0 + kt * 16 + 4 * j4 + i;
+            if (kk >= k_hi || (a.causal && kk > qpos[qt])) v = -INFINITY;
+          }
           s[kt][qt][i] = v;
           mx = fmaxf(mx, v);
         }

@@ -53,36 +53,39 @@ struct Mainloop {
         acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         if constexpr (DUAL) acc1[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
       }
-    u32x4_t rw[CW], rw1[DUAL ? CW : 1], rx[CX];
+    // two register sets of prefetched global tiles: two k-tiles are in flight while one is
+    // multiplied out of LDS
+    u32x4_t rw[2][CW], rw1[2][DUAL ? CW : 1], rx[2][CX];
     const int nk = K / BK;
 
-    auto gload = [&](int kt) {
+    auto gload = [&](int set, int kt) {
       const int kof = kt * BK;
 #pragma unroll
       for (int i = 0; i < CW; ++i) {
         const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
-        rw[i] = ld16(w0 + static_cast<long>(r) * K + kof + col);
-        if constexpr (DUAL) rw1[i] = ld16(w1 + static_cast<long>(r) * K + kof + col);
+        rw[set][i] = ld16(w0 + static_cast<long>(r) * K + kof + col);
+        if constexpr (DUAL) rw1[set][i] = ld16(w1 + static_cast<long>(r) * K + kof + col);
       }
 #pragma unroll
       for (int i = 0; i < CX; ++i) {
         const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
-        const int t = t0 + r;
-        rx[i] = (t < n_tok) ? ld16(x + static_cast<long>(t) * ldx + kof + col)
-                            : u32x4_t{0u, 0u, 0u, 0u};
+        // rows past n_tok re-read the last row (unconditional loads keep the wait counts
+        // exact); their outputs are never stored
+        const int t = min(t0 + r, n_tok - 1);
+        rx[set][i] = ld16(x + static_cast<long>(t) * ldx + kof + col);
       }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, int set) {
 #pragma unroll
       for (int i = 0; i < CW; ++i) {
         const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
-        st16(&sm.w[buf][0][r][col], rw[i]);
-        if constexpr (DUAL) st16(&sm.w[buf][DUAL ? 1 : 0][r][col], rw1[i]);
+        st16(&sm.w[buf][0][r][col], rw[set][i]);
+        if constexpr (DUAL) st16(&sm.w[buf][DUAL ? 1 : 0][r][col], rw1[set][i]);
       }
 #pragma unroll
       for (int i = 0; i < CX; ++i) {
         const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
-        st16(&sm.x[buf][r][col], rx[i]);
+        st16(&sm.x[buf][r][col], rx[set][i]);
       }
     };
     auto compute = [&](int buf) {
@@ -107,13 +110,29 @@ struct Mainloop {
       }
     };
 
-    gload(0);
-    sstore(0);
+    // k-tile t lives in LDS buffer t & 1 and arrives through register set t & 1 (tile 0 is
+    // stored at once); a register set is refilled with tile t + 2 right after its tile t went
+    // to LDS, so tiles t + 1 and t + 2 are in flight while tile t is multiplied.
+    // Loads are unconditional (tile index clamped to the last tile, which is then re-read) so
+    // no branch surrounds a load and the compiler's wait counts stay exact.
+    gload(0, 0);
+    sstore(0, 0);
+    gload(1, min(1, nk - 1));
+    gload(0, min(2, nk - 1));
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) gload(kt + 1);
-      compute(kt & 1);
-      if (kt + 1 < nk) sstore((kt + 1) & 1);
+    for (int kt = 0; kt < nk; kt += 2) {
+      compute(0);
+      sched_fence();
+      sstore(1, 1);
+      gload(1, min(kt + 3, nk - 1));
+      sched_fence();
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      compute(1);
+      sched_fence();
+      sstore(0, 0);
+      gload(0, min(kt + 4, nk - 1));
+      sched_fence();
       __syncthreads();
     }
   }
@@ -317,10 +336,11 @@ void launch_cfg(const GemmArgs& a, hipStream_t s) {
 template <int EPI>
 void launch_epi(const GemmArgs& a, hipStream_t s) {
   // Pick the tile so the grid still covers the 256 CUs: wide token tiles only when there are
-  // enough feature tiles.
-  const int tiles128 = (a.N / 64) * ((a.n_tok + 127) / 128);
-  if (a.n_tok >= 128 && tiles128 >= 512) launch_cfg<64, 128, EPI>(a, s);
-  else launch_cfg<64, 64, EPI>(a, s);
+  // enough feature tiles, narrow feature tiles when there are few.
+  const int tt64 = (a.n_tok + 63) / 64, tt128 = (a.n_tok + 127) / 128;
+  if (a.n_tok >= 128 && (a.N / 64) * tt128 >= 512) launch_cfg<64, 128, EPI>(a, s);
+  else if ((a.N / 64) * tt64 >= 256 || a.N % 64 != 0 || EPI == EPI_SWIGLU_BF16) launch_cfg<64, 64, EPI>(a, s);
+  else launch_cfg<32, 64, EPI>(a, s);
 }
 
 }  // namespace
@@ -329,7 +349,7 @@ void launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
   switch (epi) {
     case EPI_STORE_F32: launch_epi<EPI_STORE_F32>(a, s); break;
     case EPI_ADD_F32: launch_epi<EPI_ADD_F32>(a, s); break;
-    case EPI_SWIGLU_BF16: launch_cfg<64, 64, EPI_SWIGLU_BF16>(a, s); break;
+    case EPI_SWIGLU_BF16: launch_cfg<64, 64, EPI_SWIGLU_BF16>(a, s); break;  // N % 64 == 0
     default: launch_epi<EPI_STORE_BF16>(a, s); break;
   }
 }

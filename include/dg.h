@@ -53,8 +53,8 @@ enum {
   DG_ERR_UNSUPPORTED = -5  /* flag combination not supported */
 };
 
-/* Model shape.  Supported: head_dim 64 or 128; d_model, n_q_heads*head_dim, d_ff_expert and
- * d_ff_shared multiples of 64; n_q_heads a multiple of n_kv_heads; 1 <= top_k <= n_experts
+/* Model shape.  Supported: head_dim 64 or 128; d_model a multiple of 128 (<= 8192);
+ * d_ff_expert a multiple of 128 (<= 1024); n_q_heads*head_dim and d_ff_shared multiples of 64; n_q_heads a multiple of n_kv_heads; 1 <= top_k <= n_experts
  * <= 64; vocab a multiple of 128; canvas == 256 ([GUIDE] "Arquitetura em Detalhes": fixed
  * 256-token blocks).  rope_theta 0 disables RoPE (rotate-half, absolute positions). */
 typedef struct {
@@ -165,7 +165,10 @@ typedef struct {
   const dg_debug* debug; /* (host) optional, may be NULL */
 } dg_step_params;
 
-/* Create a context for `desc` over caller-owned device weights.  max_batch: largest batch
+/* Create a context for `desc` over caller-owned device weights.  The expert banks (w_gate,
+ * w_up, w_down) are copied once into the context's own memory in the layout the expert GEMMs
+ * stream (MFMA operand fragments, contiguous per 16-row tile); they are read only during
+ * dg_create.  Every other weight pointer must stay valid for the context's lifetime.  max_batch: largest batch
  * (<= 64) of later calls; max_prefill_rows: largest prefill chunk processed at once (rows are
  * split into chunks of this size).  Returns DG_OK and *out, or an error code. */
 int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_batch,
