@@ -73,6 +73,8 @@ struct dg_ctx {
   uint16_t* sact = nullptr;    // [r_max][Fs]
   uint16_t* f = nullptr;       // [r_canvas][d]
   float* head_part = nullptr;  // [r_canvas][V/64][8]
+  float* gpart = nullptr;      // split-K partial slices of the dense GEMMs
+  float* rope = nullptr;       // [r_max][D/2][2] cos/sin of the rows of the current step
   uint16_t* ck = nullptr;      // [L][max_batch][Hkv][C][D]
   uint16_t* cv = nullptr;
   std::vector<uint16_t*> pk1;  // per layer: packed gate/up expert weights
@@ -104,6 +106,7 @@ struct dg_ctx {
 namespace {
 
 constexpr int kMaxSplit = 16;
+constexpr long kGemmPartFloats = 8L << 20;  // 32 MB of split-K partial slices
 constexpr int kHeadSlice = 64;  // vocab entries per head partial (half the 128-wide tile)
 
 // Run `launch` (one or more kernel launches on stream s); with timing on, bracket it by events.
@@ -185,14 +188,19 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   timed(c, "rmsnorm", s, [&] { launch_rmsnorm(c->h, lw.attn_norm, m.rms_eps, c->a, rows, d, s); });
 
   GemmArgs g{};
+  g.part = c->gpart;
   g.x = c->a; g.ldx = d; g.n_tok = rows;
   g.seg_w[0] = lw.wq; g.seg_w[1] = lw.wk; g.seg_w[2] = lw.wv;
   g.seg_start[0] = 0; g.seg_start[1] = Hq * D; g.seg_start[2] = (Hq + Hkv) * D; g.seg_start[3] = nqkv;
   g.n_seg = 3; g.K = d; g.N = nqkv; g.out_f32 = c->qkv; g.ldo = nqkv;
+  g.split = gemm_split(g, EPI_STORE_F32, kGemmPartFloats);
+  g.part_stride = static_cast<long>(rows) * nqkv;
   timed(c, "gemm_qkv", s, [&] { launch_gemm(g, EPI_STORE_F32, s); });
 
   RopeArgs ra{};
-  ra.qkv = c->qkv; ra.rows = rows; ra.Hq = Hq; ra.Hkv = Hkv; ra.D = D; ra.theta = m.rope_theta;
+  ra.qkv = g.split > 1 ? c->gpart : c->qkv; ra.rows = rows; ra.Hq = Hq; ra.Hkv = Hkv; ra.D = D;
+  ra.n_part = g.split; ra.part_stride = g.part_stride;
+  ra.table = m.rope_theta != 0.f ? c->rope : nullptr;  // filled by the caller for these rows
   ra.q = c->q; ra.map = map;
   const long ck_layer = static_cast<long>(l) * c->max_batch * Hkv * m.canvas * D;
   if (prefill) {
@@ -229,15 +237,22 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
                          sizeof(uint16_t) * rows * Hq * D, hipMemcpyDeviceToDevice, s);
 
   GemmArgs go{};
+  go.part = c->gpart;
   go.x = c->attn; go.ldx = Hq * D; go.n_tok = rows; go.w0 = lw.wo; go.K = Hq * D; go.N = d;
   go.out_f32 = c->h; go.ldo = d;
+  go.split = gemm_split(go, EPI_ADD_F32, kGemmPartFloats);
+  go.part_stride = static_cast<long>(rows) * d;
   timed(c, "gemm_o_residual", s, [&] { launch_gemm(go, EPI_ADD_F32, s); });
+
+  // (the attention-output residual lands here when the O-projection was split: h += slices)
+  timed(c, "norm_router_topk", s, [&] {
+    launch_norm_router(c->h, c->gpart, go.split > 1 ? go.split : 0, go.part_stride, lw.ffn_norm,
+                       m.rms_eps, lw.w_router, rows, d, m.n_experts, m.top_k, c->a, c->eidx,
+                       c->gates, s);
+  });
   if (dbg && dbg->h_mid)
     (void)hipMemcpyAsync(dbg->h_mid + static_cast<long>(l) * rows * d, c->h,
                          sizeof(float) * rows * d, hipMemcpyDeviceToDevice, s);
-
-  timed(c, "norm_router_topk", s, [&] { launch_norm_router(c->h, lw.ffn_norm, m.rms_eps, lw.w_router, rows, d, m.n_experts, m.top_k,
-                     c->a, c->eidx, c->gates, s); });
   if (dbg && dbg->expert_idx)
     (void)hipMemcpyAsync(dbg->expert_idx + static_cast<long>(l) * rows * m.top_k, c->eidx,
                          sizeof(int32_t) * rows * m.top_k, hipMemcpyDeviceToDevice, s);
@@ -258,17 +273,31 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   g2.n_exp = m.n_experts;
   timed(c, "moe_gemm2", s, [&] { launch_moe_gemm2(g2, routes / m.n_experts, s); });
 
+  int n_res = 0;  // split-K slices of the shared down projection, added by the combine
   if (m.d_ff_shared > 0) {
     GemmArgs gs{};
+    gs.part = c->gpart;
     gs.x = c->a; gs.ldx = d; gs.n_tok = rows; gs.w0 = lw.ws_gate; gs.w1 = lw.ws_up; gs.K = d;
     gs.N = m.d_ff_shared; gs.out_bf16 = c->sact; gs.ldo = m.d_ff_shared;
-    timed(c, "shared_gate_up_swiglu", s, [&] { launch_gemm(gs, EPI_SWIGLU_BF16, s); });
+    gs.split = gemm_split(gs, EPI_SWIGLU_BF16, kGemmPartFloats);
+    gs.part_stride = 2L * rows * m.d_ff_shared;
+    timed(c, "shared_gate_up_swiglu", s, [&] {
+      launch_gemm(gs, EPI_SWIGLU_BF16, s);
+      if (gs.split > 1) launch_swiglu_reduce(c->gpart, gs.part_stride, gs.split, c->sact, rows, m.d_ff_shared, s);
+    });
     GemmArgs gd{};
+    gd.part = c->gpart;
     gd.x = c->sact; gd.ldx = m.d_ff_shared; gd.n_tok = rows; gd.w0 = lw.ws_down;
     gd.K = m.d_ff_shared; gd.N = d; gd.out_f32 = c->h; gd.ldo = d;
+    gd.split = gemm_split(gd, EPI_ADD_F32, kGemmPartFloats);
+    gd.part_stride = static_cast<long>(rows) * d;
+    n_res = gd.split > 1 ? gd.split : 0;
     timed(c, "shared_down_residual", s, [&] { launch_gemm(gd, EPI_ADD_F32, s); });
   }
-  timed(c, "moe_combine", s, [&] { launch_moe_combine(c->h, c->y, c->inv, c->gates, rows, d, m.top_k, s); });
+  timed(c, "moe_combine", s, [&] {
+    launch_moe_combine(c->h, c->gpart, n_res, static_cast<long>(rows) * d, c->y, c->inv, c->gates, rows,
+                       d, m.top_k, s);
+  });
 }
 
 int check_kv(dg_ctx* c, const dg_kv_cache* kv) {
@@ -339,7 +368,9 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
             c->alloc(&c->sact, R * std::max(1, m.d_ff_shared)) &&
             c->alloc(&c->f, static_cast<long>(c->r_canvas) * d) &&
             c->alloc(&c->head_part, static_cast<long>(c->r_canvas) * (m.vocab / kHeadSlice) * 8) &&
-            c->alloc(&c->ck, ckv) && c->alloc(&c->cv, ckv);
+            c->alloc(&c->ck, ckv) && c->alloc(&c->cv, ckv) &&
+            c->alloc(&c->gpart, kGemmPartFloats) &&
+            c->alloc(&c->rope, R * m.head_dim);
   // expert banks, repacked once into the MFMA fragment order the expert GEMMs stream
   const long ew = static_cast<long>(m.n_experts) * m.d_ff_expert * m.d_model;
   c->pk1.assign(m.n_layers, nullptr);
@@ -395,6 +426,7 @@ int dg_prefill_causal(dg_ctx* c, const int32_t* tokens, const int32_t* n_new, in
       const int n = std::min(c->max_prefill, n_new[b] - done);
       launch_embed(tokens + tok_ofs + done, c->w.embed, c->h, n, m.d_model, s);
       const int32_t len_b = kv->len[b] + done;
+      if (m.rope_theta != 0.f) launch_rope_table(make_map(n, 1, &len_b), n, m.head_dim, m.rope_theta, c->rope, s);
       for (int l = 0; l < m.n_layers; ++l) {
         const long base = l * kv_layer_stride(m, kv->batch, kv->cap) +
                           static_cast<long>(b) * m.n_kv_heads * kv->cap * m.head_dim;
@@ -438,6 +470,10 @@ static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
       (void)hipMemcpyAsync(c->h, p->hidden_in, sizeof(float) * rows * d, hipMemcpyDeviceToDevice, s);
     else
       timed(c, "embed", s, [&] { launch_embed(canvas, c->w.embed, c->h, rows, d, s); });
+    if (m.rope_theta != 0.f)
+      timed(c, "rope_table", s, [&] {
+        launch_rope_table(make_map(C, B, kv->len), rows, m.head_dim, m.rope_theta, c->rope, s);
+      });
     for (int l = 0; l < m.n_layers; ++l)
       run_layer(c, l, B, C, kv->len, false, kv->k + l * kv_layer_stride(m, B, kv->cap),
                 kv->v + l * kv_layer_stride(m, B, kv->cap), kv->cap, dbg, s);

@@ -23,9 +23,14 @@ void launch_rmsnorm(const float* h, const float* gain, float eps, uint16_t* out,
 void launch_f32_to_bf16(const float* in, uint16_t* out, long n, hipStream_t s);
 // ffn norm + router: b = bf16(rms(h)*gain); logits in fp32 from the fp32 normed row;
 // top-k (value desc, index asc); softmax gates over the k picks.
-void launch_norm_router(const float* h, const float* gain, float eps, const uint16_t* w_router,
-                        int rows, int d, int n_exp, int top_k, uint16_t* b_out, int32_t* idx,
-                        float* gates, hipStream_t s);
+// Residual update + FFN norm + router, one row per work-group: h += sum_z part_z (n_part
+// split-K slices, z order; written back); x = h * rsqrt(mean h^2 + eps) * gain in float32 and
+// its bf16 copy b (the experts' input); router logits W_router x in float32; top-k (value desc,
+// index asc); softmax gates over the k picks.
+void launch_norm_router(float* h, const float* part, int n_part, long part_stride,
+                        const float* gain, float eps, const uint16_t* w_router, int rows, int d,
+                        int n_exp, int top_k, uint16_t* b_out, int32_t* idx, float* gates,
+                        hipStream_t s);
 
 // ---- k_gemm.hip : C[t][f] = sum_k X[t][k] * W[f][k]
 enum GemmEpi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU_BF16 = 2, EPI_STORE_BF16 = 3 };
@@ -36,8 +41,18 @@ struct GemmArgs {
   const uint16_t* seg_w[3]; int seg_start[4]; int n_seg;
   int K; int N;
   float* out_f32; uint16_t* out_bf16; int ldo;
+  // split-K: with split > 1 the k range is cut into `split` slices and slice z stores its raw
+  // fp32 product to part + z * part_stride (+ part_stride / 2 for the up matrix of the SwiGLU
+  // pair), row-major [n_tok][N]; the consumer sums the slices in z order.
+  int split; float* part; long part_stride;
 };
+// Largest split (1, 2, 4 or 8) that keeps >= 4 k-tiles per slice and stays within `cap`
+// partial floats while the grid stays within ~1024 work-groups.
+int gemm_split(const GemmArgs& a, int epi, long cap);
 void launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
+// act[t][f] = bf16(silu(sum_z gate_z) * sum_z up_z) over `split` partial slices
+void launch_swiglu_reduce(const float* part, long part_stride, int split, uint16_t* act, int rows,
+                          int n, hipStream_t s);
 
 // Fused vocab head: logits never leave registers.  Writes per (row, 64-wide vocab slice)
 // partial statistics; launch_head_merge reduces them into row statistics.
@@ -57,10 +72,19 @@ void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
                        float* lse, float* ent, hipStream_t s);
 
 // ---- k_attn.hip
-// Split qkv fp32 [rows][(Hq+2Hkv)*D] into rotated bf16 q [rows][Hq*D] and rotated k / v written
-// at kv_dst + ((b*Hkv + g)*kv_cap + slot0[b] + i)*D.
+constexpr int kMaxParts = 4;  // largest split-K slice count a consumer sums
+
+// cos / sin of the RoPE angle pos * theta^(-2j/D) for every row and j < D/2, formed in float64
+// and rounded to float32: table[r][j] = {cos, sin}.  Built once per step (all layers share it).
+void launch_rope_table(const RowMap& map, int rows, int D, float theta, float* table, hipStream_t s);
+
+// qkv holds n_part split-K slices (row-major [rows][(Hq+2Hkv)*D], part_stride apart) summed in
+// order; q heads and k heads are rotated with the table (rotate-half), q -> q [rows][Hq*D] bf16,
+// k / v -> kv_dst + ((b*Hkv + g)*kv_cap + slot0[b] + i)*D bf16.
 struct RopeArgs {
-  const float* qkv; int rows; int Hq; int Hkv; int D; float theta;
+  const float* qkv; int rows; int Hq; int Hkv; int D;
+  int n_part; long part_stride;
+  const float* table;  // null = no rotation
   uint16_t* q; uint16_t* k_dst; uint16_t* v_dst; int kv_cap;  // per-layer base
   RowMap map; int32_t slot0[kMaxBatch];
 };
@@ -104,8 +128,10 @@ void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int 
 // mean_rows: routed rows per expert on average (selects the token-tile depth per pass)
 void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s);
 void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s);
-void launch_moe_combine(float* h, const float* y, const int32_t* inv, const float* gates,
-                        int rows, int d, int top_k, hipStream_t s);
+// h[t] += sum_z part_z[t] (n_part residual slices, z order) + sum_j gate[t][j] * y[inv[t][j]]
+void launch_moe_combine(float* h, const float* part, int n_part, long part_stride, const float* y,
+                        const int32_t* inv, const float* gates, int rows, int d, int top_k,
+                        hipStream_t s);
 
 // ---- k_sampler.hip
 struct SamplerArgs {

@@ -42,8 +42,9 @@ struct Mainloop {
   floatx4_t acc[FM][TN];
   floatx4_t acc1[DUAL ? FM : 1][DUAL ? TN : 1];
 
+  // K: reduction length of this work-group; ldw: row stride of W (elements)
   DG_DEVICE void run(Smem<BF, BT, DUAL>& sm, const uint16_t* w0, const uint16_t* w1,
-                     const uint16_t* x, int ldx, int n_tok, int t0, int K) {
+                     const uint16_t* x, int ldx, int n_tok, int t0, int K, int ldw) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wf = wave & 1, wt = wave >> 1;
 #pragma unroll
@@ -63,8 +64,8 @@ struct Mainloop {
 #pragma unroll
       for (int i = 0; i < CW; ++i) {
         const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
-        rw[set][i] = ld16(w0 + static_cast<long>(r) * K + kof + col);
-        if constexpr (DUAL) rw1[set][i] = ld16(w1 + static_cast<long>(r) * K + kof + col);
+        rw[set][i] = ld16(w0 + static_cast<long>(r) * ldw + kof + col);
+        if constexpr (DUAL) rw1[set][i] = ld16(w1 + static_cast<long>(r) * ldw + kof + col);
       }
 #pragma unroll
       for (int i = 0; i < CX; ++i) {
@@ -138,27 +139,32 @@ struct Mainloop {
   }
 };
 
+// Split-K: grid = tiles x S.  With S > 1 work-group (tile, z) multiplies the z-th K / S slice
+// and stores the raw fp32 product to its own slice of the partial buffer; the consuming kernel
+// adds the S slices in z order (a kernel boundary is the only synchronisation).
 template <int BF, int BT, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, int S) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
   using ML = Mainloop<BF, BT, DUAL>;
   __shared__ Smem<BF, BT, DUAL> sm;
   const int n_tt = (a.n_tok + BT - 1) / BT, n_ft = a.N / BF;
-  const int L = xcd_remap(blockIdx.x, n_tt * n_ft);
-  const int ft = L / n_tt, tt = L % n_tt;
+  const int L = xcd_remap(blockIdx.x, n_tt * n_ft * S);
+  const int tile = L / S, z = L % S;
+  const int ft = tile / n_tt, tt = tile % n_tt;
   const int f0 = ft * BF, t0 = tt * BT;
+  const int kz = a.K / S, k0 = z * kz;
   const uint16_t* w0;
   const uint16_t* w1 = nullptr;
   if (a.n_seg > 0) {
-    int s = 0;
-    while (s + 1 < a.n_seg && f0 >= a.seg_start[s + 1]) ++s;
-    w0 = a.seg_w[s] + static_cast<long>(f0 - a.seg_start[s]) * a.K;
+    int sg = 0;
+    while (sg + 1 < a.n_seg && f0 >= a.seg_start[sg + 1]) ++sg;
+    w0 = a.seg_w[sg] + static_cast<long>(f0 - a.seg_start[sg]) * a.K + k0;
   } else {
-    w0 = a.w0 + static_cast<long>(f0) * a.K;
-    if (DUAL) w1 = a.w1 + static_cast<long>(f0) * a.K;
+    w0 = a.w0 + static_cast<long>(f0) * a.K + k0;
+    if (DUAL) w1 = a.w1 + static_cast<long>(f0) * a.K + k0;
   }
   ML ml;
-  ml.run(sm, w0, w1, a.x, a.ldx, a.n_tok, t0, a.K);
+  ml.run(sm, w0, w1, a.x + k0, a.ldx, a.n_tok, t0, kz, a.K);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wf = wave & 1, wt = wave >> 1;
@@ -170,7 +176,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       const int f = f0 + wf * ML::WF + fm * 16 + 4 * (lane >> 4);
       if (t >= a.n_tok) continue;
       const floatx4_t v = ml.acc[fm][tn];
-      if constexpr (EPI == EPI_STORE_F32) {
+      if (S > 1) {
+        float* p = a.part + z * a.part_stride + static_cast<long>(t) * a.N + f;
+        *reinterpret_cast<floatx4_t*>(p) = v;
+        if constexpr (DUAL)
+          *reinterpret_cast<floatx4_t*>(p + a.part_stride / 2) = ml.acc1[DUAL ? fm : 0][DUAL ? tn : 0];
+      } else if constexpr (EPI == EPI_STORE_F32) {
         *reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(t) * a.ldo + f) = v;
       } else if constexpr (EPI == EPI_ADD_F32) {
         floatx4_t* p = reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(t) * a.ldo + f);
@@ -189,6 +200,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             u32x2_t{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
       }
     }
+}
+
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restrict__ part,
+                                                            long part_stride, int split,
+                                                            uint16_t* __restrict__ act, long n4) {
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  floatx4_t gz[kMaxParts], uz[kMaxParts];
+#pragma unroll
+  for (int z = 0; z < kMaxParts; ++z)
+    if (z < split) {
+      gz[z] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + i * 4);
+      uz[z] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + part_stride / 2 + i * 4);
+    }
+  floatx4_t g = floatx4_t{0.f, 0.f, 0.f, 0.f}, u = g;
+#pragma unroll
+  for (int z = 0; z < kMaxParts; ++z)
+    if (z < split) { g += gz[z]; u += uz[z]; }
+  float y[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) y[q] = g[q] / (1.0f + expf(-g[q])) * u[q];
+  *reinterpret_cast<u32x2_t*>(act + i * 4) = u32x2_t{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
 }
 
 // ------------------------------------------------------------------------------------------
@@ -244,7 +277,7 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   const int ft = L / n_tt, tt = L % n_tt;
   const int f0 = ft * BF, t0 = tt * BT;
   ML ml;
-  ml.run(sm, a.w + static_cast<long>(f0) * a.K, nullptr, a.f, a.K, a.n_rows, t0, a.K);
+  ml.run(sm, a.w + static_cast<long>(f0) * a.K, nullptr, a.f, a.K, a.n_rows, t0, a.K, a.K);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wf = wave & 1, wt = wave >> 1;
@@ -329,29 +362,68 @@ __global__ __launch_bounds__(64) void head_merge_kernel(const float* __restrict_
 
 template <int BF, int BT, int EPI>
 void launch_cfg(const GemmArgs& a, hipStream_t s) {
-  const int G = ((a.n_tok + BT - 1) / BT) * (a.N / BF);
-  hipLaunchKernelGGL((gemm_kernel<BF, BT, EPI>), dim3(G), dim3(256), 0, s, a);
+  const int tiles = ((a.n_tok + BT - 1) / BT) * (a.N / BF);
+  const int S = a.split > 1 ? a.split : 1;
+  hipLaunchKernelGGL((gemm_kernel<BF, BT, EPI>), dim3(tiles * S), dim3(256), 0, s, a, S);
+}
+
+// Tile shape: wide token tiles only when there are plenty of feature tiles, narrow feature tiles
+// when there are few.  Returns (BF, BT) through the out parameters.
+template <int EPI>
+void pick_tile(const GemmArgs& a, int* bf, int* bt) {
+  const int tt64 = (a.n_tok + 63) / 64, tt128 = (a.n_tok + 127) / 128;
+  if (a.n_tok >= 128 && (a.N / 64) * tt128 >= 512) { *bf = 64; *bt = 128; }
+  else if ((a.N / 64) * tt64 >= 256 || EPI == EPI_SWIGLU_BF16) { *bf = 64; *bt = 64; }
+  else { *bf = 32; *bt = 64; }
 }
 
 template <int EPI>
 void launch_epi(const GemmArgs& a, hipStream_t s) {
-  // Pick the tile so the grid still covers the 256 CUs: wide token tiles only when there are
-  // enough feature tiles, narrow feature tiles when there are few.
-  const int tt64 = (a.n_tok + 63) / 64, tt128 = (a.n_tok + 127) / 128;
-  if (a.n_tok >= 128 && (a.N / 64) * tt128 >= 512) launch_cfg<64, 128, EPI>(a, s);
-  else if ((a.N / 64) * tt64 >= 256 || a.N % 64 != 0 || EPI == EPI_SWIGLU_BF16) launch_cfg<64, 64, EPI>(a, s);
+  int bf, bt;
+  pick_tile<EPI>(a, &bf, &bt);
+  if (bf == 64 && bt == 128) launch_cfg<64, 128, EPI>(a, s);
+  else if (bf == 64) launch_cfg<64, 64, EPI>(a, s);
   else launch_cfg<32, 64, EPI>(a, s);
 }
 
+template <int EPI>
+int split_for(const GemmArgs& a, long cap) {
+  constexpr int NA = (EPI == EPI_SWIGLU_BF16) ? 2 : 1;
+  int bf, bt;
+  pick_tile<EPI>(a, &bf, &bt);
+  const int tiles = ((a.n_tok + bt - 1) / bt) * (a.N / bf);
+  int S = 1;
+  while (S < kMaxParts && tiles * S * 2 <= 1024 && (a.K / BK) % (S * 2) == 0 && a.K / (S * 2) >= 4 * BK &&
+         static_cast<long>(S) * 2 * NA * a.n_tok * a.N <= cap)
+    S *= 2;
+  return S;
+}
+
 }  // namespace
+
+int gemm_split(const GemmArgs& a, int epi, long cap) {
+  switch (epi) {
+    case EPI_STORE_F32: return split_for<EPI_STORE_F32>(a, cap);
+    case EPI_ADD_F32: return split_for<EPI_ADD_F32>(a, cap);
+    case EPI_SWIGLU_BF16: return 1;  // measured: the extra reduce pass costs more than it saves
+    default: return 1;  // bf16 output: no split
+  }
+}
 
 void launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
   switch (epi) {
     case EPI_STORE_F32: launch_epi<EPI_STORE_F32>(a, s); break;
     case EPI_ADD_F32: launch_epi<EPI_ADD_F32>(a, s); break;
-    case EPI_SWIGLU_BF16: launch_cfg<64, 64, EPI_SWIGLU_BF16>(a, s); break;  // N % 64 == 0
+    case EPI_SWIGLU_BF16: launch_epi<EPI_SWIGLU_BF16>(a, s); break;
     default: launch_epi<EPI_STORE_BF16>(a, s); break;
   }
+}
+
+void launch_swiglu_reduce(const float* part, long part_stride, int split, uint16_t* act, int rows,
+                          int n, hipStream_t s) {
+  const long n4 = static_cast<long>(rows) * n / 4;
+  hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((n4 + 255) / 256), dim3(256), 0, s, part, part_stride,
+                     split, act, n4);
 }
 
 void launch_head(const HeadArgs& a, hipStream_t s) {

@@ -265,8 +265,11 @@ __global__ __launch_bounds__(256) void moe_pack_kernel(const uint16_t* __restric
   st16(out + c * 8, ld16(src));
 }
 
-// h[t] += sum_j gate[t][j] * y[inv[t*k+j]]  (j in order; one thread per 4 columns)
+// h[t] += sum_z part_z[t] + sum_j gate[t][j] * y[inv[t*k+j]]  (z then j in order; one thread
+// per 4 columns)
 __global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
+                                                          const float* __restrict__ part,
+                                                          int n_part, long part_stride,
                                                           const float* __restrict__ y,
                                                           const int32_t* __restrict__ inv,
                                                           const float* __restrict__ gates,
@@ -275,11 +278,29 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
   const int per_row = d / 4;
   if (i >= static_cast<long>(rows) * per_row) return;
   const int t = static_cast<int>(i / per_row), c = static_cast<int>(i % per_row) * 4;
+  floatx4_t pz[kMaxParts], yj[8];
+  float gj[8];
+#pragma unroll
+  for (int z = 0; z < kMaxParts; ++z)
+    if (z < n_part) pz[z] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + static_cast<long>(t) * d + c);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < top_k) {
+      gj[j] = gates[static_cast<long>(t) * top_k + j];
+      yj[j] = *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(inv[static_cast<long>(t) * top_k + j]) * d + c);
+    }
   floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int z = 0; z < kMaxParts; ++z)
+    if (z < n_part) acc += pz[z];
   for (int j = 0; j < top_k; ++j) {
-    const float g = gates[static_cast<long>(t) * top_k + j];
-    const int p = inv[static_cast<long>(t) * top_k + j];
-    acc += g * *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(p) * d + c);
+    if (j < 8) {
+      acc += gj[j] * yj[j];
+    } else {
+      const float g = gates[static_cast<long>(t) * top_k + j];
+      const int p = inv[static_cast<long>(t) * top_k + j];
+      acc += g * *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(p) * d + c);
+    }
   }
   floatx4_t* hp = reinterpret_cast<floatx4_t*>(h + static_cast<long>(t) * d + c);
   floatx4_t o = *hp;
@@ -327,11 +348,12 @@ void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int 
                      N, K, na);
 }
 
-void launch_moe_combine(float* h, const float* y, const int32_t* inv, const float* gates, int rows,
-                        int d, int top_k, hipStream_t s) {
+void launch_moe_combine(float* h, const float* part, int n_part, long part_stride, const float* y,
+                        const int32_t* inv, const float* gates, int rows, int d, int top_k,
+                        hipStream_t s) {
   const long n = static_cast<long>(rows) * (d / 4);
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, h, y, inv, gates,
-                     rows, d, top_k);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, h, part, n_part,
+                     part_stride, y, inv, gates, rows, d, top_k);
 }
 
 }  // namespace dg
