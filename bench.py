@@ -43,6 +43,43 @@ def expert_gemm1_bytes(shape, routes: int, experts_touched: int) -> float:
     return float(w + x + out)
 
 
+# HBM traffic of the dominant kernel from hardware counters (rocprofv3 --pmc FETCH_SIZE, then
+# WRITE_SIZE, in separate runs of this script), per launch, each scaled by the ratio
+# true bytes / counter bytes that the same counter gives for a plain 1 GiB device copy.  Valid
+# only for the kernel source it was taken on: a changed source reports traffic null.
+PMC_TRAFFIC = {
+    "kernel": "moe_gemm_kernel<true, 2, 1>", "source": "block_discrete_diffusion_amd/csrc/k_moe.hip",
+    "sha": "e6f9c6eee996283f",
+    "fetch_kib": 207401.2, "fetch_scale": 1048576.0 / 524308.1,  # copy of 1 GiB reads 524308 KiB
+    "write_kib": 1536.0, "write_scale": 1048576.0 / 1048576.0,   # and writes 1048576 KiB
+}
+
+
+def source_digest(rel: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    if PMC_TRAFFIC is None or source_digest(PMC_TRAFFIC["source"]) != PMC_TRAFFIC["sha"]:
+        return None
+    return PMC_TRAFFIC["fetch_kib"] * 1024 * PMC_TRAFFIC["fetch_scale"] + \
+        PMC_TRAFFIC["write_kib"] * 1024 * PMC_TRAFFIC["write_scale"]
+
+
+def copy_calibration(mib: int):
+    """One plain device-to-device copy of `mib` MiB (float32), for scaling the HBM counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4}), flush=True)
+
+
 def _host(t):
     import torch
     return t.detach().to("cpu", torch.float32).numpy()
@@ -106,6 +143,8 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the HIP-event per-kernel pass (e.g. under a profiler)")
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run one plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}). "
@@ -116,6 +155,9 @@ def main():
     from block_discrete_diffusion_amd import dg, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     shape = synth.FULL
     prefix_len = 2048
     log("drawing weights on the device")
@@ -175,7 +217,7 @@ def main():
         ach = nbytes / (g1["avg_ms"] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": "moe_gemm1_swiglu", "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": None, "avg_launch_us": round(g1["avg_ms"] * 1e3, 2),
+                    "traffic": measured_traffic(), "avg_launch_us": round(g1["avg_ms"] * 1e3, 2),
                     "algorithmic_bytes_per_launch": nbytes}
     cpu = None
     if not args.no_cpu_baseline:

@@ -46,8 +46,8 @@ struct GemmArgs {
   // pair), row-major [n_tok][N]; the consumer sums the slices in z order.
   int split; float* part; long part_stride;
 };
-// Largest split (1, 2, 4 or 8) that keeps >= 4 k-tiles per slice and stays within `cap`
-// partial floats while the grid stays within ~1024 work-groups.
+// Largest split (1, 2 or 4) that keeps >= 16 k-tiles of 64 per slice and stays within `cap`
+// partial floats while the grid stays within ~512 work-groups.
 int gemm_split(const GemmArgs& a, int epi, long cap);
 void launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
 // act[t][f] = bf16(silu(sum_z gate_z) * sum_z up_z) over `split` partial slices

@@ -159,15 +159,15 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const float sl2 = a.scale * 1.4426950408889634f;
 
+  // Base pointers as values: selecting between two kernel-argument fields per lane would make
+  // the compiler load the pointer itself from the argument segment before every K/V load.
   const long kv_head = static_cast<long>(b) * a.Hkv + g;
-  auto key_ptr_k = [&](int kk) -> const uint16_t* {
-    return kk < n_cache ? a.kc + (kv_head * a.cap + kk) * D
-                        : a.kx + (kv_head * a.xcap + (kk - n_cache)) * D;
-  };
-  auto key_ptr_v = [&](int kk) -> const uint16_t* {
-    return kk < n_cache ? a.vc + (kv_head * a.cap + kk) * D
-                        : a.vx + (kv_head * a.xcap + (kk - n_cache)) * D;
-  };
+  const uint16_t* const kc0 = a.kc + kv_head * a.cap * D;
+  const uint16_t* const vc0 = a.vc + kv_head * a.cap * D;
+  const uint16_t* const kx0 = a.kx + (kv_head * a.xcap - n_cache) * D;  // indexed by kk >= n_cache
+  const uint16_t* const vx0 = a.vx + (kv_head * a.xcap - n_cache) * D;
+  auto key_ptr_k = [=](int kk) -> const uint16_t* { return (kk < n_cache ? kc0 : kx0) + static_cast<long>(kk) * D; };
+  auto key_ptr_v = [=](int kk) -> const uint16_t* { return (kk < n_cache ? vc0 : vx0) + static_cast<long>(kk) * D; };
 
   // Keys past the range end re-read the last valid key (never uninitialised cache memory, and
   // every load is unconditional so wait counts stay exact); their scores are masked to -inf.
