@@ -298,6 +298,9 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
     launch_moe_combine(c->h, c->gpart, n_res, static_cast<long>(rows) * d, c->y, c->inv, c->gates, rows,
                        d, m.top_k, s);
   });
+  if (dbg && dbg->layer_out)
+    (void)hipMemcpyAsync(dbg->layer_out + static_cast<long>(l) * rows * d, c->h,
+                         sizeof(float) * rows * d, hipMemcpyDeviceToDevice, s);
 }
 
 int check_kv(dg_ctx* c, const dg_kv_cache* kv) {

@@ -64,7 +64,7 @@ class SamplerCfg(C.Structure):
 
 class Debug(C.Structure):
     _fields_ = [(n, vp) for n in ("hidden_out", "attn_out", "h_mid", "expert_idx", "gates", "logits",
-                                  "canvas_k", "canvas_v")]
+                                  "canvas_k", "canvas_v", "layer_out")]
 
 
 class StepParams(C.Structure):

@@ -149,6 +149,8 @@ typedef struct {
   float* logits;           /* [rows][vocab] raw logits (test sizes only) */
   uint16_t* canvas_k;      /* [n_layers][batch][n_kv_heads][canvas][head_dim] */
   uint16_t* canvas_v;      /* same */
+  float* layer_out;        /* [n_layers][rows][d_model] residual after each layer (the next
+                              layer's input; the last one equals hidden_out) */
 } dg_debug;
 
 enum {

@@ -4,6 +4,7 @@ import pytest
 import torch
 
 from block_discrete_diffusion_amd import synth
+from oracle import model as omodel
 
 # Parity bar for continuous outputs (attention, FFN, logits) against the float64 oracle with
 # bf16 weights: max-abs 2e-2 and relative L2 1e-2.
@@ -93,3 +94,74 @@ def load_cache(kv, k: np.ndarray, v: np.ndarray, lens):
     kv.k.copy_(np_bf16_dev(k))
     kv.v.copy_(np_bf16_dev(v))
     kv.set_lengths(lens)
+
+
+def layer_debug(dg, m, shape, rows, n_layers, batch=1):
+    HD = shape.n_q_heads * shape.head_dim
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt, device="cuda")
+    return {
+        "hidden_out": z(rows, shape.d_model),
+        "attn_out": z(n_layers, rows, HD, dt=torch.bfloat16),
+        "h_mid": z(n_layers, rows, shape.d_model),
+        "expert_idx": z(n_layers, rows, shape.top_k, dt=torch.int32),
+        "gates": z(n_layers, rows, shape.top_k),
+        "canvas_k": z(n_layers, batch, shape.n_kv_heads, 256, shape.head_dim, dt=torch.bfloat16),
+        "canvas_v": z(n_layers, batch, shape.n_kv_heads, 256, shape.head_dim, dt=torch.bfloat16),
+        "layer_out": z(n_layers, rows, shape.d_model),
+    }
+
+
+def check_layer(dg, m, w, shape, Lp, seed, cap, min_safe=0.75):
+    """One layer from a synthetic residual state: attention, FFN and canvas K/V vs the oracle."""
+    kv = dg.KV(shape, 1, cap)
+    k, v = random_cache(shape, Lp, cap, seed)
+    load_cache(kv, k, v, [Lp])
+    h = synth.hidden(256, shape.d_model, seed, 5)
+    dbg = layer_debug(dg, m, shape, 256, shape.n_layers)
+    m.denoise_step(None, kv, None, 0, None, flags=dg.DG_STEP_HIDDEN_IN | dg.DG_STEP_NO_HEAD,
+                   hidden_in=torch.from_numpy(h).cuda(), debug=dbg)
+    torch.cuda.synchronize()
+    pos = Lp + np.arange(256)
+    h_out, ok_k, ok_v, od = omodel.layer(h, w["layers"][0], shape, pos, k[0, 0, :, :Lp], v[0, 0, :, :Lp], None)
+    close(bf16_to_np(dbg["attn_out"][0]), od["attn_out"], what="attention output")
+    close(dbg["h_mid"][0].cpu().numpy(), od["h_mid"], what="h after attention")
+    close(bf16_to_np(dbg["canvas_k"][0, 0]), ok_k, what="canvas K")
+    close(bf16_to_np(dbg["canvas_v"][0, 0]), ok_v, what="canvas V")
+    gi = dbg["expert_idx"][0].cpu().numpy()
+    safe = check_topk(gi, od["router_logits"], shape.top_k)
+    assert safe.mean() > min_safe, safe.mean()
+    order_ok = np.all(gi == od["expert_idx"], axis=1) & safe
+    close(dbg["gates"][0].cpu().numpy()[order_ok], od["gates"][order_ok], max_abs=1e-2, what="gates")
+    close(dbg["hidden_out"].cpu().numpy()[safe], h_out[safe], what="layer output")
+    close((dbg["hidden_out"].cpu().numpy() - dbg["h_mid"][0].cpu().numpy())[safe], od["ffn_out"][safe],
+          what="FFN output")
+
+
+def check_layers_teacher_forced(w, shape, dbg, b, tokens, cache_k, cache_v, Lb, min_safe=0.7):
+    """Every layer of request b's canvas against the oracle layer fed the GPU's own input to that
+    layer (the token embedding for layer 0, the GPU's previous layer output after that), over
+    the same cached prefix.  A router near-tie that flips an expert only moves that row's FFN
+    output inside its layer; feeding each layer the GPU's input keeps it from reaching the other
+    rows through the next layer's attention.  Compares the canvas K/V, the attention output and
+    residual (all rows), the expert choice, and the layer output on rows with a clear choice.
+
+    dbg: the layer_debug buffers of a denoise step; cache_k/cache_v: per layer [Hkv, >=Lb, D]."""
+    sl = slice(b * 256, (b + 1) * 256)
+    pos = Lb + np.arange(256)
+    h_in = np.asarray(w["embed"], np.float64)[np.asarray(tokens, np.int64)]
+    n_safe = []
+    for l in range(shape.n_layers):
+        if l > 0:
+            h_in = dbg["layer_out"][l - 1][sl].cpu().numpy().astype(np.float64)
+        h_out, k, v, od = omodel.layer(h_in, w["layers"][l], shape, pos, cache_k[l][:, :Lb],
+                                       cache_v[l][:, :Lb], None)
+        tag = f"request {b} layer {l}"
+        close(bf16_to_np(dbg["canvas_k"][l, b]), k, what=f"canvas K {tag}")
+        close(bf16_to_np(dbg["canvas_v"][l, b]), v, what=f"canvas V {tag}")
+        close(bf16_to_np(dbg["attn_out"][l][sl]), od["attn_out"], what=f"attention {tag}")
+        close(dbg["h_mid"][l][sl].cpu().numpy(), od["h_mid"], what=f"residual after attention {tag}")
+        safe = check_topk(dbg["expert_idx"][l][sl].cpu().numpy(), od["router_logits"], shape.top_k)
+        assert safe.mean() > min_safe, (tag, safe.mean())
+        close(dbg["layer_out"][l][sl].cpu().numpy()[safe], h_out[safe], what=f"layer output {tag}")
+        n_safe.append(int(safe.sum()))
+    return n_safe

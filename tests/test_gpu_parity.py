@@ -9,8 +9,8 @@ import torch
 from block_discrete_diffusion_amd import synth
 from oracle import model as omodel
 from oracle import sampler as osampler
-from tests.gpu_common import (MARGIN, ROUTER_BOUND, bf16_to_np, check_topk, close, load_cache,
-                              need_gpu, np_bf16_dev, oracle_cfg, random_cache, topk_margin)
+from tests.gpu_common import (MARGIN, ROUTER_BOUND, bf16_to_np, check_layer, close, layer_debug,
+                              load_cache, need_gpu, np_bf16_dev, oracle_cfg, random_cache, topk_margin)
 
 pytestmark = pytest.mark.gpu
 
@@ -124,46 +124,6 @@ def test_sampler_bitexact_over_steps(env):
             break
 
 
-def _layer_debug(dg, m, shape, rows, n_layers):
-    HD = shape.n_q_heads * shape.head_dim
-    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt, device="cuda")
-    return {
-        "hidden_out": z(rows, shape.d_model),
-        "attn_out": z(n_layers, rows, HD, dt=torch.bfloat16),
-        "h_mid": z(n_layers, rows, shape.d_model),
-        "expert_idx": z(n_layers, rows, shape.top_k, dt=torch.int32),
-        "gates": z(n_layers, rows, shape.top_k),
-        "canvas_k": z(n_layers, 1, shape.n_kv_heads, 256, shape.head_dim, dt=torch.bfloat16),
-        "canvas_v": z(n_layers, 1, shape.n_kv_heads, 256, shape.head_dim, dt=torch.bfloat16),
-    }
-
-
-def check_layer(dg, m, w, shape, Lp, seed, cap):
-    """One layer from a synthetic residual state: attention, FFN and canvas K/V vs the oracle."""
-    kv = dg.KV(shape, 1, cap)
-    k, v = random_cache(shape, Lp, cap, seed)
-    load_cache(kv, k, v, [Lp])
-    h = synth.hidden(256, shape.d_model, seed, 5)
-    dbg = _layer_debug(dg, m, shape, 256, shape.n_layers)
-    m.denoise_step(None, kv, None, 0, None, flags=dg.DG_STEP_HIDDEN_IN | dg.DG_STEP_NO_HEAD,
-                   hidden_in=torch.from_numpy(h).cuda(), debug=dbg)
-    torch.cuda.synchronize()
-    pos = Lp + np.arange(256)
-    h_out, ok_k, ok_v, od = omodel.layer(h, w["layers"][0], shape, pos, k[0, 0, :, :Lp], v[0, 0, :, :Lp], None)
-    close(bf16_to_np(dbg["attn_out"][0]), od["attn_out"], what="attention output")
-    close(dbg["h_mid"][0].cpu().numpy(), od["h_mid"], what="h after attention")
-    close(bf16_to_np(dbg["canvas_k"][0, 0]), ok_k, what="canvas K")
-    close(bf16_to_np(dbg["canvas_v"][0, 0]), ok_v, what="canvas V")
-    gi = dbg["expert_idx"][0].cpu().numpy()
-    safe = check_topk(gi, od["router_logits"], shape.top_k)
-    assert safe.mean() > 0.75, safe.mean()
-    order_ok = np.all(gi == od["expert_idx"], axis=1) & safe
-    close(dbg["gates"][0].cpu().numpy()[order_ok], od["gates"][order_ok], max_abs=1e-2, what="gates")
-    close(dbg["hidden_out"].cpu().numpy()[safe], h_out[safe], what="layer output")
-    close((dbg["hidden_out"].cpu().numpy() - dbg["h_mid"][0].cpu().numpy())[safe], od["ffn_out"][safe],
-          what="FFN output")
-
-
 def test_single_layer_parity(env):
     dg, w, _ = env
     shape = dataclasses.replace(SHAPE, n_layers=1)
@@ -267,7 +227,7 @@ def test_commit_after_denoise_appends_the_step_kv(env):
     dg, w, m = env
     kv, k, v = _kv(dg, cap=L + 256)
     x = torch.from_numpy(synth.tokens(256, SHAPE.vocab, SEED, 70)).cuda()
-    dbg = _layer_debug(dg, m, SHAPE, 256, 2)
+    dbg = layer_debug(dg, m, SHAPE, 256, 2)
     cfg = dg.sampler_cfg(seed=1)
     m.denoise_step(x, kv, cfg, 0, dg.Stats(1, 256), debug={"canvas_k": dbg["canvas_k"], "canvas_v": dbg["canvas_v"]})
     m.commit_block(x, kv, refresh=False)
