@@ -134,11 +134,29 @@ def cpu_baseline(shape, weights, prefix_len: int, sample_rows: int):
     }
 
 
+WORKLOADS = {
+    "full_canvas_loop": "12 layers d2048 16q/8kv hd128, 64 experts top-4 d_ff 768 + shared FFN 4096, "
+                        "vocab 65536, prefix 2048, canvas 256, sampler 48 steps 0.8->0.4 commit 16",
+    "batch8_ragged_32k": "same model, 8 requests with prefixes round(32768*(1+U(-1/4,1/4))) prefilled "
+                         "causally, 8 canvases of 256 denoised together (2048 rows per step)",
+    "long_generation": "same model, prefix 8192, 8 consecutive canvases each denoised until the sampler "
+                       "stops and then committed to the KV cache (final length 10240)",
+}
+
+
+def attention_flops(shape, lens) -> float:
+    """Algorithmic MFMA flops of one canvas-attention launch: QK^T and PV over the cached prefix
+    plus the canvas, 2 flops per multiply-add each."""
+    C = shape.canvas
+    return float(4 * shape.n_q_heads * shape.head_dim * sum(C * (L + C) for L in lens))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="full_canvas_loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the HIP-event per-kernel pass (e.g. under a profiler)")
@@ -148,7 +166,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}). "
-              "Requests shard across GPUs with no exchange; see the design notes.", file=sys.stderr)
+              "Independent requests would shard across GPUs with no exchange.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -159,19 +177,30 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     shape = synth.FULL
-    prefix_len = 2048
     log("drawing weights on the device")
     w = synth.torch_model_weights(shape, "cuda", SEED)
-    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=2048)
-    kv = dg.KV(shape, 1, prefix_len + shape.canvas)
-    prefix = torch.from_numpy(synth.tokens(prefix_len, shape.vocab, SEED, 1)).cuda()
-    log("prefill")
-    m.prefill(prefix, [prefix_len], kv)
-    torch.cuda.synchronize()
     cfg = dg.sampler_cfg(seed=SEED)
-    st = dg.Canvas(1, shape.canvas)
-    stats = dg.Stats(1, shape.canvas)
-    status = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    if args.workload == "long_generation":
+        return long_generation(args, shape, w, cfg)
+
+    if args.workload == "batch8_ragged_32k":
+        lens = synth.ragged_lengths(8, 32768, 0.25, SEED)
+    else:
+        lens = [2048]
+    B = len(lens)
+    m = dg.Model(shape, w, max_batch=B, max_prefill_rows=2048)
+    kv = dg.KV(shape, B, max(lens) + shape.canvas)
+    log(f"prefill {B} request(s), lengths {lens}")
+    t0 = time.perf_counter()
+    for b, L in enumerate(lens):  # one request at a time keeps progress visible
+        n = [0] * B
+        n[b] = L
+        m.prefill(torch.from_numpy(synth.tokens(L, shape.vocab, SEED, 1 + b)).cuda(), n, kv)
+        torch.cuda.synchronize()
+        log(f"  request {b}: {L} tokens, {time.perf_counter() - t0:.1f} s")
+    st = dg.Canvas(B, shape.canvas)
+    stats = dg.Stats(B, shape.canvas)
+    status = torch.zeros((B, 8), dtype=torch.int32, device="cuda")
     m.canvas_init(st, kv, cfg)
     counter = {"s": 0}
 
@@ -199,10 +228,11 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
-    value = shape.canvas / (ms * 1e-3)
+    value = B * shape.canvas / (ms * 1e-3)
 
     roofline = None
     kernels = None
+    extra = {}
     if not args.no_kernel_timing:
         m.timing(True)
         for _ in range(args.steps):
@@ -212,27 +242,90 @@ def main():
         m.timing(False)
         kernels = {k: round(v["total_ms"] / args.steps * 1e3, 2) for k, v in kt.items()}  # us per step
         g1 = kt["moe_gemm1_swiglu"]
-        routes = shape.canvas * shape.top_k
+        routes = B * shape.canvas * shape.top_k
         nbytes = expert_gemm1_bytes(shape, routes, shape.n_experts)
         ach = nbytes / (g1["avg_ms"] * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": "moe_gemm1_swiglu", "achieved": round(ach, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(), "avg_launch_us": round(g1["avg_ms"] * 1e3, 2),
-                    "algorithmic_bytes_per_launch": nbytes}
+        gemm1 = {"bound": "hbm", "kernel": "moe_gemm1_swiglu", "achieved": round(ach, 1),
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                 "traffic": measured_traffic() if B == 1 else None,
+                 "avg_launch_us": round(g1["avg_ms"] * 1e3, 2), "algorithmic_bytes_per_launch": nbytes}
+        at = kt["attention"]
+        fl = attention_flops(shape, lens)
+        tf = fl / (at["avg_ms"] * 1e-3) / 1e12
+        attn = {"bound": "mfma", "kernel": "attention (+ split combine)", "achieved": round(tf, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "avg_launch_us": round(at["avg_ms"] * 1e3, 2),
+                "algorithmic_flops_per_launch": fl}
+        roofline = gemm1 if args.workload == "full_canvas_loop" else attn
+        extra["attention_roofline"] = attn
+        extra["expert_gemm1_roofline"] = gemm1
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "full_canvas_loop":
         log("CPU oracle baseline (bounded sample)")
-        cpu = cpu_baseline(shape, w, prefix_len, args.cpu_sample_rows)
+        cpu = cpu_baseline(shape, w, lens[0], args.cpu_sample_rows)
     out = {
         "metric": "canvas positions/s (denoise step, 1 GPU)", "value": round(value, 1),
         "unit": "canvas positions/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded device RNG weights, uniform random tokens)",
-        "config": {"workload": "full_canvas_loop: 12 layers d2048 16q/8kv hd128, 64 experts top-4 "
-                               "d_ff 768 + shared FFN 4096, vocab 65536, prefix 2048, canvas 256, "
-                               "sampler 48 steps 0.8->0.4 commit 16",
-                   "global_batch": 1, "seq_len": prefix_len + shape.canvas, "parallelism": "single GPU"},
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}",
+                   "global_batch": B, "seq_len": max(lens) + shape.canvas, "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernel_us_per_step": kernels,
+        "wall_s_timed": round(t_wall, 3), **extra,
+    }
+    print(json.dumps(out), flush=True)
+    m.close()
+
+
+def long_generation(args, shape, w, cfg):
+    """Prefill 8192 tokens, then 8 canvases, each denoised until the sampler stops and then
+    committed (dg_commit_block), the next canvas attending to the grown cache.  The timed region
+    is the whole block loop; one pinned status read per step is its only host synchronisation."""
+    import torch
+    from block_discrete_diffusion_amd import dg, synth
+
+    L0, n_blocks = 8192, 8
+    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=2048)
+    kv = dg.KV(shape, 1, L0 + n_blocks * shape.canvas)
+    log(f"prefill {L0}")
+    m.prefill(torch.from_numpy(synth.tokens(L0, shape.vocab, SEED, 1)).cuda(), [L0], kv)
+    torch.cuda.synchronize()
+    stats = dg.Stats(1, shape.canvas)
+
+    def one_block():
+        st = dg.Canvas(1, shape.canvas)
+        m.canvas_init(st, kv, cfg)
+        res = m.denoise_canvas(st, kv, cfg, stats)
+        m.commit_block(st.tokens, kv, any(d["changed"] for d in res["status"]))
+        return res["steps"]
+
+    # warm-up on a scratch copy of the lengths: run one canvas, then roll the cache length back
+    log("warmup: one canvas (rolled back)")
+    one_block()
+    kv.set_lengths([L0])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps = []
+    t_wall = time.perf_counter()
+    e0.record()
+    for j in range(n_blocks):
+        steps.append(one_block())
+        log(f"  canvas {j}: {steps[-1]} steps")
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = e0.elapsed_time(e1)
+    n_steps = sum(steps)
+    out = {
+        "metric": "canvas positions/s (block-autoregressive generation, 1 GPU)",
+        "value": round(n_blocks * shape.canvas / (total_ms * 1e-3), 1), "unit": "finalised canvas positions/s",
+        "n_gpus": 1, "steps": n_steps, "warmup": 1, "ms_per_step": round(total_ms / n_steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded device RNG weights, uniform random tokens)",
+        "config": {"workload": f"long_generation: {WORKLOADS['long_generation']}", "global_batch": 1,
+                   "seq_len": L0 + n_blocks * shape.canvas, "parallelism": "single GPU"},
+        "steps_per_canvas": steps, "canvas_ms": round(total_ms / n_blocks, 3),
+        "final_kv_len": kv.lengths[0], "roofline": None, "cpu_baseline": None,
         "wall_s_timed": round(t_wall, 3),
     }
     print(json.dumps(out), flush=True)

@@ -166,9 +166,9 @@ RowMap make_map(int rows_per_req, int n_req, const int32_t* pos0) {
 }
 
 int choose_split(const dg_ctx* c, int base_wgs, int n_keys, int rows) {
-  // one work-group per CU (the attention kernel runs one 4-wave group per CU)
-  int ns = std::max(1, std::min(kMaxSplit, (256 + base_wgs - 1) / base_wgs));
-  ns = std::min(ns, std::max(1, (n_keys + 63) / 64));
+  // two 4-wave work-groups per CU, each split keeping at least four 64-key blocks
+  int ns = std::max(1, std::min(kMaxSplit, (512 + base_wgs - 1) / base_wgs));
+  ns = std::min(ns, std::max(1, n_keys / 256));
   ns = std::min(ns, std::max(1, c->part_cap / std::max(1, rows * c->m.n_q_heads)));
   return ns;
 }

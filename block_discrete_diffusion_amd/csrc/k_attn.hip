@@ -93,6 +93,11 @@ __global__ __launch_bounds__(256) void rope_scatter_kernel(RopeArgs a) {
 
 // ---------------------------------------------------------------------------- attention
 constexpr int KB = 64;       // keys per block
+
+// 2^x with the hardware instruction alone: results below 2^-126 flush to zero instead of going
+// through the denormal range fix-up (a probability that small is invisible next to the row sum,
+// which is at least 1).
+DG_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int VPAD = 4;      // V^T row padding (bf16)
 
 template <int D>
@@ -101,8 +106,11 @@ struct AttnSmem {
   uint16_t vt[D][KB + VPAD];
 };
 
+// Two work-groups per CU (at most 256 registers per lane): one group's MFMAs overlap the
+// other's softmax and K/V staging.
 template <int D>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attention_kernel(AttnArgs a) {
   constexpr int NKS = D / 32;   // MFMA k-steps over the head dimension
   constexpr int NDT = D / 16;   // 16-row tiles of O^T
   constexpr int KCH = KB * D / 8 / 256;      // 16-byte K chunks per thread
@@ -126,7 +134,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   const int n_cache = a.n_cache[b];
   const int n_keys = n_cache + a.n_extra;
   // key range of this split; with a causal mask it ends after the last query of the group
-  int k_lo = blockIdx.y * a.split_keys;
+  const int k_lo = blockIdx.y * a.split_keys;
   int k_hi = min(n_keys, k_lo + a.split_keys);
   if (a.causal) {
     const int last_task = min(blockIdx.x * 4 + 3, group * n_rb - 1);
@@ -156,153 +164,163 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  // running max (in log2 units, scale folded in) and sum per query
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const float sl2 = a.scale * 1.4426950408889634f;
 
-  // Base pointers as values: selecting between two kernel-argument fields per lane would make
-  // the compiler load the pointer itself from the argument segment before every K/V load.
   const long kv_head = static_cast<long>(b) * a.Hkv + g;
-  const uint16_t* const kc0 = a.kc + kv_head * a.cap * D;
-  const uint16_t* const vc0 = a.vc + kv_head * a.cap * D;
-  const uint16_t* const kx0 = a.kx + (kv_head * a.xcap - n_cache) * D;  // indexed by kk >= n_cache
-  const uint16_t* const vx0 = a.vx + (kv_head * a.xcap - n_cache) * D;
-  auto key_ptr_k = [=](int kk) -> const uint16_t* { return (kk < n_cache ? kc0 : kx0) + static_cast<long>(kk) * D; };
-  auto key_ptr_v = [=](int kk) -> const uint16_t* { return (kk < n_cache ? vc0 : vx0) + static_cast<long>(kk) * D; };
-
-  // Keys past the range end re-read the last valid key (never uninitialised cache memory, and
-  // every load is unconditional so wait counts stay exact); their scores are masked to -inf.
   u32x4_t rk[KCH], rv[VPT][4];
-  auto gload = [&](int kb0) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int kk = min(kb0 + key, k_hi - 1);
-      rk[i] = ld16(key_ptr_k(kk) + col);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int t = min(tid + 256 * i, VTASK - 1);
-      const int kq = t % (KB / 4), dq = t / (KB / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = min(kb0 + kq * 4 + r, k_hi - 1);
-        rv[i][r] = ld16(key_ptr_v(kk) + dq * 8);
-      }
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
-      st16(&sm.k[key][col], rk[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int t = tid + 256 * i;
-      if (t >= VTASK) continue;
-      const int kq = t % (KB / 4), dq = t / (KB / 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // element e of each of the 4 keys -> V^T[dq*8+e][kq*4 .. +4]
-        const int w = e >> 1;
-        const bool hi = e & 1;
-        uint32_t h4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) h4[r] = hi ? (rv[i][r][w] >> 16) : (rv[i][r][w] & 0xffffu);
-        *reinterpret_cast<u32x2_t*>(&sm.vt[dq * 8 + e][kq * 4]) =
-            u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
-      }
-    }
-  };
 
-  const int n_blk = (k_hi > k_lo) ? (k_hi - k_lo + KB - 1) / KB : 0;
-  if (n_blk > 0) gload(k_lo);
-  for (int blk = 0; blk < n_blk; ++blk) {
-    const int kb0 = k_lo + blk * KB;
-    __syncthreads();  // previous block's LDS reads are done
-    sstore();
-    __syncthreads();
-    gload(blk + 1 < n_blk ? kb0 + KB : kb0);  // unconditional: exact wait counts
-    sched_fence();
-    if (!active) continue;
-
-    // S^T for 4 key sub-blocks x 2 query tiles
-    floatx4_t s[4][2];
+  // Keys come in two ranges with one base pointer each (uniform, so addresses are a scalar
+  // base plus a lane offset): the cached prefix [0, n_cache) and the canvas [n_cache, n_keys).
+  // Keys past a range end re-read its last key (every load is unconditional, so wait counts
+  // stay exact) and are masked to -inf.
+  auto run_range = [&](const uint16_t* kbase, const uint16_t* vbase, int key0, int kb_lo, int kb_hi) {
+    auto gload = [&](int kb0) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const u32x4_t kf = ld16(&sm.k[kt * 16 + l16][ks * 32 + 8 * j4]);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
+      for (int i = 0; i < KCH; ++i) {
+        const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
+        const int kk = min(kb0 + key, kb_hi - 1) - key0;
+        rk[i] = ld16(kbase + static_cast<long>(kk) * D + col);
       }
-    }
-    // scale, mask (only blocks that cross the key range end or the causal diagonal),
-    // online softmax (per lane = per query)
-    const bool edge = (kb0 + KB > k_hi) || (a.causal && kb0 + KB - 1 > qmin);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float mx = -INFINITY;
+      for (int i = 0; i < VPT; ++i) {
+        const int t = min(tid + 256 * i, VTASK - 1);
+        const int kq = t % (KB / 4), dq = t / (KB / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = min(kb0 + kq * 4 + r, kb_hi - 1) - key0;
+          rv[i][r] = ld16(vbase + static_cast<long>(kk) * D + dq * 8);
+        }
+      }
+    };
+    auto sstore = [&]() {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
+        st16(&sm.k[key][col], rk[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int t = tid + 256 * i;
+        if (t >= VTASK) continue;
+        const int kq = t % (KB / 4), dq = t / (KB / 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // element e of each of the 4 keys -> V^T[dq*8+e][kq*4 .. +4]
+          const int w = e >> 1;
+          const bool hi = e & 1;
+          uint32_t h4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h4[r] = hi ? (rv[i][r][w] >> 16) : (rv[i][r][w] & 0xffffu);
+          *reinterpret_cast<u32x2_t*>(&sm.vt[dq * 8 + e][kq * 4]) =
+              u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
+        }
+      }
+    };
+
+    const int n_blk = (kb_hi > kb_lo) ? (kb_hi - kb_lo + KB - 1) / KB : 0;
+    if (n_blk > 0) gload(kb_lo);
+    for (int blk = 0; blk < n_blk; ++blk) {
+      const int kb0 = kb_lo + blk * KB;
+      __syncthreads();  // previous block's LDS reads are done
+      sstore();
+      __syncthreads();
+      gload(blk + 1 < n_blk ? kb0 + KB : kb0);  // unconditional: exact wait counts
+      sched_fence();
+      if (!active) continue;
+
+      // S^T for 4 key sub-blocks x 2 query tiles (raw dot products)
+      floatx4_t s[4][2];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[kt][qt][i] * sl2;
-          if (edge) {
-            const int kk = kb0 + kt * 16 + 4 * j4 + i;
-            if (kk >= k_hi || (a.causal && kk > qpos[qt])) v = -INFINITY;
-          }
-          s[kt][qt][i] = v;
-          mx = fmaxf(mx, v);
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const u32x4_t kf = ld16(&sm.k[kt * 16 + l16][ks * 32 + 8 * j4]);
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[qt], mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[qt] - m_new);
-      float sum = 0.f;
+      }
+      // mask only blocks that cross the range end or the causal diagonal (uniform branch)
+      if ((kb0 + KB > kb_hi) || (a.causal && kb0 + KB - 1 > qmin)) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = (m_new == -INFINITY) ? 0.f : exp2f(s[kt][qt][i] - m_new);
-          s[kt][qt][i] = p;
-          sum += p;
-        }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      l_run[qt] = l_run[qt] * alpha + sum;
-      m_run[qt] = m_new;
+          for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha;
-    }
-    // O^T += V^T P^T over two 32-key steps
-#pragma unroll
-    for (int kk2 = 0; kk2 < 2; ++kk2) {
-      u32x4_t pf[2];
+            for (int i = 0; i < 4; ++i) {
+              const int kk = kb0 + kt * 16 + 4 * j4 + i;
+              if (kk >= kb_hi || (a.causal && kk > qpos[qt])) s[kt][qt][i] = -INFINITY;
+            }
+      }
+      // online softmax per lane (= per query): p = 2^(s*sl2 - m), one FMA + one exp each
+      bool rescale = false;
+      float alpha[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        const floatx4_t p0 = s[2 * kk2][qt], p1 = s[2 * kk2 + 1][qt];
-        pf[qt] = u32x4_t{pack_bf2(p0[0], p0[1]), pack_bf2(p0[2], p0[3]), pack_bf2(p1[0], p1[1]),
-                         pack_bf2(p1[2], p1[3])};
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          mx = fmaxf(fmaxf(mx, fmaxf(s[kt][qt][0], s[kt][qt][1])), fmaxf(s[kt][qt][2], s[kt][qt][3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[qt], mx * sl2);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all keys masked so far
+        alpha[qt] = fast_exp2(m_run[qt] - m_use);                // 0 when m_run is -inf
+        rescale |= (alpha[qt] != 1.f);
+        float sum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(fmaf(s[kt][qt][i], sl2, -m_use));
+            s[kt][qt][i] = p;
+            sum += p;
+          }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        l_run[qt] = l_run[qt] * alpha[qt] + sum;
+        m_run[qt] = m_new;
       }
+      // rescaling O^T by alpha == 1 is exact, so it is skipped when no lane of the wave needs it
+      if (__any(rescale)) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint16_t* vr = &sm.vt[dt * 16 + l16][kk2 * 32 + 4 * j4];
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16);
-        const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma16(vf, pf[qt], o[dt][qt]);
+          for (int qt = 0; qt < 2; ++qt) o[dt][qt] *= alpha[qt];
+      }
+      // O^T += V^T P^T over two 32-key steps
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        u32x4_t pf[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const floatx4_t p0 = s[2 * kk2][qt], p1 = s[2 * kk2 + 1][qt];
+          pf[qt] = u32x4_t{pack_bf2(p0[0], p0[1]), pack_bf2(p0[2], p0[3]), pack_bf2(p1[0], p1[1]),
+                           pack_bf2(p1[2], p1[3])};
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint16_t* vr = &sm.vt[dt * 16 + l16][kk2 * 32 + 4 * j4];
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16);
+          const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma16(vf, pf[qt], o[dt][qt]);
+        }
       }
     }
-  }
+  };
+  run_range(a.kc + kv_head * a.cap * D, a.vc + kv_head * a.cap * D, 0, k_lo, min(k_hi, n_cache));
+  if (a.n_extra > 0)
+    run_range(a.kx + kv_head * a.xcap * D, a.vx + kv_head * a.xcap * D, n_cache, max(k_lo, n_cache), k_hi);
 
   if (!active) return;
-  // write: lane owns query qt*16+l16, dims dt*16 + 4*j4 + i
+  // write: lane owns query qt*16+l16, dims dt*16 + 4*j4 + i; partial maxima are in log2 units
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int qr = row0 + qt * 16 + l16;

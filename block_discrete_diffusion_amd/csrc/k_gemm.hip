@@ -116,19 +116,22 @@ struct Mainloop {
     // to LDS, so tiles t + 1 and t + 2 are in flight while tile t is multiplied.
     // Loads are unconditional (tile index clamped to the last tile, which is then re-read) so
     // no branch surrounds a load and the compiler's wait counts stay exact.
+    // The loop body always runs both halves and an odd last tile is handled after it: an exit
+    // between the halves would give the loop header a second predecessor in which the other
+    // register set was loaded last, and the compiler's wait counts would then drain every load.
     gload(0, 0);
     sstore(0, 0);
     gload(1, min(1, nk - 1));
     gload(0, min(2, nk - 1));
     __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
       compute(0);
       sched_fence();
       sstore(1, 1);
       gload(1, min(kt + 3, nk - 1));
       sched_fence();
       __syncthreads();
-      if (kt + 1 >= nk) break;
       compute(1);
       sched_fence();
       sstore(0, 0);
@@ -136,6 +139,7 @@ struct Mainloop {
       sched_fence();
       __syncthreads();
     }
+    if (kt < nk) compute(0);  // odd tile count: the last tile sits in buffer 0
   }
 };
 

@@ -14,7 +14,7 @@ diffusion head sits on the same backbone and reuses its prefill).  Two ways of r
   prefix and to every canvas position; the canvas K/V of each layer are returned (kept in
   float64 here) so they can be appended to the cache when the block is finished.
 
-Readings where the pages are silent (each one is listed with its reason in the design notes):
+Readings where the pages are silent:
 RMSNorm x * rsqrt(mean(x^2) + eps) * gain; RoPE rotate-half with theta 10000 at absolute
 positions, K cached after rotation; attention scale 1/sqrt(head_dim), query head h reads KV head
 h // (Hq/Hkv); router logits are a plain linear map, top-k by (logit descending, index

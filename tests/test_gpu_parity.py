@@ -180,8 +180,8 @@ def test_prefill_matches_oracle(env):
     cv = [np.zeros((2, L + 256, 64)) for _ in range(2)]
     omodel.prefill(w, SHAPE, toks, ck, cv, 0)
     for l in range(2):
-        close(bf16_to_np(kv.k[l, 0, :, :L]), ck[l][:, :L], what=f"prefill K layer {l}")
-        close(bf16_to_np(kv.v[l, 0, :, :L]), cv[l][:, :L], what=f"prefill V layer {l}")
+        close(bf16_to_np(kv.k[l, 0, :, :L]), ck[l][:, :L], what=f"prefill K layer {l}", bf16_out=True)
+        close(bf16_to_np(kv.v[l, 0, :, :L]), cv[l][:, :L], what=f"prefill V layer {l}", bf16_out=True)
 
 
 def test_prefill_chunked_equals_whole(env):
@@ -195,7 +195,7 @@ def test_prefill_chunked_equals_whole(env):
     torch.cuda.synchronize()
     assert a.lengths == b.lengths == [200]
     close(bf16_to_np(a.k[:, :, :, :200]), bf16_to_np(b.k[:, :, :, :200]), max_abs=2e-2, rel_l2=2e-3,
-          what="chunked prefill")
+          what="chunked prefill", bf16_out=True)
 
 
 def test_commit_block_bitexact_with_canaries(env):
@@ -239,7 +239,7 @@ def test_commit_after_denoise_appends_the_step_kv(env):
     fw = omodel.denoise_forward(w, SHAPE, x.cpu().numpy(), [k[l, 0] for l in range(2)],
                                 [v[l, 0] for l in range(2)], L, with_head=False)
     for l in range(2):
-        close(bf16_to_np(kv.k[l, 0, :, L:L + 256]), fw["canvas_k"][l], what=f"appended K layer {l}")
+        close(bf16_to_np(kv.k[l, 0, :, L:L + 256]), fw["canvas_k"][l], what=f"appended K layer {l}", bf16_out=True)
 
 
 def test_refresh_recomputes_kv_of_final_canvas(env):
