@@ -382,8 +382,8 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
     ok = c->alloc(&c->pk1[l], 2 * ew) && c->alloc(&c->pk2[l], ew);
     if (!ok) break;
     const dg_layer_weights& lw = c->layers[l];
-    launch_moe_pack(lw.w_gate, lw.w_up, c->pk1[l], m.n_experts, m.d_ff_expert, m.d_model, nullptr);
-    launch_moe_pack(lw.w_down, nullptr, c->pk2[l], m.n_experts, m.d_model, m.d_ff_expert, nullptr);
+    launch_moe_pack(lw.w_gate, lw.w_up, c->pk1[l], m.n_experts, m.d_ff_expert, m.d_model, kGroupTiles1, nullptr);
+    launch_moe_pack(lw.w_down, nullptr, c->pk2[l], m.n_experts, m.d_model, m.d_ff_expert, kGroupTiles2, nullptr);
   }
   if (ok) ok = hipDeviceSynchronize() == hipSuccess && hipGetLastError() == hipSuccess;
   if (!ok) {

@@ -121,10 +121,13 @@ struct MoeArgs {
 };
 // Packed expert weights: for expert e, 16-row tile ft and 32-wide k-step s, the MFMA A-operand
 // fragment of every matrix q (GEMM1: q = gate, up; GEMM2: q = down) is 64 lanes x 16 B, lane l
-// holding W_q[e][16 ft + l % 16][32 s + 8 (l / 16) .. + 8].  Order: [e][ft][s][q][lane], so a
-// wave streaming one tile over k reads contiguous memory.
+// holding W_q[e][16 ft + l % 16][32 s + 8 (l / 16) .. + 8].  Order:
+// [e][ft / G][s][ft % G][q][lane] with G = group_tiles, the tiles one work-group streams, so a
+// work-group reads one contiguous run.  N must be a multiple of 16 G.
+constexpr int kGroupTiles1 = 4;  // gate/up: 64 features per work-group
+constexpr int kGroupTiles2 = 8;  // down: 128 features per work-group
 void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int n_exp, int N,
-                     int K, hipStream_t s);
+                     int K, int group_tiles, hipStream_t s);
 // mean_rows: routed rows per expert on average (selects the token-tile depth per pass)
 void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s);
 void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s);

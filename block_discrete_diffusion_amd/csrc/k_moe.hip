@@ -79,187 +79,159 @@ __global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __rest
 }
 
 // --------------------------------------------------------------------------- expert GEMMs
-// Work-group = 4 waves on one 16-row tile of one expert's weights; wave w takes the w-th
-// quarter of the reduction dimension, so every wave streams a short contiguous run of the
-// packed weights (many waves in flight, small tail), and the four partial tiles are added in
-// LDS in wave order (deterministic).  The expert's routed rows are covered in passes of TT
-// 16-row tiles.  The k loop runs over chunks of KS k-steps through a two-stage register
-// pipeline: the weight fragments (non-temporal 16-byte loads; each wave-wide load is one
-// contiguous 1 KB fragment) and the gathered activation fragments of chunk c+1 are issued
-// before the MFMAs of chunk c.  Every load in the loop is unconditional (clamped row / chunk
-// indices) and a scheduling fence keeps each prefetch ahead of the MFMAs, so the compiler
-// waits only for the older chunk.
-template <bool GATED, int TT, int KS>
-__global__ __launch_bounds__(256) void moe_gemm_kernel(MoeArgs a) {
+// Expert GEMM with the activation operand shared through LDS: a work-group of 4 waves owns
+// 64 * FPW output features of one expert (wave w: the FPW 16-row weight tiles 4 FPW blockIdx.x +
+// FPW w + f) and covers the expert's routed rows in passes of TT 16-row tiles.  Per chunk of
+// KC = 32 * KS columns the group stages the pass's rows (gathered through perm for the gate/up
+// projection) into LDS once and all four waves read their B fragments from there, so each
+// activation row is fetched once per 64 * FPW features.  The weights stream straight into
+// registers from the packed fragment layout, whose tile groups match the work-groups: the
+// group reads one contiguous run (non-temporal 16-byte loads), two chunks ahead.
+//
+// Pipeline per chunk c: MFMAs of chunk c (weights in register set c & 1, activations in LDS
+// buffer c & 1); store chunk c+1's activations (loaded one chunk earlier) to the other buffer;
+// issue the loads of chunk c+2; barrier.  Loads are unconditional (clamped chunk and row
+// indices) and the loop body is the same on every trip, so the compiler's wait counts leave
+// the younger chunks in flight.
+template <bool GATED, int TT, int KS, int FPW>
+__global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
   constexpr int NA = GATED ? 2 : 1;
-  __shared__ floatx4_t red[3][NA][TT][64];
-  const int e = blockIdx.y, ft = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int GT = 4 * FPW;  // tiles per work-group = tiles per packed group
+  constexpr int KC = 32 * KS, ROWS = TT * 16, LDX = KC + 8, CPR = KC / 8;
+  constexpr int PIECES = ROWS * CPR, PPT = (PIECES + 255) / 256;
+  __shared__ uint16_t xs[2][ROWS * LDX];
+  const int e = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j4 = lane >> 4, l16 = lane & 15;
   const int p0 = a.offs[e], n_e = a.offs[e + 1] - p0;
   if (n_e == 0) return;  // uniform over the work-group
-  const int S = a.K / 32, sq = S / 4, s0 = w * sq;  // this wave's k-steps [s0, s0 + sq)
+  const int ft0 = blockIdx.x * GT + w * FPW;
+  const int S = a.K / 32, nch = S / KS;
   const uint16_t* wp =
-      a.wp + ((static_cast<long>(e) * (a.N / 16) + ft) * S + s0) * NA * 512 + lane * 8;
-  const int nch = sq / KS;
+      a.wp + ((static_cast<long>(e) * (a.N / (16 * GT)) + blockIdx.x) * S * GT + w * FPW) * NA * 512 + lane * 8;
 
-  for (int ps = 0; ps < n_e; ps += TT * 16) {
-    // rows past the expert's count re-read its last row; those columns are never stored
-    const uint16_t* xr[TT];
+  for (int ps = 0; ps < n_e; ps += ROWS) {
+    // this thread's staging pieces; rows past the expert's count repeat its last row and
+    // pieces past the tile are loaded (clamped) but not stored
+    const uint16_t* src[PPT];
+    int dst[PPT];
+    bool keep[PPT];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      const int r = min(ps + t * 16 + l16, n_e - 1);
-      const long row = GATED ? (a.perm[p0 + r] / a.top_k) : (p0 + r);
-      xr[t] = a.x + row * a.ldx + s0 * 32 + 8 * j4;
+    for (int j = 0; j < PPT; ++j) {
+      const int piece = tid + 256 * j, pc = min(piece, PIECES - 1);
+      const int r = pc / CPR, col = (pc % CPR) * 8;
+      const int rr = min(ps + r, n_e - 1);
+      const long row = GATED ? (a.perm[p0 + rr] / a.top_k) : static_cast<long>(p0 + rr);
+      src[j] = a.x + row * a.ldx + col;
+      dst[j] = r * LDX + col;
+      keep[j] = piece < PIECES;
     }
-    floatx4_t acc[NA][TT];
+    floatx4_t acc[FPW][NA][TT];
 #pragma unroll
-    for (int q = 0; q < NA; ++q)
-#pragma unroll
-      for (int t = 0; t < TT; ++t) acc[q][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    u32x4_t fw[2][KS][NA], fx[2][KS][TT];
-    auto load = [&](int b, int c) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int st = c * KS + ks;
-#pragma unroll
-        for (int q = 0; q < NA; ++q) fw[b][ks][q] = ld16_nt(wp + (st * NA + q) * 512);
-#pragma unroll
-        for (int t = 0; t < TT; ++t) fx[b][ks][t] = ld16(xr[t] + st * 32);
-      }
-    };
-    auto compute = [&](int b) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-#pragma unroll
-          for (int q = 0; q < NA; ++q) acc[q][t] = mfma16(fw[b][ks][q], fx[b][ks][t], acc[q][t]);
-    };
-    load(0, 0);
-    for (int c = 0; c < nch; c += 2) {
-      load(1, min(c + 1, nch - 1));
-      sched_fence();
-      compute(0);
-      sched_fence();
-      load(0, min(c + 2, nch - 1));
-      sched_fence();
-      if (c + 1 < nch) compute(1);
-      sched_fence();
-    }
-    if (w > 0) {
+    for (int f = 0; f < FPW; ++f)
 #pragma unroll
       for (int q = 0; q < NA; ++q)
 #pragma unroll
-        for (int t = 0; t < TT; ++t) red[w - 1][q][t][lane] = acc[q][t];
-    }
-    __syncthreads();
-    if (w == 0) {
-      // lane holds out[16 ft + 4 j4 + i][token col l16] of each tile
+        for (int t = 0; t < TT; ++t) acc[f][q][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4_t fw[2][KS][FPW][NA], xr[PPT];
+    auto load_w = [&](int b, int c) {
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        floatx4_t v[NA];
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int q = 0; q < NA; ++q)
-          v[q] = ((acc[q][t] + red[0][q][t][lane]) + red[1][q][t][lane]) + red[2][q][t][lane];
-        const int r = ps + t * 16 + l16;
-        if (r >= n_e) continue;
-        const long orow = static_cast<long>(p0 + r) * a.ldo + ft * 16 + 4 * j4;
-        if constexpr (GATED) {
-          float y[4];
+        for (int f = 0; f < FPW; ++f)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = v[0][i] / (1.0f + expf(-v[0][i])) * v[NA - 1][i];
-          *reinterpret_cast<u32x2_t*>(a.out_bf16 + orow) =
-              u32x2_t{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
-        } else {
-          *reinterpret_cast<floatx4_t*>(a.out_f32 + orow) = v[0];
+          for (int q = 0; q < NA; ++q)
+            fw[b][ks][f][q] = ld16_nt(wp + (((c * KS + ks) * GT + f) * NA + q) * 512);
+    };
+    auto load_x = [&](int c) {
+#pragma unroll
+      for (int j = 0; j < PPT; ++j) xr[j] = ld16(src[j] + c * KC);
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < PPT; ++j)
+        if (keep[j]) st16(&xs[buf][dst[j]], xr[j]);
+    };
+    auto compute = [&](int buf, int b) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const u32x4_t xf = ld16(&xs[buf][(t * 16 + l16) * LDX + ks * 32 + 8 * j4]);
+#pragma unroll
+          for (int f = 0; f < FPW; ++f)
+#pragma unroll
+            for (int q = 0; q < NA; ++q) acc[f][q][t] = mfma16(fw[b][ks][f][q], xf, acc[f][q][t]);
         }
-      }
-    }
-    __syncthreads();  // red is reused by the next pass
-  }
-}
-
-// Down projection (no gate): the expert's routed rows of the SwiGLU output are small (K = d_ff),
-// so a work-group stages TT*16 of them in LDS once and its 4 waves each stream the full K of
-// their own 16-row weight tile (64 output features per work-group) with the activation
-// fragments read from LDS; only weights come from HBM in the k loop.
-template <int TT, int KS>
-__global__ __launch_bounds__(256) void moe_down_kernel(MoeArgs a) {
-  extern __shared__ uint16_t xs[];  // [TT*16][K + 8]
-  const int e = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int j4 = lane >> 4, l16 = lane & 15;
-  const int p0 = a.offs[e], n_e = a.offs[e + 1] - p0;
-  if (n_e == 0) return;  // uniform over the work-group
-  const int ft = blockIdx.x * 4 + w;
-  const int S = a.K / 32, ldx = a.K + 8;
-  const uint16_t* wp = a.wp + (static_cast<long>(e) * (a.N / 16) + ft) * S * 512 + lane * 8;
-  const int nch = S / KS;
-  const int cpr = a.K / 8;  // 16-byte chunks per activation row
-  for (int ps = 0; ps < n_e; ps += TT * 16) {
-    // stage rows [ps, ps + TT*16) (rows past the count repeat the last one; never stored)
-    for (int c = threadIdx.x; c < TT * 16 * cpr; c += 256) {
-      const int r = c / cpr, col = (c - r * cpr) * 8;
-      const long row = p0 + min(ps + r, n_e - 1);
-      st16(xs + r * ldx + col, ld16(a.x + row * a.ldx + col));
-    }
+    };
+    load_x(0);
+    load_w(0, 0);
+    store_x(0);
+    load_x(min(1, nch - 1));
+    load_w(1, min(1, nch - 1));
     __syncthreads();
-    floatx4_t acc[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    u32x4_t fw[2][KS];
-    auto load = [&](int b, int c) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) fw[b][ks] = ld16_nt(wp + (c * KS + ks) * 512);
-    };
-    auto compute = [&](int b, int c) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int kk = (c * KS + ks) * 32 + 8 * j4;
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-          acc[t] = mfma16(fw[b][ks], ld16(xs + (t * 16 + l16) * ldx + kk), acc[t]);
-      }
-    };
-    load(0, 0);
-    for (int c = 0; c < nch; c += 2) {
-      load(1, min(c + 1, nch - 1));
+    int c = 0;
+    for (; c + 1 < nch; c += 2) {
+      compute(0, 0);
       sched_fence();
-      compute(0, c);
+      store_x(1);
+      load_x(min(c + 2, nch - 1));
+      load_w(0, min(c + 2, nch - 1));
       sched_fence();
-      load(0, min(c + 2, nch - 1));
+      __syncthreads();
+      compute(1, 1);
       sched_fence();
-      if (c + 1 < nch) compute(1, c + 1);
+      store_x(0);
+      load_x(min(c + 3, nch - 1));
+      load_w(1, min(c + 3, nch - 1));
       sched_fence();
+      __syncthreads();
     }
+    if (c < nch) compute(0, 0);  // odd chunk count: the last chunk sits in buffer / set 0
+    // lane holds out[16 ft + 4 j4 + i][row col l16] of each tile
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       const int r = ps + t * 16 + l16;
       if (r >= n_e) continue;
-      *reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(p0 + r) * a.ldo + ft * 16 + 4 * j4) = acc[t];
+#pragma unroll
+      for (int f = 0; f < FPW; ++f) {
+        const long orow = static_cast<long>(p0 + r) * a.ldo + (ft0 + f) * 16 + 4 * j4;
+        if constexpr (GATED) {
+          float y[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            y[i] = acc[f][0][t][i] / (1.0f + expf(-acc[f][0][t][i])) * acc[f][NA - 1][t][i];
+          *reinterpret_cast<u32x2_t*>(a.out_bf16 + orow) = u32x2_t{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
+        } else {
+          *reinterpret_cast<floatx4_t*>(a.out_f32 + orow) = acc[f][0][t];
+        }
+      }
     }
-    __syncthreads();  // xs is restaged by the next pass
+    if (ps + ROWS < n_e) __syncthreads();  // the next pass restages xs (uniform condition)
   }
 }
 
-// One thread per 16-byte fragment piece of the packed layout.
+// One thread per 16-byte fragment piece of the packed layout
+// [e][tile group fg][k-step s][tile w in group][matrix q][lane], tile ft = gt fg + w.
 __global__ __launch_bounds__(256) void moe_pack_kernel(const uint16_t* __restrict__ w0,
                                                        const uint16_t* __restrict__ w1,
                                                        uint16_t* __restrict__ out, int n_exp,
-                                                       int N, int K, int na) {
-  const int S = K / 32, T = N / 16;
-  const long total = static_cast<long>(n_exp) * T * S * na * 64;
+                                                       int N, int K, int na, int gt) {
+  const int S = K / 32, G = N / (16 * gt);
+  const long total = static_cast<long>(n_exp) * G * S * gt * na * 64;
   const long c = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
   if (c >= total) return;
   const int lane = static_cast<int>(c % 64);
   long r = c / 64;
   const int q = static_cast<int>(r % na);
   r /= na;
+  const int w = static_cast<int>(r % gt);
+  r /= gt;
   const int st = static_cast<int>(r % S);
   r /= S;
-  const int ft = static_cast<int>(r % T);
-  const long e = r / T;
+  const int fg = static_cast<int>(r % G);
+  const long e = r / G;
+  const int ft = gt * fg + w;
   const uint16_t* src = (q == 0 ? w0 : w1) + ((e * N + ft * 16 + (lane & 15)) * static_cast<long>(K)) +
                         st * 32 + 8 * (lane >> 4);
   st16(out + c * 8, ld16(src));
@@ -316,36 +288,25 @@ void launch_moe_permute(const int32_t* idx, int n_routes, int n_exp, int32_t* of
                      perm, inv);
 }
 
-// Gate/up: token tiles per pass from the mean routed rows per expert; one k-step per chunk
-// (measured fastest: lowest register count, most waves in flight).
-void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s) {
-  const dim3 grid(a.N / 16, a.n_exp);
-  if (mean_rows <= 24) hipLaunchKernelGGL((moe_gemm_kernel<true, 2, 1>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((moe_gemm_kernel<true, 4, 1>), grid, dim3(256), 0, s, a);
+// Row tiles per pass from the mean routed rows per expert (one pass for most experts).
+template <bool GATED, int FPW>
+void launch_stream(const MoeArgs& a, int mean_rows, hipStream_t s) {
+  const dim3 grid(a.N / (64 * FPW), a.n_exp);
+  if (mean_rows <= 24) hipLaunchKernelGGL((expert_stream_kernel<GATED, 2, 2, FPW>), grid, dim3(256), 0, s, a);
+  else if (mean_rows <= 48) hipLaunchKernelGGL((expert_stream_kernel<GATED, 4, 2, FPW>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((expert_stream_kernel<GATED, 8, 2, FPW>), grid, dim3(256), 0, s, a);
 }
 
-// Down: activation rows staged in LDS ((TT*16) x (K+8) bf16), 64 output features per group.
-void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s) {
-  const dim3 grid(a.N / 64, a.n_exp);
-  const int S = a.K / 32;
-  if (mean_rows <= 24) {
-    const size_t lds = 2 * 16 * static_cast<size_t>(a.K + 8) * 2;
-    if (S % 4 == 0) hipLaunchKernelGGL((moe_down_kernel<2, 4>), grid, dim3(256), lds, s, a);
-    else if (S % 2 == 0) hipLaunchKernelGGL((moe_down_kernel<2, 2>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((moe_down_kernel<2, 1>), grid, dim3(256), lds, s, a);
-  } else {
-    const size_t lds = 4 * 16 * static_cast<size_t>(a.K + 8) * 2;
-    if (S % 2 == 0) hipLaunchKernelGGL((moe_down_kernel<4, 2>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((moe_down_kernel<4, 1>), grid, dim3(256), lds, s, a);
-  }
-}
+// gate/up: 64 features per work-group; down: 128 (a longer weight run per wave)
+void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s) { launch_stream<true, kGroupTiles1 / 4>(a, mean_rows, s); }
+void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s) { launch_stream<false, kGroupTiles2 / 4>(a, mean_rows, s); }
 
 void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int n_exp, int N, int K,
-                     hipStream_t s) {
+                     int group_tiles, hipStream_t s) {
   const int na = w1 ? 2 : 1;
   const long total = static_cast<long>(n_exp) * (N / 16) * (K / 32) * na * 64;
   hipLaunchKernelGGL(moe_pack_kernel, dim3((total + 255) / 256), dim3(256), 0, s, w0, w1, out, n_exp,
-                     N, K, na);
+                     N, K, na, group_tiles);
 }
 
 void launch_moe_combine(float* h, const float* part, int n_part, long part_stride, const float* y,

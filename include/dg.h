@@ -169,7 +169,7 @@ typedef struct {
 
 /* Create a context for `desc` over caller-owned device weights.  The expert banks (w_gate,
  * w_up, w_down) are copied once into the context's own memory in the layout the expert GEMMs
- * stream (MFMA operand fragments, contiguous per 16-row tile); they are read only during
+ * stream (MFMA operand fragments, contiguous per group of four 16-row tiles); they are read only during
  * dg_create.  Every other weight pointer must stay valid for the context's lifetime.  max_batch: largest batch
  * (<= 64) of later calls; max_prefill_rows: largest prefill chunk processed at once (rows are
  * split into chunks of this size).  Returns DG_OK and *out, or an error code. */
