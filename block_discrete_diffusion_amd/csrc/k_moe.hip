@@ -292,7 +292,7 @@ void launch_moe_permute(const int32_t* idx, int n_routes, int n_exp, int32_t* of
 template <bool GATED, int FPW>
 void launch_stream(const MoeArgs& a, int mean_rows, hipStream_t s) {
   const dim3 grid(a.N / (64 * FPW), a.n_exp);
-  if (mean_rows <= 24) hipLaunchKernelGGL((expert_stream_kernel<GATED, 2, 2, FPW>), grid, dim3(256), 0, s, a);
+  if (mean_rows <= 24) hipLaunchKernelGGL((expert_stream_kernel<GATED, 3, 1, FPW>), grid, dim3(256), 0, s, a);
   else if (mean_rows <= 48) hipLaunchKernelGGL((expert_stream_kernel<GATED, 4, 2, FPW>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((expert_stream_kernel<GATED, 8, 2, FPW>), grid, dim3(256), 0, s, a);
 }
