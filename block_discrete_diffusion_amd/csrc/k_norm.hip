@@ -74,122 +74,125 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
   }
 }
 
-// Residual update + FFN norm + router + top-k, one work-group (4 waves) per row.
+// Residual update + FFN norm + router + top-k, one work-group (8 waves) per row.
 //  - every load of the row (residual, its split-K slices) is issued before the reduction;
 //  - h += slices (z order, written back); x = h * rsqrt(mean h^2 + eps) * gain in float32;
-//    the bf16 copy of x feeds the experts;
-//  - router logits in float32: thread t owns x[8t' .. 8t'+8) for its chunks t' and forms the
-//    partial dot product with every expert row of W_router (coalesced 16-byte reads: 256
-//    threads cover 4 KB of one expert row); the 64 partials are summed over the wave by a
-//    butterfly transpose-reduce (6 exchange steps halving the expert window; lane e ends with
-//    expert e) and over the 4 waves in LDS in wave order;
+//    the bf16 copy of x feeds the experts and the float32 x is kept in LDS;
+//  - router logits in float32: wave w owns experts 8w .. 8w+7 and requests the weights of all
+//    eight rows at once (one memory round trip for d <= 2048); lane l owns the row elements
+//    [8 (l + 64 j), +8) (coalesced 16-byte reads: a wave covers 1 KB of one expert row per
+//    request); the eight partials are summed over the wave by a transpose-reduce (three
+//    exchange steps halving the expert window, then three plain steps), after which lane l
+//    holds expert 8w + (l >> 3);
 //  - wave 0: lane e = expert e, k rounds of wave arg-max (ties to the lower expert index),
 //    softmax gates over the k picks.
-template <int NCH>  // 8-element chunks per thread: ceil(d / 2048)
-__global__ __launch_bounds__(256) void norm_router_kernel(
+constexpr int kRouterWaves = 8;
+template <int NCH>  // 4-element chunks per thread: ceil(d / 2048)
+__global__ __launch_bounds__(512) void norm_router_kernel(
     float* __restrict__ h, const float* __restrict__ part, int n_part, long part_stride,
     const float* __restrict__ gain, float eps, const uint16_t* __restrict__ wr, int d, int n_exp,
     int top_k, uint16_t* __restrict__ bout, int32_t* __restrict__ idx, float* __restrict__ gates) {
-  __shared__ float red[4];
-  __shared__ float lg[4][64];
-  const int r = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float* x = h + static_cast<long>(r) * d;
-  float v[NCH][8];
-  floatx4_t pz[kMaxParts][NCH][2];
+  __shared__ float red[kRouterWaves];
+  __shared__ float lg[64];
+  __shared__ float xs[NCH * 2048];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float* hr = h + static_cast<long>(r) * d;
+  floatx4_t v[NCH], pz[kMaxParts][NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = (threadIdx.x + 256 * i) * 8;
+    const int c = (tid + 512 * i) * 4;
     const bool ok = c < d;
-    const floatx4_t a0 = ok ? *reinterpret_cast<const floatx4_t*>(x + c) : floatx4_t{0.f, 0.f, 0.f, 0.f};
-    const floatx4_t a1 = ok ? *reinterpret_cast<const floatx4_t*>(x + c + 4) : floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { v[i][q] = a0[q]; v[i][4 + q] = a1[q]; }
+    v[i] = ok ? *reinterpret_cast<const floatx4_t*>(hr + c) : floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int z = 0; z < kMaxParts; ++z)
-      if (z < n_part && ok) {
-        const float* pp = part + z * part_stride + static_cast<long>(r) * d + c;
-        pz[z][i][0] = *reinterpret_cast<const floatx4_t*>(pp);
-        pz[z][i][1] = *reinterpret_cast<const floatx4_t*>(pp + 4);
-      }
+      if (z < n_part && ok) pz[z][i] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + static_cast<long>(r) * d + c);
   }
   if (n_part > 0) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = (threadIdx.x + 256 * i) * 8;
+      const int c = (tid + 512 * i) * 4;
 #pragma unroll
       for (int z = 0; z < kMaxParts; ++z)
-        if (z < n_part)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { v[i][q] += pz[z][i][0][q]; v[i][4 + q] += pz[z][i][1][q]; }
-      if (c < d) {
-        *reinterpret_cast<floatx4_t*>(x + c) = floatx4_t{v[i][0], v[i][1], v[i][2], v[i][3]};
-        *reinterpret_cast<floatx4_t*>(x + c + 4) = floatx4_t{v[i][4], v[i][5], v[i][6], v[i][7]};
-      }
+        if (z < n_part) v[i] += pz[z][i];
+      if (c < d) *reinterpret_cast<floatx4_t*>(hr + c) = v[i];
     }
   }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) ss += v[i][q] * v[i][q];
+    for (int q = 0; q < 4; ++q) ss += v[i][q] * v[i][q];
   ss = wave_sum(ss);
   if (lane == 0) red[w] = ss;
   __syncthreads();
-  ss = (red[0] + red[1]) + (red[2] + red[3]);
+  ss = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
   const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = (threadIdx.x + 256 * i) * 8;
+    const int c = (tid + 512 * i) * 4;
     if (c >= d) continue;
-    const floatx4_t g0 = *reinterpret_cast<const floatx4_t*>(gain + c);
-    const floatx4_t g1 = *reinterpret_cast<const floatx4_t*>(gain + c + 4);
+    const floatx4_t g = *reinterpret_cast<const floatx4_t*>(gain + c);
+    floatx4_t x;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) { v[i][q] *= inv * g0[q]; v[i][4 + q] *= inv * g1[q]; }
-    *reinterpret_cast<u32x4_t*>(bout + static_cast<long>(r) * d + c) =
-        u32x4_t{pack_bf2(v[i][0], v[i][1]), pack_bf2(v[i][2], v[i][3]), pack_bf2(v[i][4], v[i][5]),
-                pack_bf2(v[i][6], v[i][7])};
+    for (int q = 0; q < 4; ++q) x[q] = v[i][q] * inv * g[q];
+    *reinterpret_cast<u32x2_t*>(bout + static_cast<long>(r) * d + c) = u32x2_t{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])};
+    *reinterpret_cast<floatx4_t*>(&xs[c]) = x;
   }
-  // per-thread partial logits of all experts, 8 experts per batch of loads
-  float p[64];
+  __syncthreads();
+
+  // router: 8 experts per wave, 4 row chunks of 512 elements per round of loads
+  float p[8];
 #pragma unroll
-  for (int e0 = 0; e0 < 64; e0 += 8) {
-    u32x4_t wv[8][NCH];
+  for (int e = 0; e < 8; ++e) p[e] = 0.f;
+  const int nj = (d + 511) / 512;
+  for (int j0 = 0; j0 < nj; j0 += 4) {
+    u32x4_t wv[4][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int c = (threadIdx.x + 256 * i) * 8;
-        const int ee = min(e0 + e, n_exp - 1);
-        wv[e][i] = (c < d) ? ld16(wr + static_cast<long>(ee) * d + c) : u32x4_t{0u, 0u, 0u, 0u};
+      for (int e = 0; e < 8; ++e) {
+        const int c = min((lane + 64 * (j0 + jj)) * 8, d - 8);  // clamped: always in bounds
+        const int ee = min(8 * w + e, n_exp - 1);
+        wv[jj][e] = ld16(wr + static_cast<long>(ee) * d + c);
       }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float acc = 0.f;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int c = (lane + 64 * (j0 + jj)) * 8;
+      if (c >= d) continue;
+      const floatx4_t x0 = *reinterpret_cast<const floatx4_t*>(&xs[c]);
+      const floatx4_t x1 = *reinterpret_cast<const floatx4_t*>(&xs[c + 4]);
 #pragma unroll
-      for (int i = 0; i < NCH; ++i)
+      for (int e = 0; e < 8; ++e) {
+        float acc = p[e];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc += __uint_as_float(wv[e][i][q] << 16) * v[i][2 * q];
-          acc += __uint_as_float(wv[e][i][q] & 0xffff0000u) * v[i][2 * q + 1];
+        for (int q = 0; q < 2; ++q) {
+          acc += __uint_as_float(wv[jj][e][q] << 16) * x0[2 * q];
+          acc += __uint_as_float(wv[jj][e][q] & 0xffff0000u) * x0[2 * q + 1];
+          acc += __uint_as_float(wv[jj][e][2 + q] << 16) * x1[2 * q];
+          acc += __uint_as_float(wv[jj][e][2 + q] & 0xffff0000u) * x1[2 * q + 1];
         }
-      p[e0 + e] = acc;
+        p[e] = acc;
+      }
     }
   }
-  // butterfly transpose-reduce over the wave: lane e ends with the wave's sum for expert e
+  // transpose-reduce: halve the expert window over lane bits 5, 4, 3, then sum over bits 2..0
 #pragma unroll
-  for (int sft = 32; sft >= 1; sft >>= 1) {
+  for (int sft = 32, win = 4; sft >= 8; sft >>= 1, win >>= 1) {
     const bool up = (lane & sft) != 0;
 #pragma unroll
-    for (int j = 0; j < sft; ++j) {
-      const float keep = up ? p[sft + j] : p[j];
-      const float give = up ? p[j] : p[sft + j];
+    for (int j = 0; j < win; ++j) {
+      const float keep = up ? p[win + j] : p[j];
+      const float give = up ? p[j] : p[win + j];
       p[j] = keep + __shfl_xor(give, sft, 64);
     }
   }
-  lg[w][lane] = p[0];
+  p[0] += __shfl_xor(p[0], 4, 64);
+  p[0] += __shfl_xor(p[0], 2, 64);
+  p[0] += __shfl_xor(p[0], 1, 64);
+  if ((lane & 7) == 0 && 8 * w + (lane >> 3) < 64) lg[8 * w + (lane >> 3)] = p[0];
   __syncthreads();
   if (w != 0) return;
-  const float logit = (lane < n_exp) ? ((lg[0][lane] + lg[1][lane]) + lg[2][lane]) + lg[3][lane] : -INFINITY;
+  const float logit = (lane < n_exp) ? lg[lane] : -INFINITY;
   float vv = logit, my_val = -INFINITY, first = -INFINITY;
   int my_idx = 0;
   for (int j = 0; j < top_k; ++j) {
@@ -239,7 +242,7 @@ void launch_norm_router(float* h, const float* part, int n_part, long part_strid
                         hipStream_t s) {
   const int nch = (d + 2047) / 2048;
 #define DG_NR(N)                                                                               \
-  hipLaunchKernelGGL(norm_router_kernel<N>, dim3(rows), dim3(256), 0, s, h, part, n_part,         \
+  hipLaunchKernelGGL(norm_router_kernel<N>, dim3(rows), dim3(512), 0, s, h, part, n_part,         \
                      part_stride, gain, eps, w_router, d, n_exp, top_k, b_out, idx, gates)
   if (nch <= 1) DG_NR(1);
   else if (nch <= 2) DG_NR(2);
