@@ -177,7 +177,8 @@ int choose_split(const dg_ctx* c, int base_wgs, int n_keys, int rows) {
 // Denoise mode: K/V of the rows go to the canvas scratch; keys = cache[0:len) + canvas.
 // Prefill mode (one request): K/V go to the cache at len..; keys = cache[0:len+rows), causal.
 void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len, bool prefill,
-               uint16_t* kc_l, uint16_t* vc_l, int cap, const dg_debug* dbg, hipStream_t s) {
+               uint16_t* kc_l, uint16_t* vc_l, int cap, const dg_debug* dbg, const float* next_gain,
+               uint16_t* next_out, hipStream_t s) {
   const dg_model_desc& m = c->m;
   const dg_layer_weights& lw = c->layers[l];
   const int rows = n_req * rows_per_req;
@@ -185,8 +186,7 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   const int nqkv = (Hq + 2 * Hkv) * D;
   const RowMap map = make_map(rows_per_req, n_req, len);
 
-  timed(c, "rmsnorm", s, [&] { launch_rmsnorm(c->h, lw.attn_norm, m.rms_eps, c->a, rows, d, s); });
-
+  // c->a holds this layer's normed input (written by the embedding or the previous combine)
   GemmArgs g{};
   g.part = c->gpart;
   g.x = c->a; g.ldx = d; g.n_tok = rows;
@@ -296,7 +296,7 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   }
   timed(c, "moe_combine", s, [&] {
     launch_moe_combine(c->h, c->gpart, n_res, static_cast<long>(rows) * d, c->y, c->inv, c->gates, rows,
-                       d, m.top_k, s);
+                       d, m.top_k, next_gain, m.rms_eps, next_out, s);
   });
   if (dbg && dbg->layer_out)
     (void)hipMemcpyAsync(dbg->layer_out + static_cast<long>(l) * rows * d, c->h,
@@ -427,13 +427,15 @@ int dg_prefill_causal(dg_ctx* c, const int32_t* tokens, const int32_t* n_new, in
   for (int b = 0; b < batch; ++b) {
     for (int done = 0; done < n_new[b];) {
       const int n = std::min(c->max_prefill, n_new[b] - done);
-      launch_embed(tokens + tok_ofs + done, c->w.embed, c->h, n, m.d_model, s);
+      launch_embed(tokens + tok_ofs + done, c->w.embed, c->h, n, m.d_model, c->layers[0].attn_norm,
+                   m.rms_eps, c->a, s);
       const int32_t len_b = kv->len[b] + done;
       if (m.rope_theta != 0.f) launch_rope_table(make_map(n, 1, &len_b), n, m.head_dim, m.rope_theta, c->rope, s);
       for (int l = 0; l < m.n_layers; ++l) {
         const long base = l * kv_layer_stride(m, kv->batch, kv->cap) +
                           static_cast<long>(b) * m.n_kv_heads * kv->cap * m.head_dim;
-        run_layer(c, l, 1, n, &len_b, true, kv->k + base, kv->v + base, kv->cap, nullptr, s);
+        const float* ng = (l + 1 < m.n_layers) ? c->layers[l + 1].attn_norm : nullptr;
+        run_layer(c, l, 1, n, &len_b, true, kv->k + base, kv->v + base, kv->cap, nullptr, ng, c->a, s);
       }
       done += n;
     }
@@ -469,17 +471,25 @@ static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
   const bool no_head = flags & DG_STEP_NO_HEAD;
 
   if (!head_only) {
-    if (flags & DG_STEP_HIDDEN_IN)
+    if (flags & DG_STEP_HIDDEN_IN) {
       (void)hipMemcpyAsync(c->h, p->hidden_in, sizeof(float) * rows * d, hipMemcpyDeviceToDevice, s);
-    else
-      timed(c, "embed", s, [&] { launch_embed(canvas, c->w.embed, c->h, rows, d, s); });
+      launch_rmsnorm(c->h, c->layers[0].attn_norm, m.rms_eps, c->a, rows, d, s);
+    } else {
+      timed(c, "embed_norm", s, [&] {
+        launch_embed(canvas, c->w.embed, c->h, rows, d, c->layers[0].attn_norm, m.rms_eps, c->a, s);
+      });
+    }
     if (m.rope_theta != 0.f)
       timed(c, "rope_table", s, [&] {
         launch_rope_table(make_map(C, B, kv->len), rows, m.head_dim, m.rope_theta, c->rope, s);
       });
-    for (int l = 0; l < m.n_layers; ++l)
+    // each layer's combine also norms the next layer's input; the last one the head's input
+    for (int l = 0; l < m.n_layers; ++l) {
+      const bool last = l + 1 == m.n_layers;
+      const float* ng = !last ? c->layers[l + 1].attn_norm : (no_head ? nullptr : c->w.final_norm);
       run_layer(c, l, B, C, kv->len, false, kv->k + l * kv_layer_stride(m, B, kv->cap),
-                kv->v + l * kv_layer_stride(m, B, kv->cap), kv->cap, dbg, s);
+                kv->v + l * kv_layer_stride(m, B, kv->cap), kv->cap, dbg, ng, last ? c->f : c->a, s);
+    }
     if (dbg && dbg->hidden_out)
       (void)hipMemcpyAsync(dbg->hidden_out, c->h, sizeof(float) * rows * d, hipMemcpyDeviceToDevice, s);
     if (dbg && (dbg->canvas_k || dbg->canvas_v)) {
@@ -495,12 +505,8 @@ static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
     }
   }
   if (no_head) return DG_OK;
-  const uint16_t* f = c->f;
-  if (head_only) {
-    f = static_cast<const uint16_t*>(p->hidden_in);
-  } else {
-    timed(c, "final_norm", s, [&] { launch_rmsnorm(c->h, c->w.final_norm, m.rms_eps, c->f, rows, d, s); });
-  }
+  // the final norm was fused into the last layer's combine
+  const uint16_t* f = head_only ? static_cast<const uint16_t*>(p->hidden_in) : c->f;
   HeadArgs ha{};
   ha.f = f; ha.n_rows = rows; ha.w = c->w.lm_head; ha.K = d; ha.V = m.vocab;
   ha.temp = dg_temperature(cfg, p ? p->step : 0);

@@ -16,8 +16,9 @@ struct RowMap {
 };
 
 // ---- k_norm.hip
+// h = E[tok] as float32; with a gain also out = bf16(rmsnorm(h) * gain) (the first layer's input)
 void launch_embed(const int32_t* tok, const uint16_t* embed, float* h, int rows, int d,
-                  hipStream_t s);
+                  const float* gain, float eps, uint16_t* out, hipStream_t s);
 void launch_rmsnorm(const float* h, const float* gain, float eps, uint16_t* out, int rows, int d,
                     hipStream_t s);
 void launch_f32_to_bf16(const float* in, uint16_t* out, long n, hipStream_t s);
@@ -131,10 +132,11 @@ void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int 
 // mean_rows: routed rows per expert on average (selects the token-tile depth per pass)
 void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s);
 void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s);
-// h[t] += sum_z part_z[t] (n_part residual slices, z order) + sum_j gate[t][j] * y[inv[t][j]]
+// h[t] += sum_z part_z[t] (n_part residual slices, z order) + sum_j gate[t][j] * y[inv[t][j]];
+// with a gain also out[t] = bf16(rmsnorm(h[t]) * gain) (the next block's input)
 void launch_moe_combine(float* h, const float* part, int n_part, long part_stride, const float* y,
                         const int32_t* inv, const float* gates, int rows, int d, int top_k,
-                        hipStream_t s);
+                        const float* gain, float eps, uint16_t* out, hipStream_t s);
 
 // ---- k_sampler.hip
 struct SamplerArgs {

@@ -237,47 +237,79 @@ __global__ __launch_bounds__(256) void moe_pack_kernel(const uint16_t* __restric
   st16(out + c * 8, ld16(src));
 }
 
-// h[t] += sum_z part_z[t] + sum_j gate[t][j] * y[inv[t*k+j]]  (z then j in order; one thread
-// per 4 columns)
-__global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
+// Un-permute + residual, one work-group (8 waves) per row t:
+// h[t] += sum_z part_z[t] + sum_j gate[t][j] * y[inv[t*k+j]]   (z then j in order);
+// with a gain it also writes the next block's normed input out = bf16(rmsnorm(h[t]) * gain),
+// which saves a pass over h.  All of a thread's loads are issued before any arithmetic.
+template <int NCH>  // 4-element chunks per thread: ceil(d / 2048)
+__global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
                                                           const float* __restrict__ part,
                                                           int n_part, long part_stride,
                                                           const float* __restrict__ y,
                                                           const int32_t* __restrict__ inv,
-                                                          const float* __restrict__ gates,
-                                                          int rows, int d, int top_k) {
-  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-  const int per_row = d / 4;
-  if (i >= static_cast<long>(rows) * per_row) return;
-  const int t = static_cast<int>(i / per_row), c = static_cast<int>(i % per_row) * 4;
-  floatx4_t pz[kMaxParts], yj[8];
-  float gj[8];
+                                                          const float* __restrict__ gates, int d,
+                                                          int top_k, const float* __restrict__ gain,
+                                                          float eps, uint16_t* __restrict__ out) {
+  __shared__ float red[8];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float* hr = h + static_cast<long>(t) * d;
+  constexpr int KJ = 8;  // routed slots held in registers; more are read in the second loop
+  int pj[KJ];
+  float gj[KJ];
 #pragma unroll
-  for (int z = 0; z < kMaxParts; ++z)
-    if (z < n_part) pz[z] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + static_cast<long>(t) * d + c);
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < KJ; ++j)
     if (j < top_k) {
+      pj[j] = inv[static_cast<long>(t) * top_k + j];
       gj[j] = gates[static_cast<long>(t) * top_k + j];
-      yj[j] = *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(inv[static_cast<long>(t) * top_k + j]) * d + c);
     }
-  floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  floatx4_t v[NCH], pz[kMaxParts][NCH], yj[KJ][NCH];
 #pragma unroll
-  for (int z = 0; z < kMaxParts; ++z)
-    if (z < n_part) acc += pz[z];
-  for (int j = 0; j < top_k; ++j) {
-    if (j < 8) {
-      acc += gj[j] * yj[j];
-    } else {
+  for (int i = 0; i < NCH; ++i) {
+    const int c = min((tid + 512 * i) * 4, d - 4);  // clamped; chunks past d are not stored
+    v[i] = *reinterpret_cast<const floatx4_t*>(hr + c);
+#pragma unroll
+    for (int z = 0; z < kMaxParts; ++z)
+      if (z < n_part) pz[z][i] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + static_cast<long>(t) * d + c);
+#pragma unroll
+    for (int j = 0; j < KJ; ++j)
+      if (j < top_k) yj[j][i] = *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(pj[j]) * d + c);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (tid + 512 * i) * 4;
+    floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < kMaxParts; ++z)
+      if (z < n_part) acc += pz[z][i];
+#pragma unroll
+    for (int j = 0; j < KJ; ++j)
+      if (j < top_k) acc += gj[j] * yj[j][i];
+    for (int j = KJ; j < top_k; ++j) {
       const float g = gates[static_cast<long>(t) * top_k + j];
       const int p = inv[static_cast<long>(t) * top_k + j];
-      acc += g * *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(p) * d + c);
+      acc += g * *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(p) * d + min(c, d - 4));
+    }
+    v[i] += acc;
+    if (c < d) {
+      *reinterpret_cast<floatx4_t*>(hr + c) = v[i];
+      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
     }
   }
-  floatx4_t* hp = reinterpret_cast<floatx4_t*>(h + static_cast<long>(t) * d + c);
-  floatx4_t o = *hp;
-  o += acc;
-  *hp = o;
+  if (!gain) return;  // uniform
+  ss = wave_sum(ss);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  ss = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+  const float rinv = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (tid + 512 * i) * 4;
+    if (c >= d) continue;
+    const floatx4_t g = *reinterpret_cast<const floatx4_t*>(gain + c);
+    *reinterpret_cast<u32x2_t*>(out + static_cast<long>(t) * d + c) =
+        u32x2_t{pack_bf2(v[i][0] * rinv * g[0], v[i][1] * rinv * g[1]), pack_bf2(v[i][2] * rinv * g[2], v[i][3] * rinv * g[3])};
+  }
 }
 
 }  // namespace
@@ -311,10 +343,15 @@ void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int 
 
 void launch_moe_combine(float* h, const float* part, int n_part, long part_stride, const float* y,
                         const int32_t* inv, const float* gates, int rows, int d, int top_k,
-                        hipStream_t s) {
-  const long n = static_cast<long>(rows) * (d / 4);
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, h, part, n_part,
-                     part_stride, y, inv, gates, rows, d, top_k);
+                        const float* gain, float eps, uint16_t* out, hipStream_t s) {
+  const int nch = (d + 2047) / 2048;
+#define DG_MC(N)                                                                              \
+  hipLaunchKernelGGL(moe_combine_kernel<N>, dim3(rows), dim3(512), 0, s, h, part, n_part,         \
+                     part_stride, y, inv, gates, d, top_k, gain, eps, out)
+  if (nch <= 1) DG_MC(1);
+  else if (nch <= 2) DG_MC(2);
+  else DG_MC(4);
+#undef DG_MC
 }
 
 }  // namespace dg

@@ -10,22 +10,55 @@
 namespace dg {
 namespace {
 
+// Embedding gather h = E[tok] (bf16 rows widened to float32), one work-group per row; with a
+// gain it also writes the first layer's normed input out = bf16(h * rsqrt(mean h^2 + eps) * gain).
+template <int NCH>  // 8-element chunks per thread: ceil(d / 2048)
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok,
                                                     const uint16_t* __restrict__ embed,
-                                                    float* __restrict__ h, int d) {
-  const int r = blockIdx.x;
+                                                    float* __restrict__ h, int d,
+                                                    const float* __restrict__ gain, float eps,
+                                                    uint16_t* __restrict__ out) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long src = static_cast<long>(tok[r]) * d;
-  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
-    const u32x4_t v = ld16(embed + src + c);
-    float o[8];
+  u32x4_t raw[NCH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = __uint_as_float(v[i] << 16);
-      o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (threadIdx.x + 256 * i) * 8;
+    raw[i] = (c < d) ? ld16(embed + src + c) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  float o[NCH][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[i][2 * q] = __uint_as_float(raw[i][q] << 16);
+      o[i][2 * q + 1] = __uint_as_float(raw[i][q] & 0xffff0000u);
     }
+    const int c = (threadIdx.x + 256 * i) * 8;
+    if (c >= d) continue;
     float* dst = h + static_cast<long>(r) * d + c;
-    *reinterpret_cast<floatx4_t*>(dst) = floatx4_t{o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<floatx4_t*>(dst + 4) = floatx4_t{o[4], o[5], o[6], o[7]};
+    *reinterpret_cast<floatx4_t*>(dst) = floatx4_t{o[i][0], o[i][1], o[i][2], o[i][3]};
+    *reinterpret_cast<floatx4_t*>(dst + 4) = floatx4_t{o[i][4], o[i][5], o[i][6], o[i][7]};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ss += o[i][q] * o[i][q];
+  }
+  if (!gain) return;  // uniform
+  ss = wave_sum(ss);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  ss = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (threadIdx.x + 256 * i) * 8;
+    if (c >= d) continue;
+    const floatx4_t g0 = *reinterpret_cast<const floatx4_t*>(gain + c);
+    const floatx4_t g1 = *reinterpret_cast<const floatx4_t*>(gain + c + 4);
+    *reinterpret_cast<u32x4_t*>(out + static_cast<long>(r) * d + c) =
+        u32x4_t{pack_bf2(o[i][0] * inv * g0[0], o[i][1] * inv * g0[1]), pack_bf2(o[i][2] * inv * g0[2], o[i][3] * inv * g0[3]),
+                pack_bf2(o[i][4] * inv * g1[0], o[i][5] * inv * g1[1]), pack_bf2(o[i][6] * inv * g1[2], o[i][7] * inv * g1[3])};
   }
 }
 
@@ -219,8 +252,11 @@ __global__ __launch_bounds__(512) void norm_router_kernel(
 }  // namespace
 
 void launch_embed(const int32_t* tok, const uint16_t* embed, float* h, int rows, int d,
-                  hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, s, tok, embed, h, d);
+                  const float* gain, float eps, uint16_t* out, hipStream_t s) {
+  const int nch = (d + 2047) / 2048;
+  if (nch <= 1) hipLaunchKernelGGL(embed_kernel<1>, dim3(rows), dim3(256), 0, s, tok, embed, h, d, gain, eps, out);
+  else if (nch <= 2) hipLaunchKernelGGL(embed_kernel<2>, dim3(rows), dim3(256), 0, s, tok, embed, h, d, gain, eps, out);
+  else hipLaunchKernelGGL(embed_kernel<4>, dim3(rows), dim3(256), 0, s, tok, embed, h, d, gain, eps, out);
 }
 
 void launch_rmsnorm(const float* h, const float* gain, float eps, uint16_t* out, int rows, int d,
