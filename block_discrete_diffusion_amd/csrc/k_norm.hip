@@ -144,10 +144,11 @@ __global__ __launch_bounds__(512) void norm_router_kernel(
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = (tid + 512 * i) * 4;
+      if (c >= d) continue;  // no slices were loaded there: v stays zero
 #pragma unroll
       for (int z = 0; z < kMaxParts; ++z)
         if (z < n_part) v[i] += pz[z][i];
-      if (c < d) *reinterpret_cast<floatx4_t*>(hr + c) = v[i];
+      *reinterpret_cast<floatx4_t*>(hr + c) = v[i];
     }
   }
   float ss = 0.f;
