@@ -11,9 +11,9 @@
 // from LDS, B = its 32 queries from registers).  The accumulator gives each lane one query
 // (lane % 16) and four keys, which is exactly the B-operand layout of the next MFMA,
 // O^T += V^T P^T, if the 32 keys of one MFMA are taken as {4j..4j+3} of two 16-key sub-blocks
-// (the k order inside an MFMA only has to agree between A and B).  V is stored transposed in
-// LDS so the A operand V^T[d][keys] is two 8-byte reads.  The online-softmax state (max, sum)
-// is per query = per lane, so rescaling O^T needs no cross-lane traffic.
+// (the k order inside an MFMA only has to agree between A and B).  V stays [key][d] in LDS and
+// the A operand V^T[d][keys] is two transposing 8-byte LDS reads.  The online-softmax state
+// (max, sum) is per query = per lane, so rescaling O^T needs no cross-lane traffic.
 #include "dg_common.h"
 #include "dg_kernels.h"
 
@@ -94,16 +94,29 @@ __global__ __launch_bounds__(256) void rope_scatter_kernel(RopeArgs a) {
 // ---------------------------------------------------------------------------- attention
 constexpr int KB = 64;       // keys per block
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane group, lane s points
+// at 4 consecutive 16-bit values of row s / 4, columns 4 (s % 4) .. +4 of a 4 x 16 block; lane
+// 4a + c receives column 4a + c of the four rows.  Used so that V can stay [key][d] in LDS and
+// still feed the A operand V^T of O^T += V^T P^T.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+DG_DEVICE u32x2_t read_tr16(const uint16_t* p) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
 // 2^x with the hardware instruction alone: results below 2^-126 flush to zero instead of going
 // through the denormal range fix-up (a probability that small is invisible next to the row sum,
 // which is at least 1).
 DG_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-constexpr int VPAD = 4;      // V^T row padding (bf16)
 
+// K and V blocks as they are in memory ([key][d]); rows padded so that the 16-byte K-fragment
+// reads (16 rows, 4 banks each) and the transposing 8-byte V reads (4 rows x 32 bytes per
+// 16 lanes) both hit distinct banks.
 template <int D>
 struct AttnSmem {
   uint16_t k[KB][D + 8];
-  uint16_t vt[D][KB + VPAD];
+  uint16_t v[KB][D + 16];
 };
 
 // Two work-groups per CU (at most 256 registers per lane): one group's MFMAs overlap the
@@ -114,8 +127,6 @@ void attention_kernel(AttnArgs a) {
   constexpr int NKS = D / 32;   // MFMA k-steps over the head dimension
   constexpr int NDT = D / 16;   // 16-row tiles of O^T
   constexpr int KCH = KB * D / 8 / 256;      // 16-byte K chunks per thread
-  constexpr int VTASK = (KB / 4) * (D / 8);  // (key quad, d octet) tasks
-  constexpr int VPT = (VTASK + 255) / 256;
   __shared__ AttnSmem<D> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -169,7 +180,7 @@ void attention_kernel(AttnArgs a) {
   const float sl2 = a.scale * 1.4426950408889634f;
 
   const long kv_head = static_cast<long>(b) * a.Hkv + g;
-  u32x4_t rk[KCH], rv[VPT][4];
+  u32x4_t rk[KCH], rv[KCH];
 
   // Keys come in two ranges with one base pointer each (uniform, so addresses are a scalar
   // base plus a lane offset): the cached prefix [0, n_cache) and the canvas [n_cache, n_keys).
@@ -180,18 +191,9 @@ void attention_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
         const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
-        const int kk = min(kb0 + key, kb_hi - 1) - key0;
-        rk[i] = ld16(kbase + static_cast<long>(kk) * D + col);
-      }
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int t = min(tid + 256 * i, VTASK - 1);
-        const int kq = t % (KB / 4), dq = t / (KB / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kk = min(kb0 + kq * 4 + r, kb_hi - 1) - key0;
-          rv[i][r] = ld16(vbase + static_cast<long>(kk) * D + dq * 8);
-        }
+        const long kk = min(kb0 + key, kb_hi - 1) - key0;
+        rk[i] = ld16(kbase + kk * D + col);
+        rv[i] = ld16(vbase + kk * D + col);
       }
     };
     auto sstore = [&]() {
@@ -199,23 +201,7 @@ void attention_kernel(AttnArgs a) {
       for (int i = 0; i < KCH; ++i) {
         const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
         st16(&sm.k[key][col], rk[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int t = tid + 256 * i;
-        if (t >= VTASK) continue;
-        const int kq = t % (KB / 4), dq = t / (KB / 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // element e of each of the 4 keys -> V^T[dq*8+e][kq*4 .. +4]
-          const int w = e >> 1;
-          const bool hi = e & 1;
-          uint32_t h4[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) h4[r] = hi ? (rv[i][r][w] >> 16) : (rv[i][r][w] & 0xffffu);
-          *reinterpret_cast<u32x2_t*>(&sm.vt[dq * 8 + e][kq * 4]) =
-              u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
-        }
+        st16(&sm.v[key][col], rv[i]);
       }
     };
 
@@ -305,9 +291,11 @@ void attention_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const uint16_t* vr = &sm.vt[dt * 16 + l16][kk2 * 32 + 4 * j4];
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16);
+          // A = V^T[d = 16 dt + l16][the 8 keys of P's lane group]: two transposing reads, each
+          // giving this lane 4 consecutive keys of its d column
+          const int kr = kk2 * 32 + 4 * j4 + (l16 >> 2), dc = dt * 16 + 4 * (l16 & 3);
+          const u32x2_t lo = read_tr16(&sm.v[kr][dc]);
+          const u32x2_t hi = read_tr16(&sm.v[kr + 16][dc]);
           const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma16(vf, pf[qt], o[dt][qt]);
