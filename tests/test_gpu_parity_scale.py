@@ -176,3 +176,19 @@ def test_block_autoregressive_generation(tiny_env, renoise):
                                         [K[l][b] for l in range(SHAPE.n_layers)],
                                         [V[l][b] for l in range(SHAPE.n_layers)], st)
     assert not torch.equal(blocks[0], blocks[1])
+
+
+def test_layer_narrower_than_a_work_group_with_split_projection():
+    """d = 1024 (fewer row elements than the 512-lane norm/router work-group covers) with a
+    2048-wide attention output, so the O-projection is split into slices that the norm adds:
+    lanes past the row width must stay out of the sum (regression: they once summed slices
+    that were never loaded and turned every router logit into NaN)."""
+    dg = need_gpu()
+    shape = synth.ModelShape(n_layers=1, d_model=1024, n_q_heads=16, n_kv_heads=8, head_dim=128,
+                             n_experts=8, top_k=2, d_ff_expert=256, d_ff_shared=0, vocab=1024)
+    w = synth.model_weights(shape, SEED + 5)
+    m = dg.Model(shape, w, max_batch=1)
+    try:
+        check_layer(dg, m, w, shape, 300, SEED + 6, 300 + 256)
+    finally:
+        m.close()
