@@ -372,12 +372,22 @@ void launch_cfg(const GemmArgs& a, hipStream_t s) {
 }
 
 // Tile shape.  Up to 256 tokens (one canvas) 64 x 64 tiles: measured at these shapes they beat
-// both wider token tiles (fewer, longer work-groups) and narrower feature tiles.  Larger batches:
-// 64 x 128 tiles when there are plenty of them, else 64 x 64 / 32 x 64.
+// both wider token tiles (fewer, longer work-groups) and narrower feature tiles.  From 1024
+// tokens 128 x 128 tiles (64 x 64 per wave: half the LDS fragment traffic per MFMA) where every
+// weight segment is a whole number of tiles; otherwise 64 x 128 tiles when there are plenty of
+// them, else 64 x 64 / 32 x 64.
+bool segments_fit(const GemmArgs& a, int bf) {
+  if (a.N % bf) return false;
+  for (int sg = 0; sg < a.n_seg; ++sg)
+    if ((a.seg_start[sg + 1] - a.seg_start[sg]) % bf) return false;
+  return true;
+}
+
 template <int EPI>
 void pick_tile(const GemmArgs& a, int* bf, int* bt) {
   const int tt64 = (a.n_tok + 63) / 64, tt128 = (a.n_tok + 127) / 128;
-  if (a.n_tok >= 128 && (a.N / 64) * tt128 >= 512) { *bf = 64; *bt = 128; }
+  if (EPI != EPI_SWIGLU_BF16 && a.n_tok >= 1024 && segments_fit(a, 128)) { *bf = 128; *bt = 128; }
+  else if (a.n_tok >= 128 && (a.N / 64) * tt128 >= 512) { *bf = 64; *bt = 128; }
   else if (a.n_tok <= 256 || (a.N / 64) * tt64 >= 256 || EPI == EPI_SWIGLU_BF16) { *bf = 64; *bt = 64; }
   else { *bf = 32; *bt = 64; }
 }
@@ -386,6 +396,9 @@ template <int EPI>
 void launch_epi(const GemmArgs& a, hipStream_t s) {
   int bf, bt;
   pick_tile<EPI>(a, &bf, &bt);
+  if constexpr (EPI != EPI_SWIGLU_BF16) {
+    if (bf == 128) { launch_cfg<128, 128, EPI>(a, s); return; }
+  }
   if (bf == 64 && bt == 128) launch_cfg<64, 128, EPI>(a, s);
   else if (bf == 64) launch_cfg<64, 64, EPI>(a, s);
   else launch_cfg<32, 64, EPI>(a, s);
@@ -432,10 +445,16 @@ void launch_swiglu_reduce(const float* part, long part_stride, int split, uint16
                      split, act, n4);
 }
 
+// 128 vocab entries x 64 rows per work-group for one canvas; 128 x 128 from 1024 rows (half the
+// LDS fragment traffic per MFMA, and still one work-group per CU or more)
 void launch_head(const HeadArgs& a, hipStream_t s) {
-  constexpr int BF = 128, BT = 64;
-  const int G = ((a.n_rows + BT - 1) / BT) * (a.V / BF);
-  hipLaunchKernelGGL((head_kernel<BF, BT>), dim3(G), dim3(256), 0, s, a);
+  if (a.n_rows >= 1024) {
+    const int G = ((a.n_rows + 127) / 128) * (a.V / 128);
+    hipLaunchKernelGGL((head_kernel<128, 128>), dim3(G), dim3(256), 0, s, a);
+  } else {
+    const int G = ((a.n_rows + 63) / 64) * (a.V / 128);
+    hipLaunchKernelGGL((head_kernel<128, 64>), dim3(G), dim3(256), 0, s, a);
+  }
 }
 
 void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
