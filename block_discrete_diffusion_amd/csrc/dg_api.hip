@@ -165,9 +165,11 @@ RowMap make_map(int rows_per_req, int n_req, const int32_t* pos0) {
   return r;
 }
 
-int choose_split(const dg_ctx* c, int base_wgs, int n_keys, int rows) {
-  // two 4-wave work-groups per CU, each split keeping at least four 64-key blocks
-  int ns = std::max(1, std::min(kMaxSplit, (512 + base_wgs - 1) / base_wgs));
+int choose_split(const dg_ctx* c, int base_wgs, int n_keys, int rows, int waves) {
+  // two waves per SIMD (two 4-wave or one 8-wave work-group per CU), each split keeping at
+  // least four 64-key blocks
+  const int target = 256 * (8 / waves);
+  int ns = std::max(1, std::min(kMaxSplit, (target + base_wgs - 1) / base_wgs));
   ns = std::min(ns, std::max(1, n_keys / 256));
   ns = std::min(ns, std::max(1, c->part_cap / std::max(1, rows * c->m.n_q_heads)));
   return ns;
@@ -226,8 +228,9 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   at.causal = prefill ? 1 : 0;
   at.scale = 1.0f / std::sqrt(static_cast<float>(D));
   const int tasks = (Hq / Hkv) * ((rows_per_req + 31) / 32);
-  const int base = ((tasks + 3) / 4) * n_req * Hkv;
-  at.n_split = choose_split(c, base, max_keys, rows);
+  at.n_waves = attention_waves(max_keys);
+  const int base = ((tasks + at.n_waves - 1) / at.n_waves) * n_req * Hkv;
+  at.n_split = choose_split(c, base, max_keys, rows, at.n_waves);
   at.split_keys = (((max_keys + at.n_split - 1) / at.n_split + 63) / 64) * 64;
   at.n_split = (max_keys + at.split_keys - 1) / at.split_keys;
   at.part_o = c->part_o; at.part_ml = c->part_ml;

@@ -105,7 +105,11 @@ struct AttnArgs {
   float scale;                  // 1/sqrt(D)
   int n_split; int split_keys;  // split-KV: each split covers split_keys keys
   float* part_o; float* part_ml;  // partials when n_split > 1
+  int n_waves;                    // query tasks per work-group: 4 or 8 (attention_waves)
 };
+// Waves per work-group for a key range of max_keys: 8 for long ranges (each staged block serves
+// twice the queries), else 4.
+int attention_waves(int max_keys);
 void launch_attention(const AttnArgs& a, hipStream_t s);
 
 // ---- k_moe.hip

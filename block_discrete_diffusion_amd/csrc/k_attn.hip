@@ -119,14 +119,17 @@ struct AttnSmem {
   uint16_t v[KB][D + 16];
 };
 
-// Two work-groups per CU (at most 256 registers per lane): one group's MFMAs overlap the
-// other's softmax and K/V staging.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NW waves (query tasks) share each staged K/V block; at most 256 registers per lane, so two
+// waves per SIMD: with 4 waves two work-groups share a CU (one group's MFMAs overlap the other's
+// softmax and staging), with 8 waves each block is staged once for twice the queries (less
+// staging per MFMA, used for long key ranges).
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_kernel(AttnArgs a) {
+  constexpr int NT = 64 * NW;
   constexpr int NKS = D / 32;   // MFMA k-steps over the head dimension
   constexpr int NDT = D / 16;   // 16-row tiles of O^T
-  constexpr int KCH = KB * D / 8 / 256;      // 16-byte K chunks per thread
+  constexpr int KCH = KB * D / 8 / NT;      // 16-byte K/V chunks per thread
   __shared__ AttnSmem<D> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -136,7 +139,7 @@ void attention_kernel(AttnArgs a) {
   const int group = a.Hq / a.Hkv;
   const int rows = a.rows_per_req;
   const int n_rb = (rows + 31) / 32;
-  const int task = blockIdx.x * 4 + wave;
+  const int task = blockIdx.x * NW + wave;
   const bool active = task < group * n_rb;
   const int hq = g * group + (active ? task % group : 0);
   const int rb = active ? task / group : 0;
@@ -148,7 +151,7 @@ void attention_kernel(AttnArgs a) {
   const int k_lo = blockIdx.y * a.split_keys;
   int k_hi = min(n_keys, k_lo + a.split_keys);
   if (a.causal) {
-    const int last_task = min(blockIdx.x * 4 + 3, group * n_rb - 1);
+    const int last_task = min(blockIdx.x * NW + NW - 1, group * n_rb - 1);
     const int last_row = min(rows - 1, (last_task / group) * 32 + 31);
     k_hi = min(k_hi, a.q_pos0[b] + last_row + 1);
   }
@@ -190,7 +193,7 @@ void attention_kernel(AttnArgs a) {
     auto gload = [&](int kb0) {
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
-        const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
+        const int c = tid + NT * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
         const long kk = min(kb0 + key, kb_hi - 1) - key0;
         rk[i] = ld16(kbase + kk * D + col);
         rv[i] = ld16(vbase + kk * D + col);
@@ -199,7 +202,7 @@ void attention_kernel(AttnArgs a) {
     auto sstore = [&]() {
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
-        const int c = tid + 256 * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
+        const int c = tid + NT * i, key = c / (D / 8), col = (c % (D / 8)) * 8;
         st16(&sm.k[key][col], rk[i]);
         st16(&sm.v[key][col], rv[i]);
       }
@@ -364,12 +367,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
       u32x2_t{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
 }
 
-template <int D>
-void launch_attn_d(const AttnArgs& a, hipStream_t s) {
+template <int D, int NW>
+void launch_attn_w(const AttnArgs& a, hipStream_t s) {
   const int group = a.Hq / a.Hkv;
   const int tasks = group * ((a.rows_per_req + 31) / 32);
-  dim3 grid((tasks + 3) / 4, a.n_split, a.n_req * a.Hkv);
-  hipLaunchKernelGGL((attention_kernel<D>), grid, dim3(256), 0, s, a);
+  dim3 grid((tasks + NW - 1) / NW, a.n_split, a.n_req * a.Hkv);
+  hipLaunchKernelGGL((attention_kernel<D, NW>), grid, dim3(64 * NW), 0, s, a);
+}
+
+template <int D>
+void launch_attn_d(const AttnArgs& a, hipStream_t s) {
+  if (a.n_waves == 8) launch_attn_w<D, 8>(a, s);
+  else launch_attn_w<D, 4>(a, s);
   if (a.n_split > 1) {
     const int n_rh = a.n_req * a.rows_per_req * a.Hq;
     const int per = 256 / (D / 4);
@@ -379,6 +388,8 @@ void launch_attn_d(const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int attention_waves(int max_keys) { return max_keys >= 8192 ? 8 : 4; }
 
 void launch_rope_table(const RowMap& map, int rows, int D, float theta, float* table, hipStream_t s) {
   const long n = static_cast<long>(rows) * (D / 2);

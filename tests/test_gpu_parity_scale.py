@@ -34,10 +34,11 @@ def full_env():
     m.close()
 
 
-@pytest.mark.parametrize("prefix", [2048, 4096, 777])
+@pytest.mark.parametrize("prefix", [2048, 4096, 777, 8192])
 def test_full_shape_layer_with_shared_ffn(full_env, prefix):
     """One layer at the full shape with the shared FFN: attention over `prefix` cached keys plus
-    the canvas, routed experts, shared FFN; all 256 rows against the oracle."""
+    the canvas, routed experts, shared FFN; all 256 rows against the oracle.  8192 cached keys
+    take the long-range attention variant (8 waves per staged block)."""
     dg, w, m, host = full_env
     check_layer(dg, m, host, FULL1, prefix, SEED + prefix, prefix + 256)
 
@@ -190,5 +191,31 @@ def test_layer_narrower_than_a_work_group_with_split_projection():
     m = dg.Model(shape, w, max_batch=1)
     try:
         check_layer(dg, m, w, shape, 300, SEED + 6, 300 + 256)
+    finally:
+        m.close()
+
+
+def test_long_causal_prefill():
+    """Causal prefill of 8300 tokens in chunks of 512: the later chunks attend to more than 8192
+    keys (the long-range attention variant, causal); the cache equals the oracle's prefill.
+    Every expert is active (top-k = E) so that no router near-tie can swap experts for a row
+    and move the next layer's inputs: the comparison is end to end over both layers."""
+    dg = need_gpu()
+    shape = dataclasses.replace(SHAPE, n_experts=4, top_k=4)
+    w = synth.model_weights(shape, SEED + 7)
+    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=512)
+    try:
+        n = 8300
+        toks = synth.tokens(n, shape.vocab, SEED, 500)
+        kv = dg.KV(shape, 1, n + 256)
+        m.prefill(torch.from_numpy(toks).cuda(), [n], kv)
+        torch.cuda.synchronize()
+        assert kv.lengths == [n]
+        ck = [np.zeros((shape.n_kv_heads, n + 256, shape.head_dim)) for _ in range(shape.n_layers)]
+        cv = [np.zeros((shape.n_kv_heads, n + 256, shape.head_dim)) for _ in range(shape.n_layers)]
+        omodel.prefill(w, shape, toks, ck, cv, 0)
+        for l in range(shape.n_layers):
+            close(bf16_to_np(kv.k[l, 0, :, :n]), ck[l][:, :n], what=f"prefill K layer {l}", bf16_out=True)
+            close(bf16_to_np(kv.v[l, 0, :, :n]), cv[l][:, :n], what=f"prefill V layer {l}", bf16_out=True)
     finally:
         m.close()
