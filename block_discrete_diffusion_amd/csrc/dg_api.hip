@@ -151,7 +151,7 @@ std::string validate_desc(const dg_model_desc& m) {
   if (m.d_ff_expert < 128 || m.d_ff_expert % 128 || m.d_ff_expert > 1024)
     return bad("d_ff_expert: multiple of 128, <= 1024");
   if (m.d_ff_shared < 0 || m.d_ff_shared % 64) return bad("d_ff_shared % 64");
-  if (m.vocab < 128 || m.vocab % 128) return bad("vocab % 128");
+  if (m.vocab < 128 || m.vocab % 128 || m.vocab > 131072) return bad("vocab: multiple of 128, <= 131072");
   if (m.canvas != 256) return bad("canvas must be 256");
   if (!(m.rms_eps > 0.f) || !(m.rope_theta >= 0.f)) return bad("rms_eps > 0, rope_theta >= 0");
   return "";

@@ -335,33 +335,58 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   }
 }
 
-__global__ __launch_bounds__(64) void head_merge_kernel(const float* __restrict__ part, int n_rows,
-                                                        int n_slices, int slice_w,
-                                                        const int32_t* __restrict__ cur_tok,
-                                                        int32_t* cand, float* t_cand, float* t_cur,
-                                                        float* lse, float* ent) {
-  const int row = blockIdx.x, lane = threadIdx.x;
+// One work-group (4 waves) per row: thread t merges slices t, t + 256, ... (two 16-byte loads
+// each, all issued first), then the wave and the 4 wave results merge in a fixed order.
+__global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict__ part, int n_rows,
+                                                         int n_slices, int slice_w,
+                                                         const int32_t* __restrict__ cur_tok,
+                                                         int32_t* cand, float* t_cand, float* t_cur,
+                                                         float* lse, float* ent) {
+  constexpr int PER = 8;  // slices per thread held in registers (n_slices <= 2048)
+  __shared__ float wm[4][8];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  floatx4_t p0[PER], p1[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int j = min(tid + 256 * k, n_slices - 1);  // clamped; merged only when in range
+    const float* p = part + (static_cast<long>(row) * n_slices + j) * 8;
+    p0[k] = *reinterpret_cast<const floatx4_t*>(p);
+    p1[k] = *reinterpret_cast<const floatx4_t*>(p + 4);
+  }
   Stat st;
   st.m = -INFINITY; st.s = 0.f; st.st = 0.f; st.bs = -INFINITY; st.bt = 0.f; st.tc = NAN;
   st.bi = 0x7fffffff;
-  for (int j = lane; j < n_slices; j += 64) {
-    const float* p = part + (static_cast<long>(row) * n_slices + j) * 8;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (tid + 256 * k >= n_slices) continue;
     Stat o;
-    o.m = p[0]; o.s = p[1]; o.st = p[2]; o.bs = p[3]; o.bi = __float_as_int(p[4]); o.bt = p[5];
-    o.tc = NAN;
+    o.m = p0[k][0]; o.s = p0[k][1]; o.st = p0[k][2]; o.bs = p0[k][3];
+    o.bi = __float_as_int(p1[k][0]); o.bt = p1[k][1]; o.tc = NAN;
     st = merge_stat(st, o);
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) st = merge_stat(st, shfl_stat(st, o));
   if (lane == 0) {
-    const float l = st.m + logf(st.s);
-    lse[row] = l;
-    ent[row] = l - st.st / st.s;
-    cand[row] = st.bi;
-    t_cand[row] = st.bt;
-    const int x = cur_tok[row];
-    t_cur[row] = part[(static_cast<long>(row) * n_slices + x / slice_w) * 8 + 6];
+    wm[w][0] = st.m; wm[w][1] = st.s; wm[w][2] = st.st; wm[w][3] = st.bs;
+    wm[w][4] = __int_as_float(st.bi); wm[w][5] = st.bt;
   }
+  __syncthreads();
+  if (tid != 0) return;
+  Stat r = st;
+#pragma unroll
+  for (int v = 1; v < 4; ++v) {
+    Stat o;
+    o.m = wm[v][0]; o.s = wm[v][1]; o.st = wm[v][2]; o.bs = wm[v][3];
+    o.bi = __float_as_int(wm[v][4]); o.bt = wm[v][5]; o.tc = NAN;
+    r = merge_stat(r, o);
+  }
+  const float l = r.m + logf(r.s);
+  lse[row] = l;
+  ent[row] = l - r.st / r.s;
+  cand[row] = r.bi;
+  t_cand[row] = r.bt;
+  const int x = cur_tok[row];
+  t_cur[row] = part[(static_cast<long>(row) * n_slices + x / slice_w) * 8 + 6];
 }
 
 template <int BF, int BT, int EPI>
@@ -460,7 +485,7 @@ void launch_head(const HeadArgs& a, hipStream_t s) {
 void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
                        const int32_t* cur_tok, int32_t* cand, float* t_cand, float* t_cur,
                        float* lse, float* ent, hipStream_t s) {
-  hipLaunchKernelGGL(head_merge_kernel, dim3(n_rows), dim3(64), 0, s, part, n_rows, n_slices,
+  hipLaunchKernelGGL(head_merge_kernel, dim3(n_rows), dim3(256), 0, s, part, n_rows, n_slices,
                      slice_w, cur_tok, cand, t_cand, t_cur, lse, ent);
 }
 

@@ -30,8 +30,8 @@ DG_DEVICE T block_sum(T v, T* red) {
 }
 
 __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
-  __shared__ float cc_s[256];
-  __shared__ int u_s[256];
+  __shared__ __align__(16) float cc_s[256];
+  __shared__ __align__(16) int u_s[256];
   __shared__ int ired[4];
   __shared__ float fred[4];
   const int b = blockIdx.x, i = threadIdx.x;
@@ -54,15 +54,29 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
   const float lse = slot ? a.lse[r] : 0.f;
   const float cc = slot ? a.t_cand[r] - lse : 0.f;
   const float cu = slot ? a.t_cur[r] - lse : 0.f;
+  const int cand = slot ? a.cand[r] : 0;
+  const float ent = slot ? a.ent[r] : 0.f;
+  const int stable_prev = a.stable_run[b];
   const bool U = slot && !com_prev;
   cc_s[i] = cc;
   u_s[i] = U ? 1 : 0;
   const int n_u = block_sum<int>(U ? 1 : 0, ired);  // contains the barrier publishing cc_s/u_s
   const int m = min(a.commit_m, n_u);
+  // 16-byte LDS reads, eight in flight: the scan is latency-bound, not compare-bound
   int rank = 0;
   if (U) {
-    for (int j = 0; j < C; ++j)
-      rank += (u_s[j] && (cc_s[j] > cc || (cc_s[j] == cc && j < i))) ? 1 : 0;
+    const floatx4_t* cc4 = reinterpret_cast<const floatx4_t*>(cc_s);
+    const u32x4_t* u4 = reinterpret_cast<const u32x4_t*>(u_s);
+#pragma unroll 8
+    for (int j4 = 0; j4 < C / 4; ++j4) {
+      const floatx4_t cv = cc4[j4];
+      const u32x4_t uv = u4[j4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = 4 * j4 + q;
+        rank += (uv[q] && (cv[q] > cc || (cv[q] == cc && j < i))) ? 1 : 0;
+      }
+    }
   }
   const bool sel = U && rank < m;
   const int pos = a.pos0[b] + i;
@@ -73,7 +87,6 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
   bool com = com_prev;
   int renoised = 0;
   if (slot) {
-    const int cand = a.cand[r];
     if (sel) {
       x = cand;
       com = true;
@@ -90,10 +103,10 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
   const int n_com = block_sum<int>((slot && com) ? 1 : 0, ired);
   const int n_ren = block_sum<int>(renoised, ired);
   const int nonfin = block_sum<int>((slot && !isfinite(lse)) ? 1 : 0, ired);
-  const float ent_sum = block_sum<float>(slot ? a.ent[r] : 0.f, fred);
+  const float ent_sum = block_sum<float>(ent, fred);
   if (i == 0) {
     const float mean_ent = ent_sum / static_cast<float>(C);
-    const int sr = changed ? 0 : a.stable_run[b] + 1;
+    const int sr = changed ? 0 : stable_prev + 1;
     int stop = (sr >= a.stable_steps) || (a.step >= a.max_steps - 1);
     if (a.entropy_stop >= 0.f && !changed && mean_ent < a.entropy_stop) stop = 1;
     a.stable_run[b] = sr;

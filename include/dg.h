@@ -55,7 +55,7 @@ enum {
 
 /* Model shape.  Supported: head_dim 64 or 128; d_model a multiple of 128 (<= 8192);
  * d_ff_expert a multiple of 128 (<= 1024); n_q_heads*head_dim and d_ff_shared multiples of 64; n_q_heads a multiple of n_kv_heads; 1 <= top_k <= n_experts
- * <= 64; vocab a multiple of 128; canvas == 256 ([GUIDE] "Arquitetura em Detalhes": fixed
+ * <= 64; vocab a multiple of 128, <= 131072; canvas == 256 ([GUIDE] "Arquitetura em Detalhes": fixed
  * 256-token blocks).  rope_theta 0 disables RoPE (rotate-half, absolute positions). */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;

@@ -45,7 +45,7 @@ def _desc(dg, **kw):
 @pytest.mark.parametrize("bad,code", [
     (dict(head_dim=96), -2), (dict(canvas=128), -2), (dict(n_kv_heads=3), -2),
     (dict(top_k=9), -2), (dict(n_experts=65, top_k=2), -2), (dict(vocab=1000), -2),
-    (dict(d_model=200), -2), (dict(rms_eps=0.0), -2),
+    (dict(d_model=200), -2), (dict(rms_eps=0.0), -2), (dict(vocab=131072 + 128), -2),
 ])
 def test_create_rejects_bad_shapes_before_any_device_work(bad, code):
     dg = pytest.importorskip("block_discrete_diffusion_amd.dg")
