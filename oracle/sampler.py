@@ -13,11 +13,17 @@ Readings (the pages leave these open; the configuration used for this path fixes
 * t = z / T_s per logit (float32).  The draw is Gumbel-max: y = argmax_v (t_v + g_v), lowest v on
   ties.  The confidence of a position is its tempered log-probability, log kappa = t - lse(t),
   of the drawn token (candidate) or of the current token (committed positions).
-* Commit: the min(m, |U|) uncommitted positions with the highest candidate confidence (lowest
-  index on ties) take their candidate and become committed.
+* Commit (select_mode 0): the min(m, |U|) uncommitted positions with the highest candidate
+  confidence (lowest index on ties) take their candidate and become committed.
+* Commit (select_mode 1, [DOCS] table, token-selection row): the uncommitted positions are
+  taken in ascending order of entropy (lowest index on ties) and added while the running
+  float32 sum of their entropies, added in that order, stays <= the budget (0.1); the first
+  one is always taken.  Those take their candidate and become committed.
 * Re-noise: a position committed before this step whose current-token confidence is below tau
-  gets a fresh uniform token and is uncommitted (flag); every other uncommitted position takes
-  its candidate when its confidence is >= tau and a fresh uniform token otherwise.
+  gets a fresh uniform token and is uncommitted (flag).  In select_mode 0 every other
+  uncommitted position takes its candidate when its confidence is >= tau and a fresh uniform
+  token otherwise; in select_mode 1 every unselected uncommitted position gets a fresh uniform
+  token (the token-selection row re-noises what it did not select).
 * Stop: stable_run counts consecutive steps that changed no token; stop once it reaches
   `stable_steps`, or at the last allowed step, or (optional, off by default) when the mean
   entropy is below `entropy_stop` and the step changed nothing.
@@ -26,7 +32,8 @@ Decisions (argmax, ranking, threshold) are taken in float32 like the kernels tak
 entropy are accumulated in float64 and rounded to float32.
 
 Parity: pinned by tests/test_oracle_sampler.py (closed-form schedule, peaked-logits fixture with
-an exact stop step, the fixed-commit schedule, Gumbel-max statistics, invariants, determinism).
+an exact stop step, the fixed-commit schedule, Gumbel-max statistics, invariants, determinism,
+hand-worked entropy-bounded selections and a brute-force check of the selection rule).
 """
 from __future__ import annotations
 
@@ -50,6 +57,26 @@ class SamplerConfig:
     entropy_stop: float = -1.0  # < 0: off
     renoise_committed: bool = True
     seed: int = 0
+    select_mode: int = 0  # 0: top commit_per_step by confidence; 1: entropy-bounded
+    entropy_budget: float = 0.1
+
+
+def entropy_bounded_count(h_sorted: np.ndarray, budget: float) -> int:
+    """How many of the entropies (already in selection order) are selected: the longest
+    prefix whose float32 running sum, added left to right, stays <= budget; at least one
+    when there is any ([DOCS] table, token-selection row)."""
+    n = h_sorted.shape[0]
+    if n == 0:
+        return 0
+    b = np.float32(budget)
+    run = np.float32(0.0)
+    k = 0
+    for j in range(n):
+        run = np.float32(run + np.float32(h_sorted[j]))
+        if j > 0 and run > b:
+            break
+        k = j + 1
+    return k
 
 
 def temperature(cfg: SamplerConfig, step: int) -> np.float32:
@@ -106,9 +133,15 @@ def sample_commit(stats: Dict[str, np.ndarray], tokens: np.ndarray, committed: n
     fresh = philox.token_draw(cfg.seed, b, positions, step, philox.RENOISE, vocab)
 
     U = np.nonzero(~com_prev)[0]
-    m = min(cfg.commit_per_step, U.size)
-    # rank U by confidence descending, index ascending
-    order = U[np.lexsort((U, -conf_cand[U].astype(np.float64)))]
+    if cfg.select_mode == 1:
+        # rank U by entropy ascending, index ascending
+        ent = stats["entropy"].astype(np.float32)
+        order = U[np.lexsort((U, ent[U].astype(np.float64)))]
+        m = entropy_bounded_count(ent[order], cfg.entropy_budget)
+    else:
+        # rank U by confidence descending, index ascending
+        order = U[np.lexsort((U, -conf_cand[U].astype(np.float64)))]
+        m = min(cfg.commit_per_step, U.size)
     S = order[:m]
     rest = order[m:]
     x[S] = stats["cand"][S]
@@ -120,8 +153,12 @@ def sample_commit(stats: Dict[str, np.ndarray], tokens: np.ndarray, committed: n
         x[drop] = fresh[drop]
         com[drop] = False
         n_renoised += drop.size
-    low = rest[conf_cand[rest] < log_tau]
-    keep = rest[~(conf_cand[rest] < log_tau)]
+    if cfg.select_mode == 1:
+        low = rest
+        keep = rest[:0]
+    else:
+        low = rest[conf_cand[rest] < log_tau]
+        keep = rest[~(conf_cand[rest] < log_tau)]
     x[low] = fresh[low]
     x[keep] = stats["cand"][keep]
     n_renoised += low.size

@@ -173,3 +173,95 @@ def test_canvas_init_is_uniform_and_positional():
     a = sampler.canvas_init(3, 0, np.arange(256), 1024)
     b = sampler.canvas_init(3, 0, np.arange(256, 512), 1024)
     assert a.min() >= 0 and a.max() < 1024 and (a != b).mean() > 0.9
+
+
+# ----- entropy-bounded selection ([DOCS] table, token-selection row) -----
+
+def _stats(ent, cand=None, V=64):
+    C = len(ent)
+    r = np.random.default_rng(11)
+    return {"cand": (r.integers(0, V, C) if cand is None else np.asarray(cand)).astype(np.int32),
+            "t_cand": np.zeros(C, np.float32), "t_cur": np.zeros(C, np.float32),
+            "lse": np.zeros(C, np.float32), "entropy": np.asarray(ent, np.float32),
+            "margin": np.ones(C, np.float32)}
+
+
+def _select(ent, com=None, budget=0.1, **kw):
+    C = len(ent)
+    st = _stats(ent)
+    com = np.zeros(C, bool) if com is None else np.asarray(com, bool)
+    x = np.arange(C, dtype=np.int32) % 64
+    c = cfg(select_mode=1, entropy_budget=budget, renoise_committed=False, **kw)
+    x1, c1, _, status = sampler.sample_commit(st, x, com, 0, c, 0, 0, np.arange(C), 64)
+    return st, x, x1, c1, status
+
+
+def test_entropy_selection_hand_worked():
+    # uncommitted 0..5 with H = .05 .02 .04 .5 .01(committed) .03: ascending over U is
+    # 1 (.02), 5 (.03), 2 (.04), 0 (.05) ...; running sums .02 .05 .09 .14 -> {1, 5, 2}
+    ent = [0.05, 0.02, 0.04, 0.5, 0.01, 0.03]
+    com = [0, 0, 0, 0, 1, 0]
+    st, x, x1, c1, status = _select(ent, com)
+    assert list(status["selected"]) == [1, 5, 2] and status["n_new"] == 3
+    assert list(c1) == [False, True, True, False, True, True]
+    assert all(x1[i] == st["cand"][i] for i in (1, 5, 2))
+    # every unselected uncommitted slot got the fresh uniform token of its position
+    fresh = philox.token_draw(1234, 0, np.arange(6), 0, philox.RENOISE, 64)
+    assert x1[0] == fresh[0] and x1[3] == fresh[3] and status["n_renoised"] == 2
+    assert x1[4] == x[4]  # committed and not re-noised (flag off)
+
+
+def test_entropy_selection_takes_at_least_one_and_lowest_index_on_ties():
+    st, x, x1, c1, status = _select([3.0, 2.5, 2.5, 7.0])
+    assert list(status["selected"]) == [1]
+    # equal entropies: lower index first; .03 * 3 = .09 <= .1 < .12
+    _, _, _, _, status = _select([0.03] * 8)
+    assert list(status["selected"]) == [0, 1, 2]
+    # the budget is inclusive: dyadic entropies summing to exactly the budget are all taken
+    _, _, _, _, status = _select([0.25, 0.125, 0.125, 0.5], budget=0.5)
+    assert list(status["selected"]) == [1, 2, 0]
+    # nothing uncommitted: nothing selected
+    _, _, x1, _, status = _select([0.0] * 4, com=[1] * 4)
+    assert status["n_new"] == 0 and len(status["selected"]) == 0
+
+
+def test_entropy_selection_matches_bruteforce_over_exact_sums():
+    """Position i is selected iff the exact sum of the entropies of every uncommitted position
+    ordered at or before it is within the budget, or it comes first.  Entropies are multiples
+    of 1/256 below 1, so every float32 partial sum is exact and both rules must agree."""
+    from fractions import Fraction
+    r = np.random.default_rng(12)
+    for trial in range(200):
+        C = int(r.integers(1, 24))
+        q = r.integers(0, 24, C)  # many ties
+        ent = q / 256.0
+        com = r.random(C) < 0.3
+        budget = float(r.integers(0, 40)) / 256.0
+        _, _, _, _, status = _select(ent, com, budget=budget)
+        U = [i for i in range(C) if not com[i]]
+        order = sorted(U, key=lambda i: (Fraction(int(q[i]), 256), i))
+        want = [i for k, i in enumerate(order)
+                if k == 0 or sum(Fraction(int(q[j]), 256) for j in order[:k + 1])
+                <= Fraction(int(round(budget * 256)), 256)]
+        assert list(status["selected"]) == want, (trial, ent, com, budget)
+
+
+def test_entropy_selection_run_peaked_and_random():
+    V = 1024
+    target = np.random.default_rng(7).integers(0, V, 256)
+    z = np.zeros((256, V))
+    z[np.arange(256), target] = 50.0
+    # near-zero entropy everywhere: all 256 are selected at step 0, the canvas is then still,
+    # so the entropy stop ends the run at step 1 and the stable-run rule at step 2
+    x, com, hist = _run(lambda s, x: z, cfg(select_mode=1, entropy_stop=0.005), V=V)
+    assert len(hist) == 2 and hist[0][4]["n_new"] == 256 and com.all()
+    assert np.array_equal(x, target)
+    _, _, hist = _run(lambda s, x: z, cfg(select_mode=1), V=V)
+    assert len(hist) == 3
+    # random logits: entropies are far above the budget, so exactly one commit per step and
+    # every other uncommitted slot is re-noised
+    zs = np.random.default_rng(8).standard_normal((6, 256, V))
+    _, com, hist = _run(lambda s, x: zs[s], cfg(select_mode=1, max_steps=6,
+                                                 renoise_committed=False), V=V)
+    assert [h[4]["n_committed"] for h in hist] == [1, 2, 3, 4, 5, 6]
+    assert [h[4]["n_renoised"] for h in hist] == [255, 254, 253, 252, 251, 250]
