@@ -570,6 +570,10 @@ int dg_sample_commit(dg_ctx* c, dg_canvas_state* st, const dg_row_stats* rs,
     return c->fail(DG_ERR_ARG, "sample_commit: step out of [0, max_steps)");
   if (cfg->commit_per_step < 0 || cfg->stable_steps < 1 || !(cfg->renoise_conf >= 0.f))
     return c->fail(DG_ERR_ARG, "sample_commit: bad sampler config");
+  if (cfg->select_mode != 0 && cfg->select_mode != 1)
+    return c->fail(DG_ERR_ARG, "sample_commit: select_mode must be 0 or 1");
+  if (cfg->select_mode == 1 && !(cfg->entropy_budget >= 0.f && cfg->entropy_budget < INFINITY))
+    return c->fail(DG_ERR_ARG, "sample_commit: entropy_budget must be finite and >= 0");
   SamplerArgs a{};
   a.tokens = st->tokens; a.committed = st->committed; a.stable_run = st->stable_run;
   a.stopped = st->stopped;
@@ -581,6 +585,7 @@ int dg_sample_commit(dg_ctx* c, dg_canvas_state* st, const dg_row_stats* rs,
                                       : -INFINITY;
   a.stable_steps = cfg->stable_steps; a.entropy_stop = cfg->entropy_stop;
   a.renoise_committed = cfg->renoise_committed;
+  a.select_mode = cfg->select_mode; a.entropy_budget = cfg->entropy_budget;
   a.k0 = static_cast<uint32_t>(cfg->seed); a.k1 = static_cast<uint32_t>(cfg->seed >> 32);
   for (int b = 0; b < kv->batch; ++b) a.pos0[b] = kv->len[b];
   timed(c, "sample_commit", s, [&] { launch_sample_commit(a, kv->batch, s); });

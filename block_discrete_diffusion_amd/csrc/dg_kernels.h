@@ -150,6 +150,8 @@ struct SamplerArgs {
   void* status;  // dg_step_status[B]
   int C; int V; int step; int max_steps; int commit_m; float log_tau; int stable_steps;
   float entropy_stop; int renoise_committed; uint32_t k0, k1;
+  int select_mode;       // 0: top commit_m by confidence; 1: entropy-bounded
+  float entropy_budget;  // select_mode 1: bound on the running entropy sum of the selection
   int32_t pos0[kMaxBatch];
 };
 void launch_sample_commit(const SamplerArgs& a, int n_req, hipStream_t s);

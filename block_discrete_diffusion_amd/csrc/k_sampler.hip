@@ -1,10 +1,12 @@
 // Confidence sampler step, uniform-state canvas start, and the block commit (KV append).
 //
-// One work-group per canvas, one thread per slot.  The commit set is the exact top-m of the
-// uncommitted slots by (log-confidence desc, slot asc): every thread counts the slots that beat
-// it (256 compares from LDS), so ties are resolved exactly like a stable sort.  Decisions are
-// taken in float32 on log-probabilities t - lse.  Re-noise tokens come from the Philox stream
-// RENOISE keyed by (seed; 0, position, step, request).
+// One work-group per canvas, one thread per slot.  Every uncommitted slot gets its rank under
+// (key desc, slot asc) by counting the slots that beat it (256 compares from LDS), so ties are
+// resolved exactly like a stable sort.  The key is the log-confidence t - lse for the top-m
+// rule, and minus the entropy for the entropy-bounded rule ([DOCS] table, token-selection row),
+// whose cut is found by one thread adding the entropies in rank order in float32, exactly the
+// order the definition gives.  Decisions are taken in float32.  Re-noise tokens come from the
+// Philox stream RENOISE keyed by (seed; 0, position, step, request).
 #include "dg_common.h"
 #include "dg_kernels.h"
 
@@ -32,6 +34,8 @@ DG_DEVICE T block_sum(T v, T* red) {
 __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
   __shared__ __align__(16) float cc_s[256];
   __shared__ __align__(16) int u_s[256];
+  __shared__ float h_sorted[256];
+  __shared__ int m_s;
   __shared__ int ired[4];
   __shared__ float fred[4];
   const int b = blockIdx.x, i = threadIdx.x;
@@ -58,10 +62,11 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
   const float ent = slot ? a.ent[r] : 0.f;
   const int stable_prev = a.stable_run[b];
   const bool U = slot && !com_prev;
-  cc_s[i] = cc;
+  const bool by_entropy = a.select_mode == 1;
+  const float key = by_entropy ? -ent : cc;
+  cc_s[i] = key;
   u_s[i] = U ? 1 : 0;
   const int n_u = block_sum<int>(U ? 1 : 0, ired);  // contains the barrier publishing cc_s/u_s
-  const int m = min(a.commit_m, n_u);
   // 16-byte LDS reads, eight in flight: the scan is latency-bound, not compare-bound
   int rank = 0;
   if (U) {
@@ -74,9 +79,27 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int j = 4 * j4 + q;
-        rank += (uv[q] && (cv[q] > cc || (cv[q] == cc && j < i))) ? 1 : 0;
+        rank += (uv[q] && (cv[q] > key || (cv[q] == key && j < i))) ? 1 : 0;
       }
     }
+  }
+  int m = min(a.commit_m, n_u);
+  if (by_entropy) {  // uniform branch
+    if (U) h_sorted[rank] = ent;
+    __syncthreads();
+    if (i == 0) {
+      // the longest prefix whose running float32 sum stays within the budget, at least one
+      float run = 0.f;
+      int k = 0;
+      for (int j = 0; j < n_u; ++j) {
+        run += h_sorted[j];
+        if (j > 0 && run > a.entropy_budget) break;
+        k = j + 1;
+      }
+      m_s = k;
+    }
+    __syncthreads();
+    m = m_s;
   }
   const bool sel = U && rank < m;
   const int pos = a.pos0[b] + i;
@@ -93,7 +116,7 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
     } else if (com_prev) {
       if (a.renoise_committed && cu < a.log_tau) { x = fresh; com = false; renoised = 1; }
     } else {
-      if (cc < a.log_tau) { x = fresh; renoised = 1; }
+      if (by_entropy || cc < a.log_tau) { x = fresh; renoised = 1; }
       else x = cand;
     }
     a.tokens[r] = x;

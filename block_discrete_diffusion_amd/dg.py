@@ -59,7 +59,8 @@ class RowStats(C.Structure):
 class SamplerCfg(C.Structure):
     _fields_ = [("max_steps", C.c_int32), ("temp_start", C.c_float), ("temp_end", C.c_float),
                 ("commit_per_step", C.c_int32), ("renoise_conf", C.c_float), ("stable_steps", C.c_int32),
-                ("entropy_stop", C.c_float), ("renoise_committed", C.c_int32), ("seed", C.c_uint64)]
+                ("entropy_stop", C.c_float), ("renoise_committed", C.c_int32), ("seed", C.c_uint64),
+                ("select_mode", C.c_int32), ("entropy_budget", C.c_float)]
 
 
 class Debug(C.Structure):
@@ -123,11 +124,16 @@ def to_device_bf16(x, device) -> torch.Tensor:
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device).contiguous()
 
 
+SELECT_TOP_M, SELECT_ENTROPY = 0, 1
+
+
 def sampler_cfg(max_steps=48, temp_start=0.8, temp_end=0.4, commit_per_step=16, renoise_conf=0.1,
-                stable_steps=2, entropy_stop=-1.0, renoise_committed=True, seed=0) -> SamplerCfg:
+                stable_steps=2, entropy_stop=-1.0, renoise_committed=True, seed=0,
+                select_mode=SELECT_TOP_M, entropy_budget=0.1) -> SamplerCfg:
     return SamplerCfg(int(max_steps), float(temp_start), float(temp_end), int(commit_per_step),
                       float(renoise_conf), int(stable_steps), float(entropy_stop),
-                      int(bool(renoise_committed)), int(seed) & ((1 << 64) - 1))
+                      int(bool(renoise_committed)), int(seed) & ((1 << 64) - 1), int(select_mode),
+                      float(entropy_budget))
 
 
 def temperature(cfg: SamplerCfg, step: int) -> float:

@@ -131,6 +131,12 @@ typedef struct {
   float entropy_stop;        /* < 0 off; else also stop when mean entropy < it and unchanged */
   int32_t renoise_committed; /* 1: committed positions whose confidence drops are re-noised */
   uint64_t seed;
+  int32_t select_mode;       /* which uncommitted positions are committed each step:
+                                0: the commit_per_step most confident ones;
+                                1: entropy-bounded ([DOCS] table, token-selection row): in
+                                   ascending order of entropy while the running float32 sum of
+                                   their entropies stays <= entropy_budget, at least one */
+  float entropy_budget;      /* 0.1 (select_mode 1) */
 } dg_sampler_cfg;
 
 /* Per-request result of dg_sample_commit (device [batch]). */

@@ -87,7 +87,9 @@ def oracle_cfg(cfg):
                                  temp_end=float(np.float32(cfg.temp_end)), commit_per_step=cfg.commit_per_step,
                                  renoise_conf=float(np.float32(cfg.renoise_conf)), stable_steps=cfg.stable_steps,
                                  entropy_stop=float(np.float32(cfg.entropy_stop)),
-                                 renoise_committed=bool(cfg.renoise_committed), seed=cfg.seed)
+                                 renoise_committed=bool(cfg.renoise_committed), seed=cfg.seed,
+                                 select_mode=cfg.select_mode,
+                                 entropy_budget=float(np.float32(cfg.entropy_budget)))
 
 
 def random_cache(shape, L: int, cap: int, seed: int, batch: int = 1):

@@ -86,3 +86,37 @@ def test_temperature_schedule_matches_oracle_bitexact():
         oc = sampler.SamplerConfig(max_steps=ms, temp_start=float(np.float32(t0)), temp_end=float(np.float32(t1)))
         for s in range(ms):
             assert np.float32(dg.temperature(cfg, s)) == sampler.temperature(oc, s)
+
+
+def test_binding_structs_match_the_header_layout(tmp_path):
+    """Every ctypes structure of the binding has the size and field offsets that a C compiler
+    gives the struct of the same role in include/dg.h."""
+    dg = pytest.importorskip("block_discrete_diffusion_amd.dg")
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    pairs = {"dg_model_desc": dg.ModelDesc, "dg_layer_weights": dg.LayerWeights,
+             "dg_weights": dg.Weights, "dg_kv_cache": dg.KVCache,
+             "dg_canvas_state": dg.CanvasState, "dg_row_stats": dg.RowStats,
+             "dg_sampler_cfg": dg.SamplerCfg, "dg_debug": dg.Debug,
+             "dg_step_params": dg.StepParams, "dg_kernel_time": dg.KernelTime}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "dg.h"', "int main(void) {"]
+    for cname, py in pairs.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for f in py._fields_:
+            lines.append(f'printf("{cname} {f[0]} %zu\\n", offsetof({cname}, {f[0]}));')
+    lines += ["return 0; }"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, field, val = ln.split()
+        got[(cname, field)] = int(val)
+    for cname, py in pairs.items():
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for f in py._fields_:
+            assert got[(cname, f[0])] == getattr(py, f[0]).offset, (cname, f[0])

@@ -78,12 +78,14 @@ def test_head_decisions_and_stats(env, step):
     close(stats.entropy.cpu().numpy()[0], want["entropy"], max_abs=1e-3, rel_l2=1e-4, what="entropy")
 
 
-def test_sampler_bitexact_over_steps(env):
-    """dg_sample_commit on identical float32 row statistics is bit-exact against the oracle."""
+@pytest.mark.parametrize("select_mode", [0, 1])
+def test_sampler_bitexact_over_steps(env, select_mode):
+    """dg_sample_commit on identical float32 row statistics is bit-exact against the oracle,
+    under both selection rules (top-m by confidence; entropy-bounded)."""
     dg, w, m = env
     kv, _, _ = _kv(dg, batch=2)
     kv.set_lengths([L, 3 * L])
-    cfg = dg.sampler_cfg(seed=4242, max_steps=12, commit_per_step=16)
+    cfg = dg.sampler_cfg(seed=4242, max_steps=12, commit_per_step=16, select_mode=select_mode)
     oc = oracle_cfg(cfg)
     st = dg.Canvas(2, 256)
     m.canvas_init(st, kv, cfg)
@@ -104,6 +106,12 @@ def test_sampler_bitexact_over_steps(env):
             "entropy": synth.uniform((2, 256), 0.0, 3.0, s, 5),
         }
         rs["t_cand"][:, ::7] = rs["t_cand"][:, 3:4]  # exact ties in the ranking
+        if select_mode == 1:
+            # a low-entropy third so that the budget admits several slots per step; values on a
+            # 1/4096 grid give exact ties and zeros
+            low = synth.uniform((2, 256), 0.0, 0.03, s, 6)
+            pick = synth.uniform((2, 256), 0.0, 1.0, s, 7) < 0.33
+            rs["entropy"] = np.where(pick, np.floor(low * 4096) / 4096, rs["entropy"]).astype(np.float32)
         for k, v in rs.items():
             getattr(stats, k).copy_(torch.from_numpy(np.ascontiguousarray(v)))
         m.sample_commit(st, stats, cfg, s, kv, status)
