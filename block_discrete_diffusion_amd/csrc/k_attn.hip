@@ -1,8 +1,9 @@
 // Canvas attention (bidirectional, no mask) and causal prefill attention on MFMA, plus the
 // RoPE/scatter step that turns the QKV projection into rotated bf16 Q and K/V rows.
 //
-// Each work-group serves one (request, KV head) and up to four (query head, 32-row) tasks of
-// that head's query group, so every K/V tile staged in LDS is reused by all of them (GQA).
+// Each work-group serves one (request, KV head) and four or eight (query head, 32-row) tasks of
+// that head's query group, one per wave, so every K/V tile staged in LDS is reused by all of
+// them (GQA).
 // Keys are the request's cached prefix followed by the canvas keys; the key range can be split
 // across work-groups (split-KV) so that a 256-row canvas still fills the chip; the splits are
 // merged in a fixed order afterwards (deterministic).
@@ -13,7 +14,9 @@
 // O^T += V^T P^T, if the 32 keys of one MFMA are taken as {4j..4j+3} of two 16-key sub-blocks
 // (the k order inside an MFMA only has to agree between A and B).  V stays [key][d] in LDS and
 // the A operand V^T[d][keys] is two transposing 8-byte LDS reads.  The online-softmax state
-// (max, sum) is per query = per lane, so rescaling O^T needs no cross-lane traffic.
+// (max, sum) is per query = per lane, so rescaling O^T needs no cross-lane traffic; the block
+// maximum is reduced across the four lanes of a query with permlane swaps, and the sum of P
+// comes from one more MFMA against an all-ones A operand.
 #include "dg_common.h"
 #include "dg_kernels.h"
 
@@ -110,6 +113,17 @@ DG_DEVICE u32x2_t read_tr16(const uint16_t* p) {
 // which is at least 1).
 DG_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions across the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48 hold the same
+// query).  The gfx950 permlane swaps exchange lane l with l^16 (rows of 16) or l^32 (halves):
+// called with the same value in both operands they return {v[l], v[l^16]} (resp. l^32) to
+// every lane, with no trip through the LDS crossbar.
+DG_DEVICE float group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // K and V blocks as they are in memory ([key][d]); rows padded so that the 16-byte K-fragment
 // reads (16 rows, 4 banks each) and the transposing 8-byte V reads (4 rows x 32 bytes per
 // 16 lanes) both hit distinct banks.
@@ -178,17 +192,119 @@ void attention_kernel(AttnArgs a) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  // running max (in log2 units, scale folded in) and sum per query
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // running max (in log2 units, scale folded in) per query; the running sum of P is one more
+  // MFMA per step with an all-ones A operand (every row of that tile is the column sum of P^T,
+  // i.e. this lane's query sum over the step's keys, of the same bf16 P that multiplies V)
+  float m_run[2] = {-INFINITY, -INFINITY};
+  floatx4_t l_acc[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
+  const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const float sl2 = a.scale * 1.4426950408889634f;
 
   const long kv_head = static_cast<long>(b) * a.Hkv + g;
   u32x4_t rk[KCH], rv[KCH];
 
+  // S^T of one 64-key block for both query tiles (raw dot products)
+  auto qk = [&](floatx4_t (&sc)[4][2]) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) sc[kt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const u32x4_t kf = ld16(&sm.k[kt * 16 + l16][ks * 32 + 8 * j4]);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) sc[kt][qt] = mfma16(kf, qf[qt][ks], sc[kt][qt]);
+      }
+    }
+  };
+  // online softmax per lane (= per query), in place: p = 2^(s*sl2 - m), one FMA + one exp each;
+  // returns whether some lane's running max moved (O^T and the sum then need rescaling)
+  auto softmax = [&](floatx4_t (&sc)[4][2], int kb0, int kb_hi, float (&alpha)[2]) {
+    // mask only blocks that cross the range end or the causal diagonal (uniform branch)
+    if ((kb0 + KB > kb_hi) || (a.causal && kb0 + KB - 1 > qmin)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = kb0 + kt * 16 + 4 * j4 + i;
+            if (kk >= kb_hi || (a.causal && kk > qpos[qt])) sc[kt][qt][i] = -INFINITY;
+          }
+    }
+    bool rescale = false;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        mx = fmaxf(fmaxf(mx, fmaxf(sc[kt][qt][0], sc[kt][qt][1])), fmaxf(sc[kt][qt][2], sc[kt][qt][3]));
+      mx = group_max(mx);
+      const float m_new = fmaxf(m_run[qt], mx * sl2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all keys masked so far
+      alpha[qt] = fast_exp2(m_run[qt] - m_use);                // 0 when m_run is -inf
+      rescale |= (alpha[qt] != 1.f);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[kt][qt][i] = fast_exp2(fmaf(sc[kt][qt][i], sl2, -m_use));
+      m_run[qt] = m_new;
+    }
+    return rescale;
+  };
+  // P as the bf16 B operand of the two 32-key MFMA steps: lane holds the 8 keys
+  // {4 j4 .. 4 j4 + 3} of two 16-key sub-blocks for its query
+  auto pack_p = [&](const floatx4_t (&sc)[4][2], u32x4_t (&pf)[2][2]) {
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const floatx4_t p0 = sc[2 * kk2][qt], p1 = sc[2 * kk2 + 1][qt];
+        pf[kk2][qt] = u32x4_t{pack_bf2(p0[0], p0[1]), pack_bf2(p0[2], p0[3]), pack_bf2(p1[0], p1[1]),
+                              pack_bf2(p1[2], p1[3])};
+      }
+  };
+  // O^T = alpha O^T + V^T P^T over two 32-key steps (and the sum of P alongside)
+  auto pv = [&](const u32x4_t (&pf)[2][2], bool rescale, const float (&alpha)[2]) {
+    // rescaling by alpha == 1 is exact, so it is skipped when no lane of the wave needs it
+    if (__any(rescale)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha[qt];
+        l_acc[qt] *= alpha[qt];
+      }
+    }
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        // A = V^T[d = 16 dt + l16][the 8 keys of P's lane group]: two transposing reads, each
+        // giving this lane 4 consecutive keys of its d column
+        const int kr = kk2 * 32 + 4 * j4 + (l16 >> 2), dc = dt * 16 + 4 * (l16 & 3);
+        const u32x2_t lo = read_tr16(&sm.v[kr][dc]);
+        const u32x2_t hi = read_tr16(&sm.v[kr + 16][dc]);
+        const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma16(vf, pf[kk2][qt], o[dt][qt]);
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) l_acc[qt] = mfma16(ones, pf[kk2][qt], l_acc[qt]);
+    }
+  };
+
   // Keys come in two ranges with one base pointer each (uniform, so addresses are a scalar
   // base plus a lane offset): the cached prefix [0, n_cache) and the canvas [n_cache, n_keys).
   // Keys past a range end re-read its last key (every load is unconditional, so wait counts
   // stay exact) and are masked to -inf.
+  //
+  // Keys come in two ranges with one base pointer each (uniform, so addresses are a scalar
+  // base plus a lane offset): the cached prefix [0, n_cache) and the canvas [n_cache, n_keys).
+  // Keys past a range end re-read its last key (every load is unconditional, so wait counts
+  // stay exact) and are masked to -inf.  The next block's global loads are in flight while
+  // the current one is computed from LDS.
   auto run_range = [&](const uint16_t* kbase, const uint16_t* vbase, int key0, int kb_lo, int kb_hi) {
     auto gload = [&](int kb0) {
 #pragma unroll
@@ -218,99 +334,22 @@ void attention_kernel(AttnArgs a) {
       gload(blk + 1 < n_blk ? kb0 + KB : kb0);  // unconditional: exact wait counts
       sched_fence();
       if (!active) continue;
-
-      // S^T for 4 key sub-blocks x 2 query tiles (raw dot products)
-      floatx4_t s[4][2];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const u32x4_t kf = ld16(&sm.k[kt * 16 + l16][ks * 32 + 8 * j4]);
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
-        }
-      }
-      // mask only blocks that cross the range end or the causal diagonal (uniform branch)
-      if ((kb0 + KB > kb_hi) || (a.causal && kb0 + KB - 1 > qmin)) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int kk = kb0 + kt * 16 + 4 * j4 + i;
-              if (kk >= kb_hi || (a.causal && kk > qpos[qt])) s[kt][qt][i] = -INFINITY;
-            }
-      }
-      // online softmax per lane (= per query): p = 2^(s*sl2 - m), one FMA + one exp each
-      bool rescale = false;
+      floatx4_t sc[4][2];
+      u32x4_t pf[2][2];
       float alpha[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          mx = fmaxf(fmaxf(mx, fmaxf(s[kt][qt][0], s[kt][qt][1])), fmaxf(s[kt][qt][2], s[kt][qt][3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[qt], mx * sl2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all keys masked so far
-        alpha[qt] = fast_exp2(m_run[qt] - m_use);                // 0 when m_run is -inf
-        rescale |= (alpha[qt] != 1.f);
-        float sum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(fmaf(s[kt][qt][i], sl2, -m_use));
-            s[kt][qt][i] = p;
-            sum += p;
-          }
-        sum += __shfl_xor(sum, 16, 64);
-        sum += __shfl_xor(sum, 32, 64);
-        l_run[qt] = l_run[qt] * alpha[qt] + sum;
-        m_run[qt] = m_new;
-      }
-      // rescaling O^T by alpha == 1 is exact, so it is skipped when no lane of the wave needs it
-      if (__any(rescale)) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) o[dt][qt] *= alpha[qt];
-      }
-      // O^T += V^T P^T over two 32-key steps
-#pragma unroll
-      for (int kk2 = 0; kk2 < 2; ++kk2) {
-        u32x4_t pf[2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          const floatx4_t p0 = s[2 * kk2][qt], p1 = s[2 * kk2 + 1][qt];
-          pf[qt] = u32x4_t{pack_bf2(p0[0], p0[1]), pack_bf2(p0[2], p0[3]), pack_bf2(p1[0], p1[1]),
-                           pack_bf2(p1[2], p1[3])};
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          // A = V^T[d = 16 dt + l16][the 8 keys of P's lane group]: two transposing reads, each
-          // giving this lane 4 consecutive keys of its d column
-          const int kr = kk2 * 32 + 4 * j4 + (l16 >> 2), dc = dt * 16 + 4 * (l16 & 3);
-          const u32x2_t lo = read_tr16(&sm.v[kr][dc]);
-          const u32x2_t hi = read_tr16(&sm.v[kr + 16][dc]);
-          const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma16(vf, pf[qt], o[dt][qt]);
-        }
-      }
+      qk(sc);
+      const bool rescale = softmax(sc, kb0, kb_hi, alpha);
+      pack_p(sc, pf);
+      pv(pf, rescale, alpha);
     }
   };
+
   run_range(a.kc + kv_head * a.cap * D, a.vc + kv_head * a.cap * D, 0, k_lo, min(k_hi, n_cache));
   if (a.n_extra > 0)
     run_range(a.kx + kv_head * a.xcap * D, a.vx + kv_head * a.xcap * D, n_cache, max(k_lo, n_cache), k_hi);
 
   if (!active) return;
+  const float l_run[2] = {l_acc[0][0], l_acc[1][0]};
   // write: lane owns query qt*16+l16, dims dt*16 + 4*j4 + i; partial maxima are in log2 units
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {

@@ -107,126 +107,158 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
   }
 }
 
-// Residual update + FFN norm + router + top-k, one work-group (8 waves) per row.
-//  - every load of the row (residual, its split-K slices) is issued before the reduction;
-//  - h += slices (z order, written back); x = h * rsqrt(mean h^2 + eps) * gain in float32;
+// Residual update + FFN norm + router + top-k, one work-group (8 waves) per R rows.
+//  - the router weights of the wave's experts (first round of columns) are requested before
+//    anything else, so their latency hides behind the norm;
+//  - per row, every load (residual, its split-K slices) is issued before the reduction;
+//    h += slices (z order, written back); x = h * rsqrt(mean h^2 + eps) * gain in float32;
 //    the bf16 copy of x feeds the experts and the float32 x is kept in LDS;
-//  - router logits in float32: wave w owns experts 8w .. 8w+7 and requests the weights of all
-//    eight rows at once (one memory round trip for d <= 2048); lane l owns the row elements
+//  - router logits in float32: wave w owns experts 8w .. 8w+7; lane l owns the row elements
 //    [8 (l + 64 j), +8) (coalesced 16-byte reads: a wave covers 1 KB of one expert row per
-//    request); the eight partials are summed over the wave by a transpose-reduce (three
-//    exchange steps halving the expert window, then three plain steps), after which lane l
-//    holds expert 8w + (l >> 3);
-//  - wave 0: lane e = expert e, k rounds of wave arg-max (ties to the lower expert index),
-//    softmax gates over the k picks.
+//    request), and every weight chunk is used for all R rows; the eight partials of a row are
+//    summed over the wave by a transpose-reduce (three exchange steps halving the expert
+//    window, then three plain steps), after which lane l holds expert 8w + (l >> 3);
+//  - wave rr picks row rr's experts: lane e = expert e, k rounds of wave arg-max (ties to the
+//    lower expert index), softmax gates over the k picks.
 constexpr int kRouterWaves = 8;
-template <int NCH>  // 4-element chunks per thread: ceil(d / 2048)
+template <int NCH, int R>  // NCH: 4-element chunks per thread, ceil(d / 2048); R rows (<= 8)
 __global__ __launch_bounds__(512) void norm_router_kernel(
     float* __restrict__ h, const float* __restrict__ part, int n_part, long part_stride,
     const float* __restrict__ gain, float eps, const uint16_t* __restrict__ wr, int d, int n_exp,
-    int top_k, uint16_t* __restrict__ bout, int32_t* __restrict__ idx, float* __restrict__ gates) {
-  __shared__ float red[kRouterWaves];
-  __shared__ float lg[64];
-  __shared__ float xs[NCH * 2048];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float* hr = h + static_cast<long>(r) * d;
-  floatx4_t v[NCH], pz[kMaxParts][NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = (tid + 512 * i) * 4;
-    const bool ok = c < d;
-    v[i] = ok ? *reinterpret_cast<const floatx4_t*>(hr + c) : floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int z = 0; z < kMaxParts; ++z)
-      if (z < n_part && ok) pz[z][i] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + static_cast<long>(r) * d + c);
-  }
-  if (n_part > 0) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = (tid + 512 * i) * 4;
-      if (c >= d) continue;  // no slices were loaded there: v stays zero
-#pragma unroll
-      for (int z = 0; z < kMaxParts; ++z)
-        if (z < n_part) v[i] += pz[z][i];
-      *reinterpret_cast<floatx4_t*>(hr + c) = v[i];
-    }
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ss += v[i][q] * v[i][q];
-  ss = wave_sum(ss);
-  if (lane == 0) red[w] = ss;
-  __syncthreads();
-  ss = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
-  const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = (tid + 512 * i) * 4;
-    if (c >= d) continue;
-    const floatx4_t g = *reinterpret_cast<const floatx4_t*>(gain + c);
-    floatx4_t x;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) x[q] = v[i][q] * inv * g[q];
-    *reinterpret_cast<u32x2_t*>(bout + static_cast<long>(r) * d + c) = u32x2_t{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])};
-    *reinterpret_cast<floatx4_t*>(&xs[c]) = x;
-  }
-  __syncthreads();
-
-  // router: 8 experts per wave, 4 row chunks of 512 elements per round of loads
-  float p[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) p[e] = 0.f;
+    int top_k, int rows, uint16_t* __restrict__ bout, int32_t* __restrict__ idx,
+    float* __restrict__ gates) {
+  __shared__ float red[R][kRouterWaves];
+  __shared__ float lg[R][64];
+  __shared__ float xs[R][NCH * 2048];
+  const int r0 = blockIdx.x * R, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nr = min(R, rows - r0);  // rows of this group (uniform)
   const int nj = (d + 511) / 512;
-  for (int j0 = 0; j0 < nj; j0 += 4) {
-    u32x4_t wv[4][8];
+
+  // chunks of 512 columns per round of weight loads (fewer when many rows hold accumulators)
+  constexpr int JR = (R >= 4 || R * NCH >= 8) ? 2 : 4;
+  u32x4_t wv[JR][8];
+  auto load_w = [&](int j0) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < JR; ++jj)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = min((lane + 64 * (j0 + jj)) * 8, d - 8);  // clamped: always in bounds
         const int ee = min(8 * w + e, n_exp - 1);
         wv[jj][e] = ld16(wr + static_cast<long>(ee) * d + c);
       }
+  };
+  load_w(0);
+
+  floatx4_t v[R][NCH];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+  for (int rr = 0; rr < R; ++rr) {
+    if (rr >= nr) break;
+    float* hr = h + static_cast<long>(r0 + rr) * d;
+    floatx4_t pz[kMaxParts][NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = (tid + 512 * i) * 4;
+      const bool ok = c < d;
+      v[rr][i] = ok ? *reinterpret_cast<const floatx4_t*>(hr + c) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int z = 0; z < kMaxParts; ++z)
+        if (z < n_part && ok)
+          pz[z][i] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + static_cast<long>(r0 + rr) * d + c);
+    }
+    if (n_part > 0) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = (tid + 512 * i) * 4;
+        if (c >= d) continue;  // no slices were loaded there: v stays zero
+#pragma unroll
+        for (int z = 0; z < kMaxParts; ++z)
+          if (z < n_part) v[rr][i] += pz[z][i];
+        *reinterpret_cast<floatx4_t*>(hr + c) = v[rr][i];
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ss += v[rr][i][q] * v[rr][i][q];
+    ss = wave_sum(ss);
+    if (lane == 0) red[rr][w] = ss;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    if (rr >= nr) break;
+    const float ss = ((red[rr][0] + red[rr][1]) + (red[rr][2] + red[rr][3])) +
+                     ((red[rr][4] + red[rr][5]) + (red[rr][6] + red[rr][7]));
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = (tid + 512 * i) * 4;
+      if (c >= d) continue;
+      const floatx4_t g = *reinterpret_cast<const floatx4_t*>(gain + c);
+      floatx4_t x;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = v[rr][i][q] * inv * g[q];
+      *reinterpret_cast<u32x2_t*>(bout + static_cast<long>(r0 + rr) * d + c) =
+          u32x2_t{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])};
+      *reinterpret_cast<floatx4_t*>(&xs[rr][c]) = x;
+    }
+  }
+  __syncthreads();
+
+  // router: 8 experts per wave, JR row chunks of 512 elements per round of loads
+  float p[R][8];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[rr][e] = 0.f;
+  for (int j0 = 0; j0 < nj; j0 += JR) {
+    if (j0 > 0) load_w(j0);
+#pragma unroll
+    for (int jj = 0; jj < JR; ++jj) {
       const int c = (lane + 64 * (j0 + jj)) * 8;
       if (c >= d) continue;
-      const floatx4_t x0 = *reinterpret_cast<const floatx4_t*>(&xs[c]);
-      const floatx4_t x1 = *reinterpret_cast<const floatx4_t*>(&xs[c + 4]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float acc = p[e];
+      for (int rr = 0; rr < R; ++rr) {
+        const floatx4_t x0 = *reinterpret_cast<const floatx4_t*>(&xs[rr][c]);
+        const floatx4_t x1 = *reinterpret_cast<const floatx4_t*>(&xs[rr][c + 4]);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          acc += __uint_as_float(wv[jj][e][q] << 16) * x0[2 * q];
-          acc += __uint_as_float(wv[jj][e][q] & 0xffff0000u) * x0[2 * q + 1];
-          acc += __uint_as_float(wv[jj][e][2 + q] << 16) * x1[2 * q];
-          acc += __uint_as_float(wv[jj][e][2 + q] & 0xffff0000u) * x1[2 * q + 1];
+        for (int e = 0; e < 8; ++e) {
+          float acc = p[rr][e];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            acc += __uint_as_float(wv[jj][e][q] << 16) * x0[2 * q];
+            acc += __uint_as_float(wv[jj][e][q] & 0xffff0000u) * x0[2 * q + 1];
+            acc += __uint_as_float(wv[jj][e][2 + q] << 16) * x1[2 * q];
+            acc += __uint_as_float(wv[jj][e][2 + q] & 0xffff0000u) * x1[2 * q + 1];
+          }
+          p[rr][e] = acc;
         }
-        p[e] = acc;
       }
     }
   }
   // transpose-reduce: halve the expert window over lane bits 5, 4, 3, then sum over bits 2..0
 #pragma unroll
-  for (int sft = 32, win = 4; sft >= 8; sft >>= 1, win >>= 1) {
-    const bool up = (lane & sft) != 0;
+  for (int rr = 0; rr < R; ++rr) {
 #pragma unroll
-    for (int j = 0; j < win; ++j) {
-      const float keep = up ? p[win + j] : p[j];
-      const float give = up ? p[j] : p[win + j];
-      p[j] = keep + __shfl_xor(give, sft, 64);
+    for (int sft = 32, win = 4; sft >= 8; sft >>= 1, win >>= 1) {
+      const bool up = (lane & sft) != 0;
+#pragma unroll
+      for (int j = 0; j < win; ++j) {
+        const float keep = up ? p[rr][win + j] : p[rr][j];
+        const float give = up ? p[rr][j] : p[rr][win + j];
+        p[rr][j] = keep + __shfl_xor(give, sft, 64);
+      }
     }
+    p[rr][0] += __shfl_xor(p[rr][0], 4, 64);
+    p[rr][0] += __shfl_xor(p[rr][0], 2, 64);
+    p[rr][0] += __shfl_xor(p[rr][0], 1, 64);
+    if ((lane & 7) == 0 && 8 * w + (lane >> 3) < 64) lg[rr][8 * w + (lane >> 3)] = p[rr][0];
   }
-  p[0] += __shfl_xor(p[0], 4, 64);
-  p[0] += __shfl_xor(p[0], 2, 64);
-  p[0] += __shfl_xor(p[0], 1, 64);
-  if ((lane & 7) == 0 && 8 * w + (lane >> 3) < 64) lg[8 * w + (lane >> 3)] = p[0];
   __syncthreads();
-  if (w != 0) return;
-  const float logit = (lane < n_exp) ? lg[lane] : -INFINITY;
+  if (w >= nr) return;
+  const long r = r0 + w;
+  const float logit = (lane < n_exp) ? lg[w][lane] : -INFINITY;
   float vv = logit, my_val = -INFINITY, first = -INFINITY;
   int my_idx = 0;
   for (int j = 0; j < top_k; ++j) {
@@ -245,8 +277,8 @@ __global__ __launch_bounds__(512) void norm_router_kernel(
   const float e = (lane < top_k) ? expf(my_val - first) : 0.f;
   const float zsum = wave_sum(e);
   if (lane < top_k) {
-    idx[static_cast<long>(r) * top_k + lane] = my_idx;
-    gates[static_cast<long>(r) * top_k + lane] = e / zsum;
+    idx[r * top_k + lane] = my_idx;
+    gates[r * top_k + lane] = e / zsum;
   }
 }
 
@@ -278,12 +310,23 @@ void launch_norm_router(float* h, const float* part, int n_part, long part_strid
                         int n_exp, int top_k, uint16_t* b_out, int32_t* idx, float* gates,
                         hipStream_t s) {
   const int nch = (d + 2047) / 2048;
-#define DG_NR(N)                                                                               \
-  hipLaunchKernelGGL(norm_router_kernel<N>, dim3(rows), dim3(512), 0, s, h, part, n_part,         \
-                     part_stride, gain, eps, w_router, d, n_exp, top_k, b_out, idx, gates)
-  if (nch <= 1) DG_NR(1);
-  else if (nch <= 2) DG_NR(2);
-  else DG_NR(4);
+  // several rows per work-group once there are enough rows to fill the chip: the router
+  // weights are then read once per group instead of once per row
+  const int R = rows >= 2048 ? 8 : rows >= 1024 ? 4 : rows >= 512 ? 2 : 1;
+#define DG_NR(N, RR)                                                                           \
+  hipLaunchKernelGGL((norm_router_kernel<N, RR>), dim3((rows + RR - 1) / RR), dim3(512), 0, s, h, \
+                     part, n_part, part_stride, gain, eps, w_router, d, n_exp, top_k, rows, b_out, \
+                     idx, gates)
+#define DG_NR_R(N)                \
+  if (R == 8) DG_NR(N, 8);        \
+  else if (R == 4) DG_NR(N, 4);   \
+  else if (R == 2) DG_NR(N, 2);   \
+  else DG_NR(N, 1)
+  // LDS holds R float32 rows: R * nch <= 8 (64 KB)
+  if (nch <= 1) { DG_NR_R(1); }
+  else if (nch <= 2) { if (R >= 4) DG_NR(2, 4); else if (R == 2) DG_NR(2, 2); else DG_NR(2, 1); }
+  else { if (R >= 2) DG_NR(4, 2); else DG_NR(4, 1); }
+#undef DG_NR_R
 #undef DG_NR
 }
 

@@ -195,15 +195,20 @@ def test_layer_narrower_than_a_work_group_with_split_projection():
         m.close()
 
 
-def test_long_causal_prefill():
-    """Causal prefill of 8300 tokens in chunks of 512: the later chunks attend to more than 8192
-    keys (the long-range attention variant, causal); the cache equals the oracle's prefill.
+_LONG_PREFILL = {}
+
+
+@pytest.mark.parametrize("chunk", [512, 2048])
+def test_long_causal_prefill(chunk):
+    """Causal prefill of 8300 tokens in chunks of 512 or 2048 rows: the later chunks attend to
+    more than 8192 keys (the long-range attention variant, causal), and 2048-row chunks take the
+    many-rows-per-group router and the large GEMM tiles; the cache equals the oracle's prefill.
     Every expert is active (top-k = E) so that no router near-tie can swap experts for a row
     and move the next layer's inputs: the comparison is end to end over both layers."""
     dg = need_gpu()
     shape = dataclasses.replace(SHAPE, n_experts=4, top_k=4)
     w = synth.model_weights(shape, SEED + 7)
-    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=512)
+    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=chunk)
     try:
         n = 8300
         toks = synth.tokens(n, shape.vocab, SEED, 500)
@@ -211,9 +216,12 @@ def test_long_causal_prefill():
         m.prefill(torch.from_numpy(toks).cuda(), [n], kv)
         torch.cuda.synchronize()
         assert kv.lengths == [n]
-        ck = [np.zeros((shape.n_kv_heads, n + 256, shape.head_dim)) for _ in range(shape.n_layers)]
-        cv = [np.zeros((shape.n_kv_heads, n + 256, shape.head_dim)) for _ in range(shape.n_layers)]
-        omodel.prefill(w, shape, toks, ck, cv, 0)
+        if not _LONG_PREFILL:
+            ck = [np.zeros((shape.n_kv_heads, n + 256, shape.head_dim)) for _ in range(shape.n_layers)]
+            cv = [np.zeros((shape.n_kv_heads, n + 256, shape.head_dim)) for _ in range(shape.n_layers)]
+            omodel.prefill(w, shape, toks, ck, cv, 0)
+            _LONG_PREFILL["kv"] = (ck, cv)
+        ck, cv = _LONG_PREFILL["kv"]
         for l in range(shape.n_layers):
             close(bf16_to_np(kv.k[l, 0, :, :n]), ck[l][:, :n], what=f"prefill K layer {l}", bf16_out=True)
             close(bf16_to_np(kv.v[l, 0, :, :n]), cv[l][:, :n], what=f"prefill V layer {l}", bf16_out=True)
