@@ -110,7 +110,9 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
   const uint16_t* wp =
       a.wp + ((static_cast<long>(e) * (a.N / (16 * GT)) + blockIdx.x) * S * GT + w * FPW) * NA * 512 + lane * 8;
 
-  for (int ps = 0; ps < n_e; ps += ROWS) {
+  // passes of ROWS rows: work-group z takes passes z, z + Z, ... (Z = gridDim.z), so an expert
+  // with more rows than one pass holds is covered by parallel work-groups, not a serial pass
+  for (int ps = blockIdx.z * ROWS; ps < n_e; ps += ROWS * static_cast<int>(gridDim.z)) {
     // this thread's staging pieces; rows past the expert's count repeat its last row and
     // pieces past the tile are loaded (clamped) but not stored
     const uint16_t* src[PPT];
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
         }
       }
     }
-    if (ps + ROWS < n_e) __syncthreads();  // the next pass restages xs (uniform condition)
+    if (ps + ROWS * static_cast<int>(gridDim.z) < n_e) __syncthreads();  // the next pass restages xs (uniform)
   }
 }
 
@@ -320,16 +322,19 @@ void launch_moe_permute(const int32_t* idx, int n_routes, int n_exp, int32_t* of
                      perm, inv);
 }
 
-// Row tiles per pass from the mean routed rows per expert (one pass for most experts).
+// Row tiles per pass from the mean routed rows per expert, sized so that the busiest expert
+// (about four standard deviations above a uniform mean) still fits one pass; a second
+// work-group per expert picks up any pass beyond the first (it exits at once when there is
+// none), so a skewed routing costs a parallel work-group instead of a serial pass.
 template <bool GATED, int FPW>
 void launch_stream(const MoeArgs& a, int mean_rows, hipStream_t s) {
-  const dim3 grid(a.N / (64 * FPW), a.n_exp);
+  const dim3 grid(a.N / (64 * FPW), a.n_exp, 2);
   if (mean_rows <= 24) hipLaunchKernelGGL((expert_stream_kernel<GATED, 3, 1, FPW>), grid, dim3(256), 0, s, a);
-  else if (mean_rows <= 48) hipLaunchKernelGGL((expert_stream_kernel<GATED, 4, 2, FPW>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((expert_stream_kernel<GATED, 8, 2, FPW>), grid, dim3(256), 0, s, a);
+  else if (mean_rows <= 36) hipLaunchKernelGGL((expert_stream_kernel<GATED, 4, 2, FPW>), grid, dim3(256), 0, s, a);
+  else if (mean_rows <= 84) hipLaunchKernelGGL((expert_stream_kernel<GATED, 8, 2, FPW>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((expert_stream_kernel<GATED, 10, 2, FPW>), grid, dim3(256), 0, s, a);
 }
 
-// gate/up: 64 features per work-group; down: 128 (a longer weight run per wave)
 void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s) { launch_stream<true, kGroupTiles1 / 4>(a, mean_rows, s); }
 void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s) { launch_stream<false, kGroupTiles2 / 4>(a, mean_rows, s); }
 
