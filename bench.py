@@ -49,8 +49,8 @@ def expert_gemm1_bytes(shape, routes: int, experts_touched: int) -> float:
 # only for the kernel source it was taken on: a changed source reports traffic null.
 PMC_TRAFFIC = {
     "kernel": "expert_stream_kernel<true, 3, 1, 1>", "source": "block_discrete_diffusion_amd/csrc/k_moe.hip",
-    "sha": "7f6371deefe36690",
-    "fetch_kib": 202303.0, "fetch_scale": 1048576.0 / 524307.7,  # copy of 1 GiB reads 524308 KiB
+    "sha": "fbd916b0706ec844",
+    "fetch_kib": 202296.0, "fetch_scale": 1048576.0 / 524309.2,  # copy of 1 GiB reads 524309 KiB
     "write_kib": 1536.0, "write_scale": 1048576.0 / 1048576.0,   # and writes 1048576 KiB
 }
 
