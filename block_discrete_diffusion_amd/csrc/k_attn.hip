@@ -380,26 +380,38 @@ void attention_kernel(AttnArgs a) {
 }
 
 // Merge split partials in split order: O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
+// Every (max, sum) pair and every partial row of a thread is requested before any arithmetic.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            uint16_t* __restrict__ out, int n_rh,
                                                            int n_split) {
   constexpr int TPR = D / 4;  // threads per (row, head): 4 dims each
+  constexpr int MS = 16;      // most splits a launch uses
   const int rh = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (rh >= n_rh) return;
   const int d0 = (threadIdx.x % TPR) * 4;
+  const long base = static_cast<long>(rh) * n_split;
+  float2 ml[MS];
+  floatx4_t po[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s)
+    if (s < n_split) {
+      ml[s] = *reinterpret_cast<const float2*>(part_ml + (base + s) * 2);
+      po[s] = *reinterpret_cast<const floatx4_t*>(part_o + (base + s) * D + d0);
+    }
   float m = -INFINITY;
-  for (int s = 0; s < n_split; ++s) m = fmaxf(m, part_ml[(static_cast<long>(rh) * n_split + s) * 2]);
+#pragma unroll
+  for (int s = 0; s < MS; ++s)
+    if (s < n_split) m = fmaxf(m, ml[s].x);
   floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const long slot = static_cast<long>(rh) * n_split + s;
-    const float ms = part_ml[slot * 2];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - m);
-    l += w * part_ml[slot * 2 + 1];
-    acc += w * *reinterpret_cast<const floatx4_t*>(part_o + slot * D + d0);
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    if (s >= n_split || ml[s].x == -INFINITY) continue;
+    const float w = exp2f(ml[s].x - m);
+    l += w * ml[s].y;
+    acc += w * po[s];
   }
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
   *reinterpret_cast<u32x2_t*>(out + static_cast<long>(rh) * D + d0) =
