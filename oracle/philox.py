@@ -8,7 +8,7 @@ Both implementations below are written from that definition and share no code; t
 them against each other and against the published known-answer vectors.
 
 How the method uses it (the pages only say the canvas starts from random tokens and that
-low-confidence positions get random tokens; the counter layout is this build's reading):
+low-confidence positions get random tokens; the counter layout below is a reading of them):
 
 * key     = (seed & 0xffffffff, seed >> 32)
 * counter = (c0, p, s, (b << 8) | stream) with p the absolute sequence position, s the denoise
