@@ -79,6 +79,9 @@ struct dg_ctx {
   uint16_t* cv = nullptr;
   std::vector<uint16_t*> pk1;  // per layer: packed gate/up expert weights
   std::vector<uint16_t*> pk2;  // per layer: packed down expert weights
+  // E4M3 experts (desc.expert_fp8): packed bytes and per-channel scales [E][N] per matrix
+  std::vector<uint8_t*> pk1_8, pk2_8;
+  std::vector<float*> sc_gate, sc_up, sc_down;
 
   int fail(int code, const std::string& msg) {
     err = msg;
@@ -154,6 +157,7 @@ std::string validate_desc(const dg_model_desc& m) {
   if (m.vocab < 128 || m.vocab % 128 || m.vocab > 131072) return bad("vocab: multiple of 128, <= 131072");
   if (m.canvas != 256) return bad("canvas must be 256");
   if (!(m.rms_eps > 0.f) || !(m.rope_theta >= 0.f)) return bad("rms_eps > 0, rope_theta >= 0");
+  if (m.expert_fp8 != 0 && m.expert_fp8 != 1) return bad("expert_fp8 must be 0 or 1");
   return "";
 }
 
@@ -268,11 +272,13 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   MoeArgs g1{};
   g1.x = c->a; g1.ldx = d; g1.perm = c->perm; g1.top_k = m.top_k; g1.offs = c->offs;
   g1.wp = c->pk1[l]; g1.K = d; g1.N = m.d_ff_expert;
+  if (m.expert_fp8) { g1.wp8 = c->pk1_8[l]; g1.wscale0 = c->sc_gate[l]; g1.wscale1 = c->sc_up[l]; }
   g1.out_bf16 = c->act; g1.ldo = m.d_ff_expert; g1.n_exp = m.n_experts;
   timed(c, "moe_gemm1_swiglu", s, [&] { launch_moe_gemm1(g1, routes / m.n_experts, s); });
   MoeArgs g2{};
   g2.x = c->act; g2.ldx = m.d_ff_expert; g2.perm = c->perm; g2.top_k = m.top_k; g2.offs = c->offs;
   g2.wp = c->pk2[l]; g2.K = m.d_ff_expert; g2.N = d; g2.out_f32 = c->y; g2.ldo = d;
+  if (m.expert_fp8) { g2.wp8 = c->pk2_8[l]; g2.wscale0 = c->sc_down[l]; }
   g2.n_exp = m.n_experts;
   timed(c, "moe_gemm2", s, [&] { launch_moe_gemm2(g2, routes / m.n_experts, s); });
 
@@ -379,14 +385,43 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
             c->alloc(&c->rope, R * m.head_dim);
   // expert banks, repacked once into the MFMA fragment order the expert GEMMs stream
   const long ew = static_cast<long>(m.n_experts) * m.d_ff_expert * m.d_model;
+  const int E = m.n_experts, F = m.d_ff_expert;
   c->pk1.assign(m.n_layers, nullptr);
   c->pk2.assign(m.n_layers, nullptr);
-  for (int l = 0; ok && l < m.n_layers; ++l) {
-    ok = c->alloc(&c->pk1[l], 2 * ew) && c->alloc(&c->pk2[l], ew);
-    if (!ok) break;
-    const dg_layer_weights& lw = c->layers[l];
-    launch_moe_pack(lw.w_gate, lw.w_up, c->pk1[l], m.n_experts, m.d_ff_expert, m.d_model, kGroupTiles1, nullptr);
-    launch_moe_pack(lw.w_down, nullptr, c->pk2[l], m.n_experts, m.d_model, m.d_ff_expert, kGroupTiles2, nullptr);
+  if (m.expert_fp8) {
+    // quantize each matrix row-wise into scratch bytes, then lay the bytes out for streaming
+    c->pk1_8.assign(m.n_layers, nullptr);
+    c->pk2_8.assign(m.n_layers, nullptr);
+    c->sc_gate.assign(m.n_layers, nullptr);
+    c->sc_up.assign(m.n_layers, nullptr);
+    c->sc_down.assign(m.n_layers, nullptr);
+    uint8_t *qg = nullptr, *qu = nullptr, *qd = nullptr;
+    ok = ok && hipMalloc(&qg, ew) == hipSuccess && hipMalloc(&qu, ew) == hipSuccess &&
+         hipMalloc(&qd, ew) == hipSuccess;
+    for (int l = 0; ok && l < m.n_layers; ++l) {
+      ok = c->alloc(&c->pk1_8[l], 2 * ew) && c->alloc(&c->pk2_8[l], ew) &&
+           c->alloc(&c->sc_gate[l], static_cast<long>(E) * F) && c->alloc(&c->sc_up[l], static_cast<long>(E) * F) &&
+           c->alloc(&c->sc_down[l], static_cast<long>(E) * d);
+      if (!ok) break;
+      const dg_layer_weights& lw = c->layers[l];
+      launch_quantize_e4m3(lw.w_gate, static_cast<long>(E) * F, static_cast<int>(d), qg, c->sc_gate[l], nullptr);
+      launch_quantize_e4m3(lw.w_up, static_cast<long>(E) * F, static_cast<int>(d), qu, c->sc_up[l], nullptr);
+      launch_quantize_e4m3(lw.w_down, static_cast<long>(E) * d, F, qd, c->sc_down[l], nullptr);
+      launch_moe_pack_fp8(qg, qu, c->pk1_8[l], E, F, static_cast<int>(d), kGroupTiles1, nullptr);
+      launch_moe_pack_fp8(qd, nullptr, c->pk2_8[l], E, static_cast<int>(d), F, kGroupTiles2, nullptr);
+      ok = hipDeviceSynchronize() == hipSuccess;  // the scratch bytes are reused by the next layer
+    }
+    if (qg) (void)hipFree(qg);
+    if (qu) (void)hipFree(qu);
+    if (qd) (void)hipFree(qd);
+  } else {
+    for (int l = 0; ok && l < m.n_layers; ++l) {
+      ok = c->alloc(&c->pk1[l], 2 * ew) && c->alloc(&c->pk2[l], ew);
+      if (!ok) break;
+      const dg_layer_weights& lw = c->layers[l];
+      launch_moe_pack(lw.w_gate, lw.w_up, c->pk1[l], E, F, m.d_model, kGroupTiles1, nullptr);
+      launch_moe_pack(lw.w_down, nullptr, c->pk2[l], E, m.d_model, F, kGroupTiles2, nullptr);
+    }
   }
   if (ok) ok = hipDeviceSynchronize() == hipSuccess && hipGetLastError() == hipSuccess;
   if (!ok) {
@@ -411,6 +446,19 @@ float dg_temperature(const dg_sampler_cfg* cfg, int32_t step) {
                    (static_cast<double>(cfg->temp_end) - static_cast<double>(cfg->temp_start)) *
                        step / (cfg->max_steps - 1);
   return static_cast<float>(t);
+}
+
+int dg_quantize_e4m3_rows(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, float* scale,
+                          hipStream_t s) {
+  if (!w || !q || !scale) { g_create_error = "dg_quantize_e4m3_rows: null pointer"; return DG_ERR_ARG; }
+  if (rows < 0 || rows > (int64_t(1) << 31) - 1 || cols < 1 || cols > 65536) {
+    g_create_error = "dg_quantize_e4m3_rows: rows in [0, 2^31), cols in [1, 65536]";
+    return DG_ERR_ARG;
+  }
+  launch_quantize_e4m3(w, static_cast<long>(rows), cols, q, scale, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) { g_create_error = hipGetErrorString(e); return DG_ERR_HIP; }
+  return DG_OK;
 }
 
 int dg_prefill_causal(dg_ctx* c, const int32_t* tokens, const int32_t* n_new, int32_t batch,

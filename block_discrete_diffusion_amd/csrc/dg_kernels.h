@@ -123,6 +123,8 @@ struct MoeArgs {
   int K; int N;                     // reduction length and output features per expert
   uint16_t* out_bf16; float* out_f32; int ldo;
   int n_exp;
+  // E4M3 experts (instead of wp): packed bytes and per-channel scales [E][N] of matrix q
+  const uint8_t* wp8; const float* wscale0; const float* wscale1;
 };
 // Packed expert weights: for expert e, 16-row tile ft and 32-wide k-step s, the MFMA A-operand
 // fragment of every matrix q (GEMM1: q = gate, up; GEMM2: q = down) is 64 lanes x 16 B, lane l
@@ -133,6 +135,13 @@ constexpr int kGroupTiles1 = 4;  // gate/up: 64 features per work-group
 constexpr int kGroupTiles2 = 8;  // down: 128 features per work-group
 void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int n_exp, int N,
                      int K, int group_tiles, hipStream_t s);
+// E4M3 experts: per-row quantization (bf16 [rows][cols] -> bytes + float32 scale per row), and
+// the byte layout [e][ft / G][s2][ft % G][q][lane][16 B] whose 16 bytes per lane are the A
+// fragments of k-steps 2 s2 and 2 s2 + 1 (8 bytes each; K a multiple of 64)
+void launch_quantize_e4m3(const uint16_t* w, long rows, int cols, uint8_t* q, float* scale,
+                          hipStream_t s);
+void launch_moe_pack_fp8(const uint8_t* q0, const uint8_t* q1, uint8_t* out, int n_exp, int N,
+                         int K, int group_tiles, hipStream_t s);
 // mean_rows: routed rows per expert on average (selects the token-tile depth per pass)
 void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s);
 void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s);

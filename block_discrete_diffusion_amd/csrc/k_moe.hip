@@ -93,10 +93,11 @@ __global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __rest
 // issue the loads of chunk c+2; barrier.  Loads are unconditional (clamped chunk and row
 // indices) and the loop body is the same on every trip, so the compiler's wait counts leave
 // the younger chunks in flight.
-template <bool GATED, int TT, int KS, int FPW>
+template <bool GATED, int TT, int KS, int FPW, bool F8>
 __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
   constexpr int NA = GATED ? 2 : 1;
   constexpr int GT = 4 * FPW;  // tiles per work-group = tiles per packed group
+  static_assert(!F8 || KS == 2, "E4M3 fragments come in pairs of k-steps");
   constexpr int KC = 32 * KS, ROWS = TT * 16, LDX = KC + 8, CPR = KC / 8;
   constexpr int PIECES = ROWS * CPR, PPT = (PIECES + 255) / 256;
   __shared__ uint16_t xs[2][ROWS * LDX];
@@ -107,8 +108,9 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
   if (n_e == 0) return;  // uniform over the work-group
   const int ft0 = blockIdx.x * GT + w * FPW;
   const int S = a.K / 32, nch = S / KS;
-  const uint16_t* wp =
-      a.wp + ((static_cast<long>(e) * (a.N / (16 * GT)) + blockIdx.x) * S * GT + w * FPW) * NA * 512 + lane * 8;
+  const long wgrp = static_cast<long>(e) * (a.N / (16 * GT)) + blockIdx.x;  // packed tile group
+  const uint16_t* wp = F8 ? nullptr : a.wp + (wgrp * S * GT + w * FPW) * NA * 512 + lane * 8;
+  const uint8_t* wp8 = F8 ? a.wp8 + ((wgrp * (S / 2) * GT + w * FPW) * NA * 64 + lane) * 16 : nullptr;
 
   // passes of ROWS rows: work-group z takes passes z, z + Z, ... (Z = gridDim.z), so an expert
   // with more rows than one pass holds is covered by parallel work-groups, not a serial pass
@@ -135,15 +137,32 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
       for (int q = 0; q < NA; ++q)
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[f][q][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    u32x4_t fw[2][KS][FPW][NA], xr[PPT];
+    // bf16: one 16-byte fragment per (k-step, tile, matrix); E4M3: one 16-byte load holds the
+    // fragments of both k-steps of the chunk, widened to bf16 (exactly) right before the MFMA
+    constexpr int WS = F8 ? 1 : KS;
+    u32x4_t fw[2][WS][FPW][NA], xr[PPT];
     auto load_w = [&](int b, int c) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < WS; ++ks)
 #pragma unroll
         for (int f = 0; f < FPW; ++f)
 #pragma unroll
-          for (int q = 0; q < NA; ++q)
-            fw[b][ks][f][q] = ld16_nt(wp + (((c * KS + ks) * GT + f) * NA + q) * 512);
+          for (int q = 0; q < NA; ++q) {
+            if constexpr (F8) fw[b][ks][f][q] = ld16_nt(wp8 + ((c * GT + f) * NA + q) * 1024);
+            else fw[b][ks][f][q] = ld16_nt(wp + (((c * KS + ks) * GT + f) * NA + q) * 512);
+          }
+    };
+    auto frag = [&](int b, int ks, int f, int q) -> u32x4_t {
+      if constexpr (F8) {
+        const u32x4_t v = fw[b][0][f][q];
+        const uint32_t lo = v[2 * ks], hi = v[2 * ks + 1];
+        return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+      } else {
+        return fw[b][ks][f][q];
+      }
     };
     auto load_x = [&](int c) {
 #pragma unroll
@@ -163,7 +182,7 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
 #pragma unroll
           for (int f = 0; f < FPW; ++f)
 #pragma unroll
-            for (int q = 0; q < NA; ++q) acc[f][q][t] = mfma16(fw[b][ks][f][q], xf, acc[f][q][t]);
+            for (int q = 0; q < NA; ++q) acc[f][q][t] = mfma16(frag(b, ks, f, q), xf, acc[f][q][t]);
         }
     };
     load_x(0);
@@ -190,6 +209,18 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
       __syncthreads();
     }
     if (c < nch) compute(0, 0);  // odd chunk count: the last chunk sits in buffer / set 0
+    // E4M3: the per-channel scale multiplies the finished sums (scale * sum q x)
+    if constexpr (F8) {
+#pragma unroll
+      for (int f = 0; f < FPW; ++f)
+#pragma unroll
+        for (int q = 0; q < NA; ++q) {
+          const float* sp = (q == 0 ? a.wscale0 : a.wscale1) + static_cast<long>(e) * a.N + (ft0 + f) * 16 + 4 * j4;
+          const floatx4_t sc = *reinterpret_cast<const floatx4_t*>(sp);
+#pragma unroll
+          for (int t = 0; t < TT; ++t) acc[f][q][t] *= sc;
+        }
+    }
     // lane holds out[16 ft + 4 j4 + i][row col l16] of each tile
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
@@ -237,6 +268,75 @@ __global__ __launch_bounds__(256) void moe_pack_kernel(const uint16_t* __restric
   const uint16_t* src = (q == 0 ? w0 : w1) + ((e * N + ft * 16 + (lane & 15)) * static_cast<long>(K)) +
                         st * 32 + 8 * (lane >> 4);
   st16(out + c * 8, ld16(src));
+}
+
+// E4M3 byte layout: one thread per 16-byte piece [e][fg][k-step pair s2][tile w][matrix q][lane],
+// bytes 0-7 = W_q[e][16 ft + l % 16][64 s2 + 8 (l / 16) .. + 8], bytes 8-15 the same 32 columns
+// further (k-step 2 s2 + 1); tile ft = gt fg + w.
+__global__ __launch_bounds__(256) void moe_pack_fp8_kernel(const uint8_t* __restrict__ q0,
+                                                           const uint8_t* __restrict__ q1,
+                                                           uint8_t* __restrict__ out, int n_exp,
+                                                           int N, int K, int na, int gt) {
+  const int S2 = K / 64, G = N / (16 * gt);
+  const long total = static_cast<long>(n_exp) * G * S2 * gt * na * 64;
+  const long c = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (c >= total) return;
+  const int lane = static_cast<int>(c % 64);
+  long r = c / 64;
+  const int q = static_cast<int>(r % na);
+  r /= na;
+  const int w = static_cast<int>(r % gt);
+  r /= gt;
+  const int s2 = static_cast<int>(r % S2);
+  r /= S2;
+  const int fg = static_cast<int>(r % G);
+  const long e = r / G;
+  const int ft = gt * fg + w;
+  const uint8_t* src = (q == 0 ? q0 : q1) + (e * N + ft * 16 + (lane & 15)) * static_cast<long>(K) +
+                       s2 * 64 + 8 * (lane >> 4);
+  const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
+  const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 32);
+  *reinterpret_cast<u32x4_t*>(out + c * 16) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// OCP E4M3 encoding of a finite float32: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, no
+// infinities, largest finite 448; rounds to nearest with ties to even and saturates at 448.
+DG_DEVICE uint32_t e4m3_encode(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float ax = fabsf(x);
+  if (ax >= 448.0f) return sign | 0x7Eu;
+  if (ax < 0x1p-6f)  // subnormal grid 2^-9; 8 steps round up to the smallest normal, code 0x08
+    return sign | static_cast<uint32_t>(__builtin_rintf(ax * 512.0f));
+  const uint32_t ab = bits & 0x7FFFFFFFu;
+  int ex = static_cast<int>(ab >> 23) - 127;  // -6 .. 8
+  uint32_t m = (ab >> 20) & 7u;
+  const uint32_t rest = ab & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;
+  if (m == 8u) {
+    m = 0;
+    ++ex;
+  }
+  return sign | (static_cast<uint32_t>(ex + 7) << 3) | m;
+}
+
+// One work-group per row: scale = amax / 448 (1 for an all-zero row), q = E4M3(w / scale).
+__global__ __launch_bounds__(256) void quantize_e4m3_kernel(const uint16_t* __restrict__ w, int cols,
+                                                            uint8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+  __shared__ float red[4];
+  const long r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint16_t* wr = w + r * cols;
+  float amax = 0.f;
+  for (int c = tid; c < cols; c += 256) amax = fmaxf(amax, fabsf(bf2f(wr[c])));
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  if (tid == 0) scale[r] = sc;
+  for (int c = tid; c < cols; c += 256) q[r * cols + c] = static_cast<uint8_t>(e4m3_encode(bf2f(wr[c]) / sc));
 }
 
 // Un-permute + residual, one work-group (8 waves) per row t:
@@ -326,17 +426,38 @@ void launch_moe_permute(const int32_t* idx, int n_routes, int n_exp, int32_t* of
 // (about four standard deviations above a uniform mean) still fits one pass; a second
 // work-group per expert picks up any pass beyond the first (it exits at once when there is
 // none), so a skewed routing costs a parallel work-group instead of a serial pass.
+template <bool GATED, int FPW, bool F8>
+void launch_stream_t(const MoeArgs& a, int mean_rows, hipStream_t s) {
+  const dim3 grid(a.N / (64 * FPW), a.n_exp, 2);
+  constexpr int KS1 = F8 ? 2 : 1;  // E4M3 fragments come in pairs of k-steps
+  if (mean_rows <= 24) hipLaunchKernelGGL((expert_stream_kernel<GATED, 3, KS1, FPW, F8>), grid, dim3(256), 0, s, a);
+  else if (mean_rows <= 36) hipLaunchKernelGGL((expert_stream_kernel<GATED, 4, 2, FPW, F8>), grid, dim3(256), 0, s, a);
+  else if (mean_rows <= 84) hipLaunchKernelGGL((expert_stream_kernel<GATED, 8, 2, FPW, F8>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((expert_stream_kernel<GATED, 10, 2, FPW, F8>), grid, dim3(256), 0, s, a);
+}
+
 template <bool GATED, int FPW>
 void launch_stream(const MoeArgs& a, int mean_rows, hipStream_t s) {
-  const dim3 grid(a.N / (64 * FPW), a.n_exp, 2);
-  if (mean_rows <= 24) hipLaunchKernelGGL((expert_stream_kernel<GATED, 3, 1, FPW>), grid, dim3(256), 0, s, a);
-  else if (mean_rows <= 36) hipLaunchKernelGGL((expert_stream_kernel<GATED, 4, 2, FPW>), grid, dim3(256), 0, s, a);
-  else if (mean_rows <= 84) hipLaunchKernelGGL((expert_stream_kernel<GATED, 8, 2, FPW>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((expert_stream_kernel<GATED, 10, 2, FPW>), grid, dim3(256), 0, s, a);
+  if (a.wp8) launch_stream_t<GATED, FPW, true>(a, mean_rows, s);
+  else launch_stream_t<GATED, FPW, false>(a, mean_rows, s);
 }
 
 void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s) { launch_stream<true, kGroupTiles1 / 4>(a, mean_rows, s); }
 void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s) { launch_stream<false, kGroupTiles2 / 4>(a, mean_rows, s); }
+
+void launch_quantize_e4m3(const uint16_t* w, long rows, int cols, uint8_t* q, float* scale,
+                          hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(quantize_e4m3_kernel, dim3(rows), dim3(256), 0, s, w, cols, q, scale);
+}
+
+void launch_moe_pack_fp8(const uint8_t* q0, const uint8_t* q1, uint8_t* out, int n_exp, int N,
+                         int K, int group_tiles, hipStream_t s) {
+  const int na = q1 ? 2 : 1;
+  const long total = static_cast<long>(n_exp) * (N / 16) * (K / 64) * na * 64;
+  hipLaunchKernelGGL(moe_pack_fp8_kernel, dim3((total + 255) / 256), dim3(256), 0, s, q0, q1, out,
+                     n_exp, N, K, na, group_tiles);
+}
 
 void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int n_exp, int N, int K,
                      int group_tiles, hipStream_t s) {

@@ -32,7 +32,8 @@ vp = C.c_void_p
 class ModelDesc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim",
                                          "n_experts", "top_k", "d_ff_expert", "d_ff_shared", "vocab",
-                                         "canvas")] + [("rms_eps", C.c_float), ("rope_theta", C.c_float)]
+                                         "canvas")] + [("rms_eps", C.c_float), ("rope_theta", C.c_float),
+                                                       ("expert_fp8", C.c_int32)]
 
 
 class LayerWeights(C.Structure):
@@ -96,8 +97,9 @@ _lib.dg_commit_block.argtypes = [vp, vp, C.POINTER(KVCache), C.c_int32, vp]
 _lib.dg_debug_set_canvas_kv.argtypes = [vp, vp, vp, C.c_int32, vp]
 _lib.dg_timing_enable.argtypes = [vp, C.c_int32]
 _lib.dg_timing_read.argtypes = [vp, C.POINTER(KernelTime), C.c_int32]
+_lib.dg_quantize_e4m3_rows.argtypes = [vp, C.c_int64, C.c_int32, vp, vp, vp]
 for _n in ("dg_timing_enable", "dg_timing_read", "dg_prefill_causal", "dg_canvas_init", "dg_denoise_step", "dg_sample_commit",
-           "dg_commit_block", "dg_debug_set_canvas_kv"):
+           "dg_commit_block", "dg_debug_set_canvas_kv", "dg_quantize_e4m3_rows"):
     getattr(_lib, _n).restype = C.c_int
 
 
@@ -138,6 +140,20 @@ def sampler_cfg(max_steps=48, temp_start=0.8, temp_end=0.4, commit_per_step=16, 
 
 def temperature(cfg: SamplerCfg, step: int) -> float:
     return float(_lib.dg_temperature(C.byref(cfg), int(step)))
+
+
+def quantize_e4m3_rows(w: torch.Tensor, q: torch.Tensor, scale: torch.Tensor) -> None:
+    """dg_quantize_e4m3_rows on device tensors: w bf16 [rows, cols], q uint8 [rows, cols],
+    scale float32 [rows] (all contiguous, on the GPU)."""
+    if w.dtype != torch.bfloat16 or q.dtype != torch.uint8 or scale.dtype != torch.float32:
+        raise TypeError("quantize_e4m3_rows: w bf16, q uint8, scale float32")
+    if w.dim() != 2 or tuple(q.shape) != tuple(w.shape) or tuple(scale.shape) != (w.shape[0],):
+        raise ValueError("quantize_e4m3_rows: shapes w [rows, cols], q [rows, cols], scale [rows]")
+    if not (w.is_contiguous() and q.is_contiguous() and scale.is_contiguous()):
+        raise ValueError("quantize_e4m3_rows: contiguous tensors only")
+    rc = _lib.dg_quantize_e4m3_rows(_ptr(w), int(w.shape[0]), int(w.shape[1]), _ptr(q), _ptr(scale), _stream())
+    if rc != DG_OK:
+        raise DGError(rc, _lib.dg_last_error(None).decode())
 
 
 class KV:
@@ -221,7 +237,8 @@ class Model:
         self.w = Weights(_ptr(self.t["embed"]), _ptr(self.t["final_norm"]), _ptr(self.t["lm_head"]), arr)
         self.desc = ModelDesc(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                               shape.n_experts, shape.top_k, shape.d_ff_expert, shape.d_ff_shared, shape.vocab,
-                              shape.canvas, float(shape.rms_eps), float(shape.rope_theta))
+                              shape.canvas, float(shape.rms_eps), float(shape.rope_theta),
+                              int(bool(shape.expert_fp8)))
         h = C.c_void_p()
         rc = _lib.dg_create(C.byref(self.desc), C.byref(self.w), int(max_batch), int(max_prefill_rows),
                             C.byref(h))

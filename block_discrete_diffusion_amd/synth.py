@@ -50,6 +50,7 @@ class ModelShape:
     canvas: int = 256
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0
+    expert_fp8: bool = False  # routed experts quantized to OCP E4M3 (per-channel scales)
 
 
 # The shapes of the workloads this path is measured and checked on.

@@ -61,6 +61,11 @@ typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
   int32_t n_experts, top_k, d_ff_expert, d_ff_shared /* 0 = no shared FFN */, vocab, canvas;
   float rms_eps, rope_theta;
+  int32_t expert_fp8; /* 0: routed experts stream as bf16.  1: dg_create quantizes every routed
+                         expert matrix to OCP E4M3 with one float32 scale per output channel
+                         (dg_quantize_e4m3_rows) and the expert GEMMs stream those bytes
+                         ([NEWS] third and fourth paragraphs: FP8 checkpoints, FP8 serving);
+                         attention, router, shared FFN and head stay bf16. */
 } dg_model_desc;
 
 /* One decoder layer (pre-norm attention block, then routed MoE FFN + optional shared FFN).
@@ -175,18 +180,30 @@ typedef struct {
 
 /* Create a context for `desc` over caller-owned device weights.  The expert banks (w_gate,
  * w_up, w_down) are copied once into the context's own memory in the layout the expert GEMMs
- * stream (MFMA operand fragments, contiguous per group of four 16-row tiles); they are read only during
+ * stream (MFMA operand fragments, contiguous per group of 16-row tiles; as E4M3 bytes plus
+ * per-channel scales when desc->expert_fp8 is set); they are read only during
  * dg_create.  Every other weight pointer must stay valid for the context's lifetime.  max_batch: largest batch
  * (<= 64) of later calls; max_prefill_rows: largest prefill chunk processed at once (rows are
  * split into chunks of this size).  Returns DG_OK and *out, or an error code. */
 int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_batch,
               int32_t max_prefill_rows, dg_ctx** out);
 void dg_destroy(dg_ctx* ctx);
-/* Message of the last failure on ctx (or of the last dg_create failure when ctx is NULL). */
+/* Message of the last failure on ctx (or, when ctx is NULL, of the last failed dg_create or
+ * dg_quantize_e4m3_rows). */
 const char* dg_last_error(const dg_ctx* ctx);
 /* The temperature of step `step`: T0 + (T1 - T0) * step / (max_steps - 1), rounded to float32
  * once ([DOCS] table, temperature row). */
 float dg_temperature(const dg_sampler_cfg* cfg, int32_t step);
+
+/* Per-row OCP E4M3 quantization, the rule dg_create applies to the experts when
+ * desc->expert_fp8 is set ([NEWS] third paragraph: FP8 checkpoints).  w: device bf16
+ * [rows][cols]; q: device uint8 [rows][cols]; scale: device float32 [rows].  Per row:
+ * scale = amax / 448 in float32 (amax the largest |w|; 1 for an all-zero row), and
+ * q = E4M3(float32(w) / scale) with the division in float32, rounding to nearest with ties to
+ * even and saturating at +-448.  rows >= 0, 1 <= cols <= 65536.  Asynchronous on `stream`;
+ * DG_ERR_ARG for null pointers or bad sizes (nothing enqueued). */
+int dg_quantize_e4m3_rows(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q,
+                          float* scale, hipStream_t stream);
 
 /* Causal prefill ([GUIDE] "Arquitetura em Detalhes"; [NEWS] 2nd ¶; [DOCS] autoregressive
  * encoder): request b's n_new[b] tokens (packed back to back in `tokens`, device int32) are

@@ -37,7 +37,8 @@ def _desc(dg, **kw):
     s = synth.TINY
     base = dict(n_layers=s.n_layers, d_model=s.d_model, n_q_heads=s.n_q_heads, n_kv_heads=s.n_kv_heads,
                 head_dim=s.head_dim, n_experts=s.n_experts, top_k=s.top_k, d_ff_expert=s.d_ff_expert,
-                d_ff_shared=s.d_ff_shared, vocab=s.vocab, canvas=256, rms_eps=1e-6, rope_theta=1e4)
+                d_ff_shared=s.d_ff_shared, vocab=s.vocab, canvas=256, rms_eps=1e-6, rope_theta=1e4,
+                expert_fp8=0)
     base.update(kw)
     return dg.ModelDesc(*[base[n] for n, _ in dg.ModelDesc._fields_])
 

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 from block_discrete_diffusion_amd import synth
+from oracle import fp8 as ofp8
 from oracle import model as omodel
 from oracle import sampler as osampler
 from tests.gpu_common import (MARGIN, ROUTER_BOUND, bf16_to_np, check_layer, close, layer_debug,
@@ -142,6 +143,51 @@ def test_single_layer_parity(env):
         check_layer(dg, m1, w1, shape, L, SEED, L + 256)
         check_layer(dg, m1, w1, shape, 0, SEED + 1, 256)       # no prefix: pure canvas attention
         check_layer(dg, m1, w1, shape, 1000, SEED + 2, 1300)   # ragged prefix, several key tiles
+    finally:
+        m1.close()
+
+
+@pytest.mark.parametrize("cols", [2048, 768, 1000, 1])
+def test_quantize_e4m3_rows_bitexact(cols):
+    """dg_quantize_e4m3_rows gives the oracle's bytes and scales exactly: rows over six orders
+    of magnitude (so that small weights fall in the subnormal codes), an all-zero row, a row
+    with a single non-zero entry."""
+    dg = need_gpu()
+    rows = 64
+    r = np.random.default_rng(cols)
+    w = r.standard_normal((rows, cols)) * np.logspace(-4, 2, rows)[:, None]
+    w[5] = 0.0
+    w[6] = 0.0
+    w[6, cols // 2] = -3.0
+    w[7] *= np.where(r.random(cols) < 0.5, 1e-4, 1.0)  # wide range inside one row
+    wd = np_bf16_dev(w.reshape(rows, cols))
+    wq = bf16_to_np(wd)
+    q = torch.zeros((rows, cols), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros(rows, dtype=torch.float32, device="cuda")
+    dg.quantize_e4m3_rows(wd, q, sc)
+    torch.cuda.synchronize()
+    want_q, want_s = ofp8.quantize_rows(wq)
+    assert np.array_equal(sc.cpu().numpy(), want_s)
+    got = q.cpu().numpy()
+    bad = np.argwhere(got != want_q)
+    assert bad.size == 0, (bad[:5], got[tuple(bad[0])] if bad.size else None)
+    assert np.any(((want_q & 0x78) == 0) & ((want_q & 7) != 0)) or cols == 1  # subnormal codes were exercised
+
+
+def test_fp8_expert_layer_parity(env):
+    """Routed experts as E4M3 bytes with per-channel scales, quantized by dg_create: one layer
+    against the oracle layer whose experts are the oracle's own E4M3 round trip of the same
+    weights (attention, router and norms as in bf16)."""
+    dg, w, _ = env
+    shape = dataclasses.replace(SHAPE, n_layers=1, expert_fp8=True)
+    w1 = dict(w)
+    w1["layers"] = w["layers"][:1]
+    m1 = dg.Model(shape, w1, max_batch=1)
+    try:
+        wo = dict(w1)
+        wo["layers"] = [ofp8.dequantize_experts({k: np.asarray(v) for k, v in w1["layers"][0].items()})]
+        check_layer(dg, m1, wo, shape, L, SEED + 11, L + 256)
+        check_layer(dg, m1, wo, shape, 300, SEED + 12, 600)
     finally:
         m1.close()
 

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 from block_discrete_diffusion_amd import synth
+from oracle import fp8 as ofp8
 from oracle import model as omodel
 from oracle import sampler as osampler
 from tests.gpu_common import (MARGIN, bf16_to_np, check_layer, check_layers_teacher_forced, close,
@@ -52,6 +53,20 @@ def test_full_shape_layer_without_shared_ffn(full_env):
     try:
         hl = {"layers": [{k: v for k, v in host["layers"][0].items() if not k.startswith("ws_")}]}
         check_layer(dg, m, hl, shape, 4096, SEED + 1, 4096 + 256)
+    finally:
+        m.close()
+
+
+def test_full_shape_layer_fp8_experts(full_env):
+    """The full layer shape with the routed experts as E4M3 bytes (per-channel scales) and the
+    shared FFN in bf16, prefix 2048, against the oracle layer whose experts are its own E4M3
+    round trip of the same weights."""
+    dg, w, _, host = full_env
+    shape = dataclasses.replace(FULL1, expert_fp8=True)
+    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=256)
+    try:
+        hl = {"layers": [ofp8.dequantize_experts(host["layers"][0])]}
+        check_layer(dg, m, hl, shape, 2048, SEED + 77, 2048 + 256)
     finally:
         m.close()
 
