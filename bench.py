@@ -16,6 +16,7 @@ timed on a bounded sample of the same step.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -36,8 +37,12 @@ def log(msg: str):
 
 def expert_gemm1_bytes(shape, routes: int, experts_touched: int) -> float:
     """Algorithmic HBM bytes of one gate/up expert GEMM launch: each touched expert's gate and up
-    matrices once, each routed row's activations once, the SwiGLU output once."""
-    w = experts_touched * 2 * shape.d_ff_expert * shape.d_model * 2
+    matrices once (bf16, or E4M3 bytes plus one float32 scale per output channel), each routed
+    row's activations once, the SwiGLU output once."""
+    if getattr(shape, "expert_fp8", False):
+        w = experts_touched * 2 * shape.d_ff_expert * (shape.d_model * 1 + 4)
+    else:
+        w = experts_touched * 2 * shape.d_ff_expert * shape.d_model * 2
     x = routes * shape.d_model * 2
     out = routes * shape.d_ff_expert * 2
     return float(w + x + out)
@@ -141,6 +146,8 @@ WORKLOADS = {
                          "causally, 8 canvases of 256 denoised together (2048 rows per step)",
     "long_generation": "same model, prefix 8192, 8 consecutive canvases each denoised until the sampler "
                        "stops and then committed to the KV cache (final length 10240)",
+    "full_canvas_loop_fp8": "the full canvas loop with the routed experts quantized to OCP E4M3 "
+                            "(per-channel float32 scales); everything else bf16",
 }
 
 
@@ -177,6 +184,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     shape = synth.FULL
+    if args.workload == "full_canvas_loop_fp8":
+        shape = dataclasses.replace(shape, expert_fp8=True)
     log("drawing weights on the device")
     w = synth.torch_model_weights(shape, "cuda", SEED)
     cfg = dg.sampler_cfg(seed=SEED)
@@ -247,7 +256,7 @@ def main():
         ach = nbytes / (g1["avg_ms"] * 1e-3) / 1e9
         gemm1 = {"bound": "hbm", "kernel": "moe_gemm1_swiglu", "achieved": round(ach, 1),
                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                 "traffic": measured_traffic() if B == 1 else None,
+                 "traffic": measured_traffic() if args.workload == "full_canvas_loop" else None,
                  "avg_launch_us": round(g1["avg_ms"] * 1e3, 2), "algorithmic_bytes_per_launch": nbytes}
         at = kt["attention"]
         fl = attention_flops(shape, lens)
@@ -256,7 +265,7 @@ def main():
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                 "traffic": None, "avg_launch_us": round(at["avg_ms"] * 1e3, 2),
                 "algorithmic_flops_per_launch": fl}
-        roofline = gemm1 if args.workload == "full_canvas_loop" else attn
+        roofline = gemm1 if args.workload.startswith("full_canvas_loop") else attn
         extra["attention_roofline"] = attn
         extra["expert_gemm1_roofline"] = gemm1
     cpu = None
@@ -267,7 +276,8 @@ def main():
         "metric": "canvas positions/s (denoise step, 1 GPU)", "value": round(value, 1),
         "unit": "canvas positions/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded device RNG weights, uniform random tokens)",
+        "dtype": "bf16, routed experts e4m3" if shape.expert_fp8 else "bf16",
+        "data": "synthetic (seeded device RNG weights, uniform random tokens)",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}",
                    "global_batch": B, "seq_len": max(lens) + shape.canvas, "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernel_us_per_step": kernels,
