@@ -645,11 +645,17 @@ int dg_commit_block(dg_ctx* c, const int32_t* canvas, dg_kv_cache* kv, int32_t r
   if (!c) return DG_ERR_ARG;
   int rc = check_kv(c, kv);
   if (rc) return rc;
+  if (refresh < DG_COMMIT_LAST || refresh > DG_COMMIT_CAUSAL)
+    return c->fail(DG_ERR_ARG, "commit_block: refresh must be 0, 1 or 2");
   if (refresh && !canvas) return c->fail(DG_ERR_ARG, "commit_block: refresh needs the canvas");
   const dg_model_desc& m = c->m;
   for (int b = 0; b < kv->batch; ++b)
     if (static_cast<long>(kv->len[b]) + m.canvas > kv->cap)
       return c->fail(DG_ERR_CAPACITY, "commit_block: len + canvas > cap");
+  if (refresh == DG_COMMIT_CAUSAL) {  // the canvases are back to back, as prefill packs them
+    std::vector<int32_t> n_new(kv->batch, m.canvas);
+    return dg_prefill_causal(c, canvas, n_new.data(), kv->batch, kv, s);
+  }
   if (refresh) {
     dg_step_params p{};
     p.flags = DG_STEP_NO_HEAD;

@@ -127,6 +127,7 @@ def to_device_bf16(x, device) -> torch.Tensor:
 
 
 SELECT_TOP_M, SELECT_ENTROPY = 0, 1
+COMMIT_LAST, COMMIT_REFRESH, COMMIT_CAUSAL = 0, 1, 2
 
 
 def sampler_cfg(max_steps=48, temp_start=0.8, temp_end=0.4, commit_per_step=16, renoise_conf=0.1,
@@ -286,8 +287,9 @@ class Model:
         self._check(_lib.dg_sample_commit(self.ctx, C.byref(state.c), C.byref(stats.c), C.byref(cfg),
                                           int(step), C.byref(kv.c), _ptr(status), _stream()))
 
-    def commit_block(self, canvas: torch.Tensor, kv: KV, refresh: bool):
-        self._check(_lib.dg_commit_block(self.ctx, _ptr(canvas), C.byref(kv.c), int(bool(refresh)), _stream()))
+    def commit_block(self, canvas: torch.Tensor, kv: KV, refresh):
+        """refresh: COMMIT_LAST (0 / False), COMMIT_REFRESH (1 / True) or COMMIT_CAUSAL (2)."""
+        self._check(_lib.dg_commit_block(self.ctx, _ptr(canvas), C.byref(kv.c), int(refresh), _stream()))
 
     def timing(self, enable: bool):
         self._check(_lib.dg_timing_enable(self.ctx, int(bool(enable))))

@@ -241,10 +241,15 @@ int dg_sample_commit(dg_ctx* ctx, dg_canvas_state* state, const dg_row_stats* st
                      dg_step_status* status, hipStream_t stream);
 
 /* Append each finished canvas's K/V to the cache at [len[b], len[b]+canvas) and advance len
- * ([GUIDE] "Arquitetura em Detalhes"; [NEWS] 2nd ¶).  The K/V are the ones the last
- * dg_denoise_step computed; refresh != 0 first re-runs the layers (no head) on `canvas`
- * ([batch][canvas] device int32), needed when the last sampler step changed the canvas.  The
- * copy is bit-exact; nothing outside the appended slices is written. */
+ * ([GUIDE] "Arquitetura em Detalhes"; [NEWS] 2nd ¶).  refresh selects where the K/V come from:
+ *   DG_COMMIT_LAST (0): the ones the last dg_denoise_step computed (bidirectional canvas);
+ *   DG_COMMIT_REFRESH (1): first re-run the layers (no head) on `canvas` ([batch][canvas]
+ *     device int32), needed when the last sampler step changed the canvas;
+ *   DG_COMMIT_CAUSAL (2): re-encode `canvas` causally, as a continuation of the prompt (each
+ *     slot attends to the cache and to earlier slots; [DOCS] feature list, autoregressive
+ *     encoder): exactly dg_prefill_causal of the canvas tokens.
+ * The copy is bit-exact; nothing outside the appended slices is written. */
+enum { DG_COMMIT_LAST = 0, DG_COMMIT_REFRESH = 1, DG_COMMIT_CAUSAL = 2 };
 int dg_commit_block(dg_ctx* ctx, const int32_t* canvas, dg_kv_cache* kv, int32_t refresh,
                     hipStream_t stream);
 

@@ -224,6 +224,15 @@ def prefill(weights: Dict, shape, tokens: Sequence[int], cache_k: List[np.ndarra
     return h
 
 
+def commit_block_causal(weights: Dict, shape, canvas_tokens: Sequence[int], cache_k: List[np.ndarray],
+                        cache_v: List[np.ndarray], prefix_len: int) -> int:
+    """The other way to commit a finished canvas: re-encode its tokens causally as a continuation
+    of the prompt ([DOCS] feature list: the model also runs as an autoregressive encoder), i.e.
+    the causal prefill of the canvas at positions L..L+C-1.  Returns the new length."""
+    prefill(weights, shape, canvas_tokens, cache_k, cache_v, prefix_len)
+    return prefix_len + len(canvas_tokens)
+
+
 def commit_block(cache_k: List[np.ndarray], cache_v: List[np.ndarray],
                  canvas_k: List[np.ndarray], canvas_v: List[np.ndarray], prefix_len: int) -> int:
     """Append a finished canvas's K/V (rounded to the cache's bf16) at [L, L+C); return new L.

@@ -77,6 +77,8 @@ def test_null_context_is_rejected():
     assert dg._lib.dg_sample_commit(None, None, None, None, 0, None, None, None) == -1
     assert dg._lib.dg_commit_block(None, None, None, 0, None) == -1
     assert dg._lib.dg_prefill_causal(None, None, None, 0, None, None) == -1
+    assert dg._lib.dg_quantize_e4m3_rows(None, 4, 16, None, None, None) == -1
+    assert b"null pointer" in dg._lib.dg_last_error(None)
 
 
 def test_temperature_schedule_matches_oracle_bitexact():

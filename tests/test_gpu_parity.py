@@ -296,6 +296,34 @@ def test_commit_after_denoise_appends_the_step_kv(env):
         close(bf16_to_np(kv.k[l, 0, :, L:L + 256]), fw["canvas_k"][l], what=f"appended K layer {l}", bf16_out=True)
 
 
+def test_causal_commit_reencodes_the_canvas(env):
+    """DG_COMMIT_CAUSAL appends the causal prefill K/V of the canvas tokens: bit-identical to
+    dg_prefill_causal of the same tokens (whose parity with the oracle the prefill tests check
+    layer by layer), different from the bidirectional K/V of the same canvas, and for the first
+    layer within the parity bar of the oracle's causal commit.  Deeper layers are not compared
+    end to end here: over 256 rows a router near-tie in layer 0 moves a row's layer-1 input by
+    O(1), and causal attention carries it to the later rows."""
+    dg, w, m = env
+    x = torch.from_numpy(synth.tokens(256, SHAPE.vocab, SEED, 73)).cuda()
+    kv, k, v = _kv(dg, cap=L + 256)
+    m.denoise_step(x, kv, dg.sampler_cfg(), 0, dg.Stats(1, 256))
+    m.commit_block(x, kv, dg.COMMIT_CAUSAL)
+    kv2, _, _ = _kv(dg, cap=L + 256)
+    m.prefill(x, [256], kv2)
+    kv3, _, _ = _kv(dg, cap=L + 256)
+    m.denoise_step(x, kv3, dg.sampler_cfg(), 0, dg.Stats(1, 256))
+    m.commit_block(x, kv3, dg.COMMIT_LAST)
+    torch.cuda.synchronize()
+    assert kv.lengths == [L + 256] and kv2.lengths == [L + 256]
+    assert torch.equal(kv.k, kv2.k) and torch.equal(kv.v, kv2.v)
+    assert not torch.equal(kv.k[:, :, :, L:L + 256], kv3.k[:, :, :, L:L + 256])
+    ck = [k[l, 0].astype(np.float64).copy() for l in range(2)]
+    cv = [v[l, 0].astype(np.float64).copy() for l in range(2)]
+    assert omodel.commit_block_causal(w, SHAPE, x.cpu().numpy(), ck, cv, L) == L + 256
+    close(bf16_to_np(kv.k[0, 0, :, L:L + 256]), ck[0][:, L:L + 256], what="causal K layer 0", bf16_out=True)
+    close(bf16_to_np(kv.v[0, 0, :, L:L + 256]), cv[0][:, L:L + 256], what="causal V layer 0", bf16_out=True)
+
+
 def test_refresh_recomputes_kv_of_final_canvas(env):
     dg, w, m = env
     kv, k, v = _kv(dg, cap=L + 256)
