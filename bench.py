@@ -53,9 +53,9 @@ def expert_gemm1_bytes(shape, routes: int, experts_touched: int) -> float:
 # true bytes / counter bytes that the same counter gives for a plain 1 GiB device copy.  Valid
 # only for the kernel source it was taken on: a changed source reports traffic null.
 PMC_TRAFFIC = {
-    "kernel": "expert_stream_kernel<true, 3, 1, 1>", "source": "block_discrete_diffusion_amd/csrc/k_moe.hip",
-    "sha": "fbd916b0706ec844",
-    "fetch_kib": 202296.0, "fetch_scale": 1048576.0 / 524309.2,  # copy of 1 GiB reads 524309 KiB
+    "kernel": "expert_stream_kernel<true, 3, 1, 1, false>", "source": "block_discrete_diffusion_amd/csrc/k_moe.hip",
+    "sha": "1c8970ea13ed8ecc",
+    "fetch_kib": 202294.0, "fetch_scale": 1048576.0 / 524308.1,  # copy of 1 GiB reads 524308 KiB
     "write_kib": 1536.0, "write_scale": 1048576.0 / 1048576.0,   # and writes 1048576 KiB
 }
 
