@@ -75,6 +75,8 @@ struct dg_ctx {
   float* head_part = nullptr;  // [r_canvas][V/64][8]
   float* gpart = nullptr;      // split-K partial slices of the dense GEMMs
   float* rope = nullptr;       // [r_max][D/2][2] cos/sin of the rows of the current step
+  int32_t* tok = nullptr;      // [r_canvas] canvas tokens of a slot-mapped call, in call order
+  std::vector<int32_t> last_slots;  // slots of the requests whose canvas K/V the workspace holds
   uint16_t* ck = nullptr;      // [L][max_batch][Hkv][C][D]
   uint16_t* cv = nullptr;
   std::vector<uint16_t*> pk1;  // per layer: packed gate/up expert weights
@@ -126,8 +128,16 @@ void timed(dg_ctx* c, const char* name, hipStream_t s, F&& launch) {
   c->recs.push_back({name, a, b});
 }
 
-long kv_layer_stride(const dg_model_desc& m, int batch, int cap) {
-  return static_cast<long>(batch) * m.n_kv_heads * cap * m.head_dim;
+long kv_layer_stride(const dg_model_desc& m, int n_slots, int cap) {
+  return static_cast<long>(n_slots) * m.n_kv_heads * cap * m.head_dim;
+}
+int kv_slots(const dg_kv_cache* kv) { return kv->n_slots > 0 ? kv->n_slots : kv->batch; }
+int kv_slot(const dg_kv_cache* kv, int b) { return kv->slot ? kv->slot[b] : b; }
+bool kv_identity(const dg_kv_cache* kv) {
+  if (!kv->slot) return true;
+  for (int b = 0; b < kv->batch; ++b)
+    if (kv->slot[b] != b) return false;
+  return true;
 }
 
 int check_hip(dg_ctx* c, const char* where) {
@@ -161,11 +171,14 @@ std::string validate_desc(const dg_model_desc& m) {
   return "";
 }
 
-RowMap make_map(int rows_per_req, int n_req, const int32_t* pos0) {
+RowMap make_map(int rows_per_req, int n_req, const int32_t* pos0, const dg_kv_cache* kv = nullptr) {
   RowMap r{};
   r.rows_per_req = rows_per_req;
   r.n_req = n_req;
-  for (int b = 0; b < n_req; ++b) r.pos0[b] = pos0 ? pos0[b] : 0;
+  for (int b = 0; b < n_req; ++b) {
+    r.pos0[b] = pos0 ? pos0[b] : 0;
+    r.slot[b] = kv ? kv_slot(kv, b) : b;
+  }
   return r;
 }
 
@@ -184,7 +197,7 @@ int choose_split(const dg_ctx* c, int base_wgs, int n_keys, int rows, int waves)
 // Prefill mode (one request): K/V go to the cache at len..; keys = cache[0:len+rows), causal.
 void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len, bool prefill,
                uint16_t* kc_l, uint16_t* vc_l, int cap, const dg_debug* dbg, const float* next_gain,
-               uint16_t* next_out, hipStream_t s) {
+               uint16_t* next_out, hipStream_t s, const dg_kv_cache* kv_slots_of = nullptr) {
   const dg_model_desc& m = c->m;
   const dg_layer_weights& lw = c->layers[l];
   const int rows = n_req * rows_per_req;
@@ -226,6 +239,7 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   for (int b = 0; b < n_req; ++b) {
     at.n_cache[b] = prefill ? len[b] + rows_per_req : len[b];
     at.q_pos0[b] = len[b];
+    at.slot[b] = kv_slots_of ? kv_slot(kv_slots_of, b) : b;
     max_keys = std::max(max_keys, at.n_cache[b] + (prefill ? 0 : m.canvas));
   }
   at.n_extra = prefill ? 0 : m.canvas;
@@ -317,6 +331,16 @@ int check_kv(dg_ctx* c, const dg_kv_cache* kv) {
   if (kv->batch < 1 || kv->batch > c->max_batch)
     return c->fail(DG_ERR_CAPACITY, "kv->batch must be in [1, max_batch]");
   if (kv->cap < 1) return c->fail(DG_ERR_ARG, "kv->cap < 1");
+  if (kv->n_slots < 0 || (kv->n_slots > 0 && kv->n_slots < kv->batch))
+    return c->fail(DG_ERR_ARG, "kv->n_slots must be 0 or >= batch");
+  if (kv->slot) {
+    const int ns = kv_slots(kv);
+    for (int b = 0; b < kv->batch; ++b) {
+      if (kv->slot[b] < 0 || kv->slot[b] >= ns) return c->fail(DG_ERR_ARG, "kv->slot out of [0, n_slots)");
+      for (int e = 0; e < b; ++e)
+        if (kv->slot[e] == kv->slot[b]) return c->fail(DG_ERR_ARG, "kv->slot entries must be distinct");
+    }
+  }
   for (int b = 0; b < kv->batch; ++b)
     if (kv->len[b] < 0 || kv->len[b] > kv->cap) return c->fail(DG_ERR_ARG, "kv->len out of [0, cap]");
   return DG_OK;
@@ -382,7 +406,7 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
             c->alloc(&c->head_part, static_cast<long>(c->r_canvas) * (m.vocab / kHeadSlice) * 8) &&
             c->alloc(&c->ck, ckv) && c->alloc(&c->cv, ckv) &&
             c->alloc(&c->gpart, kGemmPartFloats) &&
-            c->alloc(&c->rope, R * m.head_dim);
+            c->alloc(&c->rope, R * m.head_dim) && c->alloc(&c->tok, c->r_canvas);
   // expert banks, repacked once into the MFMA fragment order the expert GEMMs stream
   const long ew = static_cast<long>(m.n_experts) * m.d_ff_expert * m.d_model;
   const int E = m.n_experts, F = m.d_ff_expert;
@@ -483,8 +507,8 @@ int dg_prefill_causal(dg_ctx* c, const int32_t* tokens, const int32_t* n_new, in
       const int32_t len_b = kv->len[b] + done;
       if (m.rope_theta != 0.f) launch_rope_table(make_map(n, 1, &len_b), n, m.head_dim, m.rope_theta, c->rope, s);
       for (int l = 0; l < m.n_layers; ++l) {
-        const long base = l * kv_layer_stride(m, kv->batch, kv->cap) +
-                          static_cast<long>(b) * m.n_kv_heads * kv->cap * m.head_dim;
+        const long base = l * kv_layer_stride(m, kv_slots(kv), kv->cap) +
+                          static_cast<long>(kv_slot(kv, b)) * m.n_kv_heads * kv->cap * m.head_dim;
         const float* ng = (l + 1 < m.n_layers) ? c->layers[l + 1].attn_norm : nullptr;
         run_layer(c, l, 1, n, &len_b, true, kv->k + base, kv->v + base, kv->cap, nullptr, ng, c->a, s);
       }
@@ -505,7 +529,7 @@ int dg_canvas_init(dg_ctx* c, dg_canvas_state* st, const dg_kv_cache* kv,
     return c->fail(DG_ERR_ARG, "canvas_init: null pointer");
   int rc = check_kv(c, kv);
   if (rc) return rc;
-  const RowMap map = make_map(c->m.canvas, kv->batch, kv->len);
+  const RowMap map = make_map(c->m.canvas, kv->batch, kv->len, kv);
   launch_canvas_init(st->tokens, st->committed, st->stable_run, st->stopped, c->m.canvas, c->m.vocab,
                      static_cast<uint32_t>(cfg->seed), static_cast<uint32_t>(cfg->seed >> 32), map, s);
   return check_hip(c, "canvas_init");
@@ -520,6 +544,10 @@ static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
   const dg_debug* dbg = p ? p->debug : nullptr;
   const bool head_only = flags & DG_STEP_HEAD_ONLY;
   const bool no_head = flags & DG_STEP_NO_HEAD;
+  if (canvas && !kv_identity(kv)) {  // the rows of this call, in call order
+    launch_gather_rows(canvas, c->tok, make_map(C, B, kv->len, kv), s);
+    canvas = c->tok;
+  }
 
   if (!head_only) {
     if (flags & DG_STEP_HIDDEN_IN) {
@@ -538,9 +566,12 @@ static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
     for (int l = 0; l < m.n_layers; ++l) {
       const bool last = l + 1 == m.n_layers;
       const float* ng = !last ? c->layers[l + 1].attn_norm : (no_head ? nullptr : c->w.final_norm);
-      run_layer(c, l, B, C, kv->len, false, kv->k + l * kv_layer_stride(m, B, kv->cap),
-                kv->v + l * kv_layer_stride(m, B, kv->cap), kv->cap, dbg, ng, last ? c->f : c->a, s);
+      run_layer(c, l, B, C, kv->len, false, kv->k + l * kv_layer_stride(m, kv_slots(kv), kv->cap),
+                kv->v + l * kv_layer_stride(m, kv_slots(kv), kv->cap), kv->cap, dbg, ng,
+                last ? c->f : c->a, s, kv);
     }
+    c->last_slots.resize(B);
+    for (int b = 0; b < B; ++b) c->last_slots[b] = kv_slot(kv, b);
     if (dbg && dbg->hidden_out)
       (void)hipMemcpyAsync(dbg->hidden_out, c->h, sizeof(float) * rows * d, hipMemcpyDeviceToDevice, s);
     if (dbg && (dbg->canvas_k || dbg->canvas_v)) {
@@ -560,16 +591,18 @@ static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
   const uint16_t* f = head_only ? static_cast<const uint16_t*>(p->hidden_in) : c->f;
   HeadArgs ha{};
   ha.f = f; ha.n_rows = rows; ha.w = c->w.lm_head; ha.K = d; ha.V = m.vocab;
-  ha.temp = dg_temperature(cfg, p ? p->step : 0);
   ha.k0 = static_cast<uint32_t>(cfg->seed); ha.k1 = static_cast<uint32_t>(cfg->seed >> 32);
-  ha.step = p ? p->step : 0;
+  for (int b = 0; b < B; ++b) {
+    ha.step[b] = (p && p->steps) ? p->steps[b] : (p ? p->step : 0);
+    ha.temp[b] = dg_temperature(cfg, ha.step[b]);
+  }
   ha.cur_tok = canvas;
-  ha.map = make_map(C, B, kv->len);
+  ha.map = make_map(C, B, kv->len, kv);
   ha.part = c->head_part;
   ha.dbg_logits = dbg ? dbg->logits : nullptr;
   timed(c, "head_lse_gumbel", s, [&] { launch_head(ha, s); });
   timed(c, "head_merge", s, [&] { launch_head_merge(c->head_part, rows, m.vocab / kHeadSlice, kHeadSlice, canvas, out->cand,
-                    out->t_cand, out->t_cur, out->lse, out->entropy, s); });
+                    out->t_cand, out->t_cur, out->lse, out->entropy, ha.map, s); });
   return DG_OK;
 }
 
@@ -594,8 +627,10 @@ int dg_denoise_step(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
     if (!out || !out->cand || !out->t_cand || !out->t_cur || !out->lse || !out->entropy)
       return c->fail(DG_ERR_ARG, "denoise: row stats pointer is null");
     if (cfg->max_steps < 1) return c->fail(DG_ERR_ARG, "denoise: max_steps < 1");
-    const int step = p ? p->step : 0;
-    if (step < 0 || step >= cfg->max_steps) return c->fail(DG_ERR_ARG, "denoise: step out of [0, max_steps)");
+    for (int b = 0; b < kv->batch; ++b) {
+      const int step = (p && p->steps) ? p->steps[b] : (p ? p->step : 0);
+      if (step < 0 || step >= cfg->max_steps) return c->fail(DG_ERR_ARG, "denoise: step out of [0, max_steps)");
+    }
     if (!(cfg->temp_start > 0.f) || !(cfg->temp_end > 0.f))
       return c->fail(DG_ERR_ARG, "denoise: temperatures must be > 0");
   }
@@ -605,8 +640,8 @@ int dg_denoise_step(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
 }
 
 int dg_sample_commit(dg_ctx* c, dg_canvas_state* st, const dg_row_stats* rs,
-                     const dg_sampler_cfg* cfg, int32_t step, const dg_kv_cache* kv,
-                     dg_step_status* status, hipStream_t s) {
+                     const dg_sampler_cfg* cfg, int32_t step, const int32_t* steps,
+                     const dg_kv_cache* kv, dg_step_status* status, hipStream_t s) {
   if (!c) return DG_ERR_ARG;
   if (!st || !st->tokens || !st->committed || !st->stable_run || !st->stopped || !rs || !rs->cand ||
       !rs->t_cand ||
@@ -614,8 +649,11 @@ int dg_sample_commit(dg_ctx* c, dg_canvas_state* st, const dg_row_stats* rs,
     return c->fail(DG_ERR_ARG, "sample_commit: null pointer");
   int rc = check_kv(c, kv);
   if (rc) return rc;
-  if (cfg->max_steps < 1 || step < 0 || step >= cfg->max_steps)
-    return c->fail(DG_ERR_ARG, "sample_commit: step out of [0, max_steps)");
+  for (int b = 0; b < kv->batch; ++b) {
+    const int sb = steps ? steps[b] : step;
+    if (cfg->max_steps < 1 || sb < 0 || sb >= cfg->max_steps)
+      return c->fail(DG_ERR_ARG, "sample_commit: step out of [0, max_steps)");
+  }
   if (cfg->commit_per_step < 0 || cfg->stable_steps < 1 || !(cfg->renoise_conf >= 0.f))
     return c->fail(DG_ERR_ARG, "sample_commit: bad sampler config");
   if (cfg->select_mode != 0 && cfg->select_mode != 1)
@@ -627,7 +665,7 @@ int dg_sample_commit(dg_ctx* c, dg_canvas_state* st, const dg_row_stats* rs,
   a.stopped = st->stopped;
   a.cand = rs->cand; a.t_cand = rs->t_cand; a.t_cur = rs->t_cur; a.lse = rs->lse; a.ent = rs->entropy;
   a.status = status;
-  a.C = c->m.canvas; a.V = c->m.vocab; a.step = step; a.max_steps = cfg->max_steps;
+  a.C = c->m.canvas; a.V = c->m.vocab; a.max_steps = cfg->max_steps;
   a.commit_m = cfg->commit_per_step;
   a.log_tau = cfg->renoise_conf > 0.f ? static_cast<float>(std::log(static_cast<double>(cfg->renoise_conf)))
                                       : -INFINITY;
@@ -635,7 +673,11 @@ int dg_sample_commit(dg_ctx* c, dg_canvas_state* st, const dg_row_stats* rs,
   a.renoise_committed = cfg->renoise_committed;
   a.select_mode = cfg->select_mode; a.entropy_budget = cfg->entropy_budget;
   a.k0 = static_cast<uint32_t>(cfg->seed); a.k1 = static_cast<uint32_t>(cfg->seed >> 32);
-  for (int b = 0; b < kv->batch; ++b) a.pos0[b] = kv->len[b];
+  for (int b = 0; b < kv->batch; ++b) {
+    a.pos0[b] = kv->len[b];
+    a.slot[b] = kv_slot(kv, b);
+    a.step[b] = steps ? steps[b] : step;
+  }
   timed(c, "sample_commit", s, [&] { launch_sample_commit(a, kv->batch, s); });
   return check_hip(c, "sample_commit");
 }
@@ -652,9 +694,14 @@ int dg_commit_block(dg_ctx* c, const int32_t* canvas, dg_kv_cache* kv, int32_t r
   for (int b = 0; b < kv->batch; ++b)
     if (static_cast<long>(kv->len[b]) + m.canvas > kv->cap)
       return c->fail(DG_ERR_CAPACITY, "commit_block: len + canvas > cap");
-  if (refresh == DG_COMMIT_CAUSAL) {  // the canvases are back to back, as prefill packs them
+  if (refresh == DG_COMMIT_CAUSAL) {  // prefill takes the canvases back to back, in call order
+    const int32_t* toks = canvas;
+    if (!kv_identity(kv)) {
+      launch_gather_rows(canvas, c->tok, make_map(m.canvas, kv->batch, kv->len, kv), s);
+      toks = c->tok;
+    }
     std::vector<int32_t> n_new(kv->batch, m.canvas);
-    return dg_prefill_causal(c, canvas, n_new.data(), kv->batch, kv, s);
+    return dg_prefill_causal(c, toks, n_new.data(), kv->batch, kv, s);
   }
   if (refresh) {
     dg_step_params p{};
@@ -662,13 +709,21 @@ int dg_commit_block(dg_ctx* c, const int32_t* canvas, dg_kv_cache* kv, int32_t r
     rc = denoise_impl(c, canvas, kv, nullptr, &p, nullptr, s);
     if (rc) return rc;
   }
-  const RowMap map = make_map(m.canvas, kv->batch, kv->len);
+  const RowMap map = make_map(m.canvas, kv->batch, kv->len, kv);
+  ReqIndex src{};  // where each request's canvas K/V sit in the workspace (the last forward)
+  for (int b = 0; b < kv->batch; ++b) {
+    src.idx[b] = -1;
+    for (size_t j = 0; j < c->last_slots.size(); ++j)
+      if (c->last_slots[j] == kv_slot(kv, b)) src.idx[b] = static_cast<int32_t>(j);
+    if (src.idx[b] < 0)
+      return c->fail(DG_ERR_ARG, "commit_block: the last forward pass did not cover this request's slot");
+  }
   const long per_layer_ws = static_cast<long>(c->max_batch) * m.n_kv_heads * m.canvas * m.head_dim;
   for (int l = 0; l < m.n_layers; ++l) {
-    const long dst = l * kv_layer_stride(m, kv->batch, kv->cap);
+    const long dst = l * kv_layer_stride(m, kv_slots(kv), kv->cap);
     timed(c, "kv_append", s, [&] {
       launch_kv_append(c->ck + l * per_layer_ws, c->cv + l * per_layer_ws, kv->k + dst, kv->v + dst,
-                       kv->batch, m.n_kv_heads, m.canvas, m.head_dim, kv->cap, map, s);
+                       kv->batch, m.n_kv_heads, m.canvas, m.head_dim, kv->cap, map, src, s);
     });
   }
   rc = check_hip(c, "commit_block");
@@ -716,6 +771,8 @@ int dg_debug_set_canvas_kv(dg_ctx* c, const uint16_t* k, const uint16_t* v, int3
     (void)hipMemcpyAsync(c->ck + dst, k + src, 2 * batch * per_b, hipMemcpyDeviceToDevice, s);
     (void)hipMemcpyAsync(c->cv + dst, v + src, 2 * batch * per_b, hipMemcpyDeviceToDevice, s);
   }
+  c->last_slots.resize(batch);  // the rows now stand for slots 0..batch-1
+  for (int b = 0; b < batch; ++b) c->last_slots[b] = b;
   return check_hip(c, "set_canvas_kv");
 }
 

@@ -9,10 +9,14 @@ constexpr int kMaxBatch = 64;
 
 // Per-request row bookkeeping passed by value to kernels: request b owns rows
 // [b*rows_per_req, (b+1)*rows_per_req) and row i of it sits at position pos0[b] + i.
+// Rows of a call: n_req requests of rows_per_req rows; request b starts at position pos0[b]
+// and owns slot slot[b] of the KV cache and of every per-request array (and of the random
+// streams, whose counters carry the slot).
 struct RowMap {
   int32_t rows_per_req;
   int32_t n_req;
   int32_t pos0[kMaxBatch];
+  int32_t slot[kMaxBatch];
 };
 
 // ---- k_norm.hip
@@ -60,8 +64,9 @@ void launch_swiglu_reduce(const float* part, long part_stride, int split, uint16
 struct HeadArgs {
   const uint16_t* f; int n_rows;      // bf16 [rows][d] final normed state
   const uint16_t* w; int K; int V;    // lm_head [V][d]
-  float inv_dummy; float temp;        // temperature T (t = z / T)
-  uint32_t k0, k1; int32_t step;      // Philox key (seed) and step
+  uint32_t k0, k1;                    // Philox key (seed)
+  float temp[kMaxBatch];              // temperature T of each request (t = z / T)
+  int32_t step[kMaxBatch];            // denoise step of each request (Philox counter)
   const int32_t* cur_tok;             // [rows] current canvas token
   RowMap map;
   float* part;                        // [rows][n_slices][8]
@@ -70,7 +75,9 @@ struct HeadArgs {
 void launch_head(const HeadArgs& a, hipStream_t s);
 void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
                        const int32_t* cur_tok, int32_t* cand, float* t_cand, float* t_cur,
-                       float* lse, float* ent, hipStream_t s);
+                       float* lse, float* ent, const RowMap& map, hipStream_t s);
+// dst[b][i] = src[map.slot[b]][i] for the map's requests (rows_per_req ints each)
+void launch_gather_rows(const int32_t* src, int32_t* dst, const RowMap& map, hipStream_t s);
 
 // ---- k_attn.hip
 constexpr int kMaxParts = 4;  // largest split-K slice count a consumer sums
@@ -94,13 +101,14 @@ void launch_rope_scatter(const RopeArgs& a, hipStream_t s);
 struct AttnArgs {
   const uint16_t* q;       // [rows][Hq*D]
   uint16_t* out;           // [rows][Hq*D]
-  const uint16_t* kc; const uint16_t* vc; int cap;   // cache base of the layer [B][Hkv][cap][D]
+  const uint16_t* kc; const uint16_t* vc; int cap;   // cache base of the layer [slots][Hkv][cap][D]
   const uint16_t* kx; const uint16_t* vx; int xcap;  // extra keys (canvas) [B][Hkv][xcap][D]
   int Hq, Hkv, D;
   int rows_per_req; int n_req;
   int32_t n_cache[kMaxBatch];   // keys read from the cache per request
   int32_t n_extra;              // canvas keys (0 in prefill)
   int32_t q_pos0[kMaxBatch];    // position of the first query row of each request
+  int32_t slot[kMaxBatch];      // cache slot of each request (kc/vc hold [n_slots][Hkv][cap][D])
   int causal;                   // key position <= query position
   float scale;                  // 1/sqrt(D)
   int n_split; int split_keys;  // split-KV: each split covers split_keys keys
@@ -157,19 +165,26 @@ struct SamplerArgs {
   const int32_t* cand; const float* t_cand; const float* t_cur; const float* lse;
   const float* ent;
   void* status;  // dg_step_status[B]
-  int C; int V; int step; int max_steps; int commit_m; float log_tau; int stable_steps;
+  int C; int V; int max_steps; int commit_m; float log_tau; int stable_steps;
   float entropy_stop; int renoise_committed; uint32_t k0, k1;
   int select_mode;       // 0: top commit_m by confidence; 1: entropy-bounded
   float entropy_budget;  // select_mode 1: bound on the running entropy sum of the selection
   int32_t pos0[kMaxBatch];
+  int32_t slot[kMaxBatch];  // per-request arrays (state, stats, status) are indexed by slot
+  int32_t step[kMaxBatch];  // sampler step of each request
 };
 void launch_sample_commit(const SamplerArgs& a, int n_req, hipStream_t s);
 void launch_canvas_init(int32_t* tokens, uint8_t* committed, int32_t* stable_run,
                         int32_t* stopped, int C, int V,
                         uint32_t k0, uint32_t k1, const RowMap& map, hipStream_t s);
 // Copy canvas K/V [B][Hkv][C][D] of one layer into the cache at [len[b], len[b]+C).
+// Request b of the map takes the canvas K/V of request src.idx[b] of the call that produced
+// them (src [requests][Hkv][C][D]).
+struct ReqIndex {
+  int32_t idx[kMaxBatch];
+};
 void launch_kv_append(const uint16_t* src_k, const uint16_t* src_v, uint16_t* dst_k,
                       uint16_t* dst_v, int B, int Hkv, int C, int D, int cap,
-                      const RowMap& map, hipStream_t s);
+                      const RowMap& map, const ReqIndex& src, hipStream_t s);
 
 }  // namespace dg

@@ -200,7 +200,8 @@ void attention_kernel(AttnArgs a) {
   const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const float sl2 = a.scale * 1.4426950408889634f;
 
-  const long kv_head = static_cast<long>(b) * a.Hkv + g;
+  const long kv_head = static_cast<long>(a.slot[b]) * a.Hkv + g;  // cache slot of the request
+  const long kx_head = static_cast<long>(b) * a.Hkv + g;          // this call's canvas rows
   u32x4_t rk[KCH], rv[KCH];
 
   // S^T of one 64-key block for both query tiles (raw dot products)
@@ -346,7 +347,7 @@ void attention_kernel(AttnArgs a) {
 
   run_range(a.kc + kv_head * a.cap * D, a.vc + kv_head * a.cap * D, 0, k_lo, min(k_hi, n_cache));
   if (a.n_extra > 0)
-    run_range(a.kx + kv_head * a.xcap * D, a.vx + kv_head * a.xcap * D, n_cache, max(k_lo, n_cache), k_hi);
+    run_range(a.kx + kx_head * a.xcap * D, a.vx + kx_head * a.xcap * D, n_cache, max(k_lo, n_cache), k_hi);
 
   if (!active) return;
   const float l_run[2] = {l_acc[0][0], l_acc[1][0]};

@@ -295,6 +295,7 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
     const int b = tc / a.map.rows_per_req;
     const int pos = a.map.pos0[b] + (tc - b * a.map.rows_per_req);
     const int cur = ok ? a.cur_tok[tc] : -1;
+    const float temp_b = a.temp[b];
     float tv[ML::FM][4];
     Stat st;
     st.m = -INFINITY; st.s = 0.f; st.st = 0.f; st.bs = -INFINITY; st.bt = 0.f; st.tc = NAN;
@@ -303,12 +304,12 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
     for (int fm = 0; fm < ML::FM; ++fm) {
       const int v0 = f0 + wf * ML::WF + fm * 16 + 4 * (lane >> 4);
       const philox_out rnd = philox4x32_10(static_cast<uint32_t>(v0 >> 2), static_cast<uint32_t>(pos),
-                                           static_cast<uint32_t>(a.step),
-                                           (static_cast<uint32_t>(b) << 8) | kStreamGumbel, a.k0, a.k1);
+                                           static_cast<uint32_t>(a.step[b]),
+                                           (static_cast<uint32_t>(a.map.slot[b]) << 8) | kStreamGumbel, a.k0, a.k1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float z = ml.acc[fm][tn][i];
-        const float t_ = z / a.temp;
+        const float t_ = z / temp_b;
         tv[fm][i] = t_;
         const float sc = t_ + gumbel(rnd.x[i]);
         if (sc > st.bs) { st.bs = sc; st.bi = v0 + i; st.bt = t_; }
@@ -337,11 +338,12 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
 
 // One work-group (4 waves) per row: thread t merges slices t, t + 256, ... (two 16-byte loads
 // each, all issued first), then the wave and the 4 wave results merge in a fixed order.
+// Row r of the call (request r / rows_per_req) writes its statistics at the request's slot.
 __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict__ part, int n_rows,
                                                          int n_slices, int slice_w,
                                                          const int32_t* __restrict__ cur_tok,
                                                          int32_t* cand, float* t_cand, float* t_cur,
-                                                         float* lse, float* ent) {
+                                                         float* lse, float* ent, RowMap map) {
   constexpr int PER = 8;  // slices per thread held in registers (n_slices <= 2048)
   __shared__ float wm[4][8];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -381,12 +383,14 @@ __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict
     r = merge_stat(r, o);
   }
   const float l = r.m + logf(r.s);
-  lse[row] = l;
-  ent[row] = l - r.st / r.s;
-  cand[row] = r.bi;
-  t_cand[row] = r.bt;
+  const int rb = row / map.rows_per_req;
+  const long orow = static_cast<long>(map.slot[rb]) * map.rows_per_req + (row - rb * map.rows_per_req);
+  lse[orow] = l;
+  ent[orow] = l - r.st / r.s;
+  cand[orow] = r.bi;
+  t_cand[orow] = r.bt;
   const int x = cur_tok[row];
-  t_cur[row] = part[(static_cast<long>(row) * n_slices + x / slice_w) * 8 + 6];
+  t_cur[orow] = part[(static_cast<long>(row) * n_slices + x / slice_w) * 8 + 6];
 }
 
 template <int BF, int BT, int EPI>
@@ -484,9 +488,22 @@ void launch_head(const HeadArgs& a, hipStream_t s) {
 
 void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
                        const int32_t* cur_tok, int32_t* cand, float* t_cand, float* t_cur,
-                       float* lse, float* ent, hipStream_t s) {
+                       float* lse, float* ent, const RowMap& map, hipStream_t s) {
   hipLaunchKernelGGL(head_merge_kernel, dim3(n_rows), dim3(256), 0, s, part, n_rows, n_slices,
-                     slice_w, cur_tok, cand, t_cand, t_cur, lse, ent);
+                     slice_w, cur_tok, cand, t_cand, t_cur, lse, ent, map);
+}
+
+// Canvas tokens of this call's requests, compacted: dst[b][i] = src[slot[b]][i].
+__global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restrict__ src,
+                                                          int32_t* __restrict__ dst, RowMap map) {
+  const int b = blockIdx.x;
+  for (int i = threadIdx.x; i < map.rows_per_req; i += 256)
+    dst[static_cast<long>(b) * map.rows_per_req + i] =
+        src[static_cast<long>(map.slot[b]) * map.rows_per_req + i];
+}
+
+void launch_gather_rows(const int32_t* src, int32_t* dst, const RowMap& map, hipStream_t s) {
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(map.n_req), dim3(256), 0, s, src, dst, map);
 }
 
 }  // namespace dg

@@ -39,20 +39,21 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
   __shared__ int ired[4];
   __shared__ float fred[4];
   const int b = blockIdx.x, i = threadIdx.x;
+  const int sb = a.slot[b];  // the request's slot in every per-request array
   const int C = a.C;
-  if (a.stopped[b]) {  // finished canvas: frozen
+  if (a.stopped[sb]) {  // finished canvas: frozen
     if (i == 0) {
-      StatusDev st = reinterpret_cast<StatusDev*>(a.status)[b];
+      StatusDev st = reinterpret_cast<StatusDev*>(a.status)[sb];
       st.changed = 0;
       st.n_new = 0;
       st.n_renoised = 0;
       st.stop = 1;
-      reinterpret_cast<StatusDev*>(a.status)[b] = st;
+      reinterpret_cast<StatusDev*>(a.status)[sb] = st;
     }
     return;
   }
   const bool slot = i < C;
-  const long r = static_cast<long>(b) * C + i;
+  const long r = static_cast<long>(sb) * C + i;
   const int x_prev = slot ? a.tokens[r] : 0;
   const bool com_prev = slot ? a.committed[r] != 0 : true;
   const float lse = slot ? a.lse[r] : 0.f;
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
   const float cu = slot ? a.t_cur[r] - lse : 0.f;
   const int cand = slot ? a.cand[r] : 0;
   const float ent = slot ? a.ent[r] : 0.f;
-  const int stable_prev = a.stable_run[b];
+  const int stable_prev = a.stable_run[sb];
   const bool U = slot && !com_prev;
   const bool by_entropy = a.select_mode == 1;
   const float key = by_entropy ? -ent : cc;
@@ -103,8 +104,8 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
   }
   const bool sel = U && rank < m;
   const int pos = a.pos0[b] + i;
-  const philox_out rnd = philox4x32_10(0u, static_cast<uint32_t>(pos), static_cast<uint32_t>(a.step),
-                                       (static_cast<uint32_t>(b) << 8) | kStreamRenoise, a.k0, a.k1);
+  const philox_out rnd = philox4x32_10(0u, static_cast<uint32_t>(pos), static_cast<uint32_t>(a.step[b]),
+                                       (static_cast<uint32_t>(sb) << 8) | kStreamRenoise, a.k0, a.k1);
   const int fresh = token_from_word(rnd.x[0], static_cast<uint32_t>(a.V));
   int x = x_prev;
   bool com = com_prev;
@@ -130,10 +131,10 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
   if (i == 0) {
     const float mean_ent = ent_sum / static_cast<float>(C);
     const int sr = changed ? 0 : stable_prev + 1;
-    int stop = (sr >= a.stable_steps) || (a.step >= a.max_steps - 1);
+    int stop = (sr >= a.stable_steps) || (a.step[b] >= a.max_steps - 1);
     if (a.entropy_stop >= 0.f && !changed && mean_ent < a.entropy_stop) stop = 1;
-    a.stable_run[b] = sr;
-    a.stopped[b] = stop;
+    a.stable_run[sb] = sr;
+    a.stopped[sb] = stop;
     StatusDev st;
     st.changed = changed ? 1 : 0;
     st.n_committed = n_com;
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256) void sample_commit_kernel(SamplerArgs a) {
     st.stop = stop;
     st.nonfinite = nonfin ? 1 : 0;
     st.mean_entropy = mean_ent;
-    reinterpret_cast<StatusDev*>(a.status)[b] = st;
+    reinterpret_cast<StatusDev*>(a.status)[sb] = st;
   }
 }
 
@@ -151,25 +152,28 @@ __global__ __launch_bounds__(256) void canvas_init_kernel(int32_t* tokens, uint8
                                                           int32_t* stable_run, int32_t* stopped,
                                                           int C, int V,
                                                           uint32_t k0, uint32_t k1, RowMap map) {
-  const int b = blockIdx.x;
+  const int b = blockIdx.x, sb = map.slot[b];
   for (int i = threadIdx.x; i < C; i += 256) {
     const philox_out rnd = philox4x32_10(0u, static_cast<uint32_t>(map.pos0[b] + i), 0u,
-                                         (static_cast<uint32_t>(b) << 8) | kStreamInit, k0, k1);
-    tokens[static_cast<long>(b) * C + i] = token_from_word(rnd.x[0], static_cast<uint32_t>(V));
-    committed[static_cast<long>(b) * C + i] = 0;
+                                         (static_cast<uint32_t>(sb) << 8) | kStreamInit, k0, k1);
+    tokens[static_cast<long>(sb) * C + i] = token_from_word(rnd.x[0], static_cast<uint32_t>(V));
+    committed[static_cast<long>(sb) * C + i] = 0;
   }
   if (threadIdx.x == 0) {
-    stable_run[b] = 0;
-    stopped[b] = 0;
+    stable_run[sb] = 0;
+    stopped[sb] = 0;
   }
 }
 
-// 16-byte chunks: src [B][Hkv][C][D] -> dst [B][Hkv][cap][D] at slot pos0[b] + i.
+// 16-byte chunks: src [requests][Hkv][C][D] (the producing call's requests) -> dst
+// [slots][Hkv][cap][D]: request b takes source request src.idx[b] and writes cache slot
+// slot[b] at positions pos0[b] + i.
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restrict__ sk,
                                                         const uint16_t* __restrict__ sv,
                                                         uint16_t* __restrict__ dk,
                                                         uint16_t* __restrict__ dv, int B, int Hkv,
-                                                        int C, int D, int cap, RowMap map) {
+                                                        int C, int D, int cap, RowMap map,
+                                                        ReqIndex src) {
   const int cpr = D / 8;  // chunks per row
   const long n = static_cast<long>(B) * Hkv * C * cpr;
   const long t = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
@@ -179,9 +183,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restri
   const int i = static_cast<int>(row % C);
   const long bg = row / C;
   const int b = static_cast<int>(bg / Hkv);
-  const long drow = bg * cap + map.pos0[b] + i;
-  st16(dk + drow * D + ch * 8, ld16(sk + row * D + ch * 8));
-  st16(dv + drow * D + ch * 8, ld16(sv + row * D + ch * 8));
+  const long g = bg - static_cast<long>(b) * Hkv;
+  const long drow = (static_cast<long>(map.slot[b]) * Hkv + g) * cap + map.pos0[b] + i;
+  const long srow = (static_cast<long>(src.idx[b]) * Hkv + g) * C + i;
+  st16(dk + drow * D + ch * 8, ld16(sk + srow * D + ch * 8));
+  st16(dv + drow * D + ch * 8, ld16(sv + srow * D + ch * 8));
 }
 
 }  // namespace
@@ -199,10 +205,10 @@ void launch_canvas_init(int32_t* tokens, uint8_t* committed, int32_t* stable_run
 
 void launch_kv_append(const uint16_t* src_k, const uint16_t* src_v, uint16_t* dst_k,
                       uint16_t* dst_v, int B, int Hkv, int C, int D, int cap, const RowMap& map,
-                      hipStream_t s) {
+                      const ReqIndex& src, hipStream_t s) {
   const long n = static_cast<long>(B) * Hkv * C * (D / 8);
   hipLaunchKernelGGL(kv_append_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src_k, src_v,
-                     dst_k, dst_v, B, Hkv, C, D, cap, map);
+                     dst_k, dst_v, B, Hkv, C, D, cap, map, src);
 }
 
 }  // namespace dg

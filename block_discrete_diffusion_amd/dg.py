@@ -46,7 +46,8 @@ class Weights(C.Structure):
 
 
 class KVCache(C.Structure):
-    _fields_ = [("k", vp), ("v", vp), ("cap", C.c_int32), ("batch", C.c_int32), ("len", C.POINTER(C.c_int32))]
+    _fields_ = [("k", vp), ("v", vp), ("cap", C.c_int32), ("batch", C.c_int32), ("len", C.POINTER(C.c_int32)),
+                ("slot", C.POINTER(C.c_int32)), ("n_slots", C.c_int32)]
 
 
 class CanvasState(C.Structure):
@@ -70,7 +71,8 @@ class Debug(C.Structure):
 
 
 class StepParams(C.Structure):
-    _fields_ = [("step", C.c_int32), ("flags", C.c_uint32), ("hidden_in", vp), ("debug", C.POINTER(Debug))]
+    _fields_ = [("step", C.c_int32), ("flags", C.c_uint32), ("hidden_in", vp), ("debug", C.POINTER(Debug)),
+                ("steps", C.POINTER(C.c_int32))]
 
 
 class KernelTime(C.Structure):
@@ -92,7 +94,7 @@ _lib.dg_canvas_init.argtypes = [vp, C.POINTER(CanvasState), C.POINTER(KVCache), 
 _lib.dg_denoise_step.argtypes = [vp, vp, C.POINTER(KVCache), C.POINTER(SamplerCfg), C.POINTER(StepParams),
                                  C.POINTER(RowStats), vp]
 _lib.dg_sample_commit.argtypes = [vp, C.POINTER(CanvasState), C.POINTER(RowStats), C.POINTER(SamplerCfg),
-                                  C.c_int32, C.POINTER(KVCache), vp, vp]
+                                  C.c_int32, C.POINTER(C.c_int32), C.POINTER(KVCache), vp, vp]
 _lib.dg_commit_block.argtypes = [vp, vp, C.POINTER(KVCache), C.c_int32, vp]
 _lib.dg_debug_set_canvas_kv.argtypes = [vp, vp, vp, C.c_int32, vp]
 _lib.dg_timing_enable.argtypes = [vp, C.c_int32]
@@ -168,7 +170,9 @@ class KV:
             self.k.fill_(fill)
             self.v.fill_(fill)
         self.len = (C.c_int32 * batch)(*([0] * batch))
-        self.c = KVCache(_ptr(self.k), _ptr(self.v), cap, batch, C.cast(self.len, C.POINTER(C.c_int32)))
+        self.n_slots = batch
+        self.c = KVCache(_ptr(self.k), _ptr(self.v), cap, batch, C.cast(self.len, C.POINTER(C.c_int32)),
+                         C.POINTER(C.c_int32)(), batch)
 
     @property
     def lengths(self) -> List[int]:
@@ -177,6 +181,32 @@ class KV:
     def set_lengths(self, lens: Sequence[int]):
         for b, v in enumerate(lens):
             self.len[b] = int(v)
+
+    def view(self, slots: Optional[Sequence[int]]):
+        """The cache as seen by a call on the requests in `slots` (all slots when None)."""
+        return _KVView(self, slots)
+
+
+class _KVView:
+    """A dg_kv_cache for a call on some slots of a KV: its lengths are copied in, and back out
+    after the call (prefill and commit advance them)."""
+
+    def __init__(self, kv: "KV", slots: Optional[Sequence[int]]):
+        self.kv = kv
+        self.slots = None if slots is None else [int(x) for x in slots]
+        if self.slots is None:
+            self.c = kv.c
+            return
+        n = len(self.slots)
+        self._len = (C.c_int32 * n)(*[kv.len[x] for x in self.slots])
+        self._slot = (C.c_int32 * n)(*self.slots)
+        self.c = KVCache(kv.c.k, kv.c.v, kv.c.cap, n, C.cast(self._len, C.POINTER(C.c_int32)),
+                         C.cast(self._slot, C.POINTER(C.c_int32)), kv.n_slots)
+
+    def done(self):
+        if self.slots is not None:
+            for i, x in enumerate(self.slots):
+                self.kv.len[x] = self._len[i]
 
 
 class Canvas:
@@ -264,32 +294,49 @@ class Model:
             raise DGError(rc, _lib.dg_last_error(self.ctx).decode())
 
     # ---------------------------------------------------------------- entry points
-    def prefill(self, tokens: torch.Tensor, n_new: Sequence[int], kv: KV):
+    # `slots`: run the call on those slots of kv (and of the per-slot arrays) only; None = all.
+    def prefill(self, tokens: torch.Tensor, n_new: Sequence[int], kv: KV, slots=None):
         n = (C.c_int32 * len(n_new))(*[int(v) for v in n_new])
-        self._check(_lib.dg_prefill_causal(self.ctx, _ptr(tokens), n, len(n_new), C.byref(kv.c), _stream()))
+        view = kv.view(slots)
+        self._check(_lib.dg_prefill_causal(self.ctx, _ptr(tokens), n, len(n_new), C.byref(view.c), _stream()))
+        view.done()
 
-    def canvas_init(self, state: Canvas, kv: KV, cfg: SamplerCfg):
-        self._check(_lib.dg_canvas_init(self.ctx, C.byref(state.c), C.byref(kv.c), C.byref(cfg), _stream()))
+    def canvas_init(self, state: Canvas, kv: KV, cfg: SamplerCfg, slots=None):
+        view = kv.view(slots)
+        self._check(_lib.dg_canvas_init(self.ctx, C.byref(state.c), C.byref(view.c), C.byref(cfg), _stream()))
 
     def denoise_step(self, canvas: Optional[torch.Tensor], kv: KV, cfg: Optional[SamplerCfg], step: int,
                      out: Optional[Stats], flags: int = 0, hidden_in: Optional[torch.Tensor] = None,
-                     debug: Optional[Dict[str, torch.Tensor]] = None):
+                     debug: Optional[Dict[str, torch.Tensor]] = None, slots=None):
         dbg = None
         if debug:
             dbg = Debug(*[_ptr(debug.get(n)) for n, _ in Debug._fields_])
-        p = StepParams(int(step), int(flags), _ptr(hidden_in), C.pointer(dbg) if dbg is not None else None)
-        self._check(_lib.dg_denoise_step(self.ctx, _ptr(canvas), C.byref(kv.c),
+        steps_arr = None
+        if not isinstance(step, (int, np.integer)):  # one step per request of the call
+            steps_arr = (C.c_int32 * len(step))(*[int(x) for x in step])
+            step = 0
+        p = StepParams(int(step), int(flags), _ptr(hidden_in), C.pointer(dbg) if dbg is not None else None,
+                       C.cast(steps_arr, C.POINTER(C.c_int32)) if steps_arr is not None else None)
+        view = kv.view(slots)
+        self._check(_lib.dg_denoise_step(self.ctx, _ptr(canvas), C.byref(view.c),
                                          C.byref(cfg) if cfg is not None else None, C.byref(p),
                                          C.byref(out.c) if out is not None else None, _stream()))
 
     def sample_commit(self, state: Canvas, stats: Stats, cfg: SamplerCfg, step: int, kv: KV,
-                      status: torch.Tensor):
+                      status: torch.Tensor, slots=None):
+        view = kv.view(slots)
+        steps_arr = None
+        if not isinstance(step, (int, np.integer)):  # one step per request of the call
+            steps_arr = (C.c_int32 * len(step))(*[int(x) for x in step])
+            step = 0
         self._check(_lib.dg_sample_commit(self.ctx, C.byref(state.c), C.byref(stats.c), C.byref(cfg),
-                                          int(step), C.byref(kv.c), _ptr(status), _stream()))
+                                          int(step), steps_arr, C.byref(view.c), _ptr(status), _stream()))
 
-    def commit_block(self, canvas: torch.Tensor, kv: KV, refresh):
+    def commit_block(self, canvas: torch.Tensor, kv: KV, refresh, slots=None):
         """refresh: COMMIT_LAST (0 / False), COMMIT_REFRESH (1 / True) or COMMIT_CAUSAL (2)."""
-        self._check(_lib.dg_commit_block(self.ctx, _ptr(canvas), C.byref(kv.c), int(refresh), _stream()))
+        view = kv.view(slots)
+        self._check(_lib.dg_commit_block(self.ctx, _ptr(canvas), C.byref(view.c), int(refresh), _stream()))
+        view.done()
 
     def timing(self, enable: bool):
         self._check(_lib.dg_timing_enable(self.ctx, int(bool(enable))))

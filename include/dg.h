@@ -93,15 +93,22 @@ typedef struct {
   const dg_layer_weights* layers; /* (host) [n_layers]; copied by dg_create */
 } dg_weights;
 
-/* KV cache: bf16 K (after RoPE) and V, layout [n_layers][batch][n_kv_heads][cap][head_dim].
- * len (host) holds each request's committed length; dg_prefill_causal and dg_commit_block
- * advance it when they enqueue their work. */
+/* KV cache: bf16 K (after RoPE) and V, layout [n_layers][n_slots][n_kv_heads][cap][head_dim].
+ * A call works on `batch` requests; request b lives in slot slot[b] (slot NULL: slot b) of the
+ * cache and of every per-request array passed with it (canvas tokens, canvas state, row
+ * statistics, step status: all [n_slots][...]), and its random streams carry the slot, so a
+ * request draws the same numbers whichever other requests share the call.  This lets a
+ * scheduler run only the live requests of a larger pool (continuous batching).  len (host)
+ * holds the committed length of each request of the call; dg_prefill_causal and
+ * dg_commit_block advance it when they enqueue their work. */
 typedef struct {
   uint16_t* k;
   uint16_t* v;
   int32_t cap;
-  int32_t batch;
-  int32_t* len; /* (host) [batch] */
+  int32_t batch;          /* requests of this call, 1 <= batch <= max_batch */
+  int32_t* len;           /* (host) [batch] */
+  const int32_t* slot;    /* (host) [batch] distinct slots in [0, n_slots), or NULL */
+  int32_t n_slots;        /* slots in k/v and in the per-request arrays; 0 means batch */
 } dg_kv_cache;
 
 /* Sampler state of `batch` canvases ([NEWS] 2nd ¶: committed anchors; re-noising). */
@@ -176,6 +183,9 @@ typedef struct {
   uint32_t flags;        /* DG_STEP_* */
   const void* hidden_in; /* see flags */
   const dg_debug* debug; /* (host) optional, may be NULL */
+  const int32_t* steps;  /* (host) [batch] the step of each request (requests at different
+                            points of their canvases, continuous batching), or NULL: `step`
+                            for every request */
 } dg_step_params;
 
 /* Create a context for `desc` over caller-owned device weights.  The expert banks (w_gate,
@@ -235,14 +245,17 @@ int dg_denoise_step(dg_ctx* ctx, const int32_t* canvas, const dg_kv_cache* kv,
  * log-confidence fell below log(renoise_conf) (if renoise_committed); other uncommitted slots
  * take their candidate if its log-confidence >= log(renoise_conf), else a fresh uniform token
  * Philox(seed; 0, pos, step, (b<<8)|1).  Updates state and writes status[batch].  A request
- * whose `stopped` flag is already set is left unchanged (status: stop 1, changed 0). */
+ * whose `stopped` flag is already set is left unchanged (status: stop 1, changed 0).  steps:
+ * (host) [batch] per-request steps, or NULL for `step` everywhere. */
 int dg_sample_commit(dg_ctx* ctx, dg_canvas_state* state, const dg_row_stats* stats,
-                     const dg_sampler_cfg* cfg, int32_t step, const dg_kv_cache* kv,
-                     dg_step_status* status, hipStream_t stream);
+                     const dg_sampler_cfg* cfg, int32_t step, const int32_t* steps,
+                     const dg_kv_cache* kv, dg_step_status* status, hipStream_t stream);
 
 /* Append each finished canvas's K/V to the cache at [len[b], len[b]+canvas) and advance len
  * ([GUIDE] "Arquitetura em Detalhes"; [NEWS] 2nd ¶).  refresh selects where the K/V come from:
- *   DG_COMMIT_LAST (0): the ones the last dg_denoise_step computed (bidirectional canvas);
+ *   DG_COMMIT_LAST (0): the ones the last forward pass computed (bidirectional canvas),
+ *     found by slot: every slot of `kv` must have been a request of that pass, in any order,
+ *     else DG_ERR_ARG and nothing is written;
  *   DG_COMMIT_REFRESH (1): first re-run the layers (no head) on `canvas` ([batch][canvas]
  *     device int32), needed when the last sampler step changed the canvas;
  *   DG_COMMIT_CAUSAL (2): re-encode `canvas` causally, as a continuation of the prompt (each

@@ -74,7 +74,7 @@ def test_create_rejects_null_weights():
 def test_null_context_is_rejected():
     dg = pytest.importorskip("block_discrete_diffusion_amd.dg")
     assert dg._lib.dg_denoise_step(None, None, None, None, None, None, None) == -1
-    assert dg._lib.dg_sample_commit(None, None, None, None, 0, None, None, None) == -1
+    assert dg._lib.dg_sample_commit(None, None, None, None, 0, None, None, None, None) == -1
     assert dg._lib.dg_commit_block(None, None, None, 0, None) == -1
     assert dg._lib.dg_prefill_causal(None, None, None, 0, None, None) == -1
     assert dg._lib.dg_quantize_e4m3_rows(None, 4, 16, None, None, None) == -1

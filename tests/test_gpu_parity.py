@@ -391,3 +391,112 @@ def test_peaked_head_stops_after_three_steps(env):
         assert int(st.committed.sum()) == 48
     finally:
         m2.close()
+
+
+def _pool(dg, n_slots=4, cap=L + 600, seed=90):
+    kv = dg.KV(SHAPE, n_slots, cap)
+    k, v = random_cache(SHAPE, L + 300, cap, seed, n_slots)
+    load_cache(kv, k, v, [L, L + 300, L + 100, L + 7][:n_slots])
+    return kv
+
+
+def _run_slots(dg, m, kv, slots, cfg, steps=3):
+    """canvas init, a few denoise + sampler steps and a commit on `slots` of a 4-slot pool."""
+    st = dg.Canvas(kv.n_slots, 256)
+    stats = dg.Stats(kv.n_slots, 256)
+    status = torch.zeros((kv.n_slots, 8), dtype=torch.int32, device="cuda")
+    m.canvas_init(st, kv, cfg, slots=slots)
+    for s in range(steps):
+        m.denoise_step(st.tokens, kv, cfg, s, stats, slots=slots)
+        m.sample_commit(st, stats, cfg, s, kv, status, slots=slots)
+    m.commit_block(st.tokens, kv, dg.COMMIT_REFRESH, slots=slots)
+    torch.cuda.synchronize()
+    return st, stats, status
+
+
+def test_slot_mapped_calls_do_not_depend_on_call_order(env):
+    """Requests run on slots of a larger pool (continuous batching): every per-slot output -- canvas
+    state, row statistics, step status, the appended cache -- is bit-identical whether the call
+    lists the slots as [3, 1] or [1, 3], and slots outside the call are left untouched."""
+    dg, w, m = env
+    cfg = dg.sampler_cfg(seed=2718, renoise_committed=False)
+    kv_a, kv_b = _pool(dg), _pool(dg)
+    k0, v0 = kv_a.k.clone(), kv_a.v.clone()
+    a = _run_slots(dg, m, kv_a, [3, 1], cfg)
+    b = _run_slots(dg, m, kv_b, [1, 3], cfg)
+    assert kv_a.lengths == kv_b.lengths == [L, L + 300 + 256, L + 100, L + 7 + 256]
+    for x in (1, 3):
+        assert torch.equal(a[0].tokens[x], b[0].tokens[x]) and torch.equal(a[0].committed[x], b[0].committed[x])
+        for k in ("cand", "t_cand", "t_cur", "lse", "entropy"):
+            assert torch.equal(getattr(a[1], k)[x], getattr(b[1], k)[x]), k
+        assert torch.equal(a[2][x], b[2][x])
+    assert torch.equal(kv_a.k, kv_b.k) and torch.equal(kv_a.v, kv_b.v)
+    for x in (0, 2):  # not in the call
+        assert torch.equal(kv_a.k[:, x], k0[:, x]) and torch.equal(kv_a.v[:, x], v0[:, x])
+        assert not a[0].tokens[x].any()
+
+
+def test_commit_last_finds_each_slot_in_the_last_forward(env):
+    """COMMIT_LAST takes each slot's canvas K/V from wherever the last forward pass held it: after
+    a pass over slots [3, 1], committing [1] and then [3] (separately, the other way round) writes
+    the same cache as committing [3, 1] at once, and a slot the pass did not cover is refused
+    without writing anything."""
+    dg, w, m = env
+    cfg = dg.sampler_cfg(seed=4242)
+    kv_a, kv_b = _pool(dg), _pool(dg)
+    st = dg.Canvas(4, 256)
+    stats = dg.Stats(4, 256)
+    m.canvas_init(st, kv_a, cfg, slots=[3, 1])
+    for kv in (kv_a, kv_b):
+        m.denoise_step(st.tokens, kv, cfg, 0, stats, slots=[3, 1])
+        if kv is kv_a:
+            m.commit_block(st.tokens, kv, dg.COMMIT_LAST, slots=[3, 1])
+        else:
+            k0, v0, n0 = kv.k.clone(), kv.v.clone(), kv.lengths
+            with pytest.raises(dg.DGError):
+                m.commit_block(st.tokens, kv, dg.COMMIT_LAST, slots=[0])
+            torch.cuda.synchronize()
+            assert kv.lengths == n0 and torch.equal(kv.k, k0) and torch.equal(kv.v, v0)
+            m.commit_block(st.tokens, kv, dg.COMMIT_LAST, slots=[1])
+            m.commit_block(st.tokens, kv, dg.COMMIT_LAST, slots=[3])
+    torch.cuda.synchronize()
+    assert kv_a.lengths == kv_b.lengths == [L, L + 300 + 256, L + 100, L + 7 + 256]
+    assert torch.equal(kv_a.k, kv_b.k) and torch.equal(kv_a.v, kv_b.v)
+
+
+def test_slot_mapped_streams_follow_the_slot(env):
+    """A request's random streams are keyed by its slot: canvas init on slots [2, 0] equals the
+    oracle's draws for requests 2 and 0, and the sampler on identical statistics is bit-exact
+    against the oracle run with b = slot."""
+    dg, w, m = env
+    kv = _pool(dg)
+    cfg = dg.sampler_cfg(seed=31415, max_steps=6)
+    oc = oracle_cfg(cfg)
+    st = dg.Canvas(4, 256)
+    m.canvas_init(st, kv, cfg, slots=[2, 0])
+    torch.cuda.synchronize()
+    lens = kv.lengths
+    o_state = {}
+    for x in (2, 0):
+        want = osampler.canvas_init(cfg.seed, x, lens[x] + np.arange(256), SHAPE.vocab)
+        assert np.array_equal(st.tokens[x].cpu().numpy(), want)
+        o_state[x] = [want, np.zeros(256, bool), 0]
+    stats = dg.Stats(4, 256)
+    status = torch.zeros((4, 8), dtype=torch.int32, device="cuda")
+    for s in range(cfg.max_steps):
+        rs = {"cand": synth.tokens(1024, SHAPE.vocab, s, 11).reshape(4, 256),
+              "t_cand": synth.uniform((4, 256), -4.0, 0.5, s, 12), "t_cur": synth.uniform((4, 256), -4.0, 0.5, s, 13),
+              "lse": synth.uniform((4, 256), 0.0, 0.5, s, 14), "entropy": synth.uniform((4, 256), 0.0, 3.0, s, 15)}
+        for k, v in rs.items():
+            getattr(stats, k).copy_(torch.from_numpy(np.ascontiguousarray(v)))
+        m.sample_commit(st, stats, cfg, s, kv, status, slots=[2, 0])
+        torch.cuda.synchronize()
+        got = dg.status_dict(status)
+        for x in (2, 0):
+            x_o, com, sr, ost = osampler.sample_commit({k: rs[k][x] for k in rs}, *o_state[x], oc, s, x,
+                                                       lens[x] + np.arange(256), SHAPE.vocab)
+            o_state[x] = [x_o, com, sr]
+            assert np.array_equal(st.tokens[x].cpu().numpy(), x_o), (s, x)
+            assert np.array_equal(st.committed[x].cpu().numpy().astype(bool), com), (s, x)
+            for k in ("changed", "n_committed", "n_new", "n_renoised", "stable_run", "stop"):
+                assert got[x][k] == ost[k], (s, x, k)
