@@ -245,8 +245,9 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   at.n_extra = prefill ? 0 : m.canvas;
   at.causal = prefill ? 1 : 0;
   at.scale = 1.0f / std::sqrt(static_cast<float>(D));
-  const int tasks = (Hq / Hkv) * ((rows_per_req + 31) / 32);
-  at.n_waves = attention_waves(max_keys);
+  at.q_tiles = attention_q_tiles(max_keys, prefill);
+  const int tasks = (Hq / Hkv) * ((rows_per_req + 16 * at.q_tiles - 1) / (16 * at.q_tiles));
+  at.n_waves = attention_waves(max_keys, prefill);
   const int base = ((tasks + at.n_waves - 1) / at.n_waves) * n_req * Hkv;
   at.n_split = choose_split(c, base, max_keys, rows, at.n_waves);
   at.split_keys = (((max_keys + at.n_split - 1) / at.n_split + 63) / 64) * 64;

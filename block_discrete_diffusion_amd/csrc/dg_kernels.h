@@ -114,10 +114,15 @@ struct AttnArgs {
   int n_split; int split_keys;  // split-KV: each split covers split_keys keys
   float* part_o; float* part_ml;  // partials when n_split > 1
   int n_waves;                    // query tasks per work-group: 4 or 8 (attention_waves)
+  int q_tiles;                    // 16-row query tiles per wave task: 1 or 2 (0 means 2)
 };
-// Waves per work-group for a key range of max_keys: 8 for long ranges (each staged block serves
-// twice the queries), else 4.
-int attention_waves(int max_keys);
+// Work-group shape for a key range of max_keys.  Waves: 8 from 2048 keys on the canvas path
+// and from 8192 in the causal prefill (each staged block serves more queries), else 4.  Query tiles per wave: 2 (32 rows) for long ranges and the
+// causal prefill, where each K fragment read from LDS then feeds two MFMAs; 1 (16 rows) for a
+// canvas over a prefix under 8192 keys, where the doubled task count lets a shorter split fill
+// the chip (fewer split partials to write and merge) at fewer registers per wave.
+int attention_waves(int max_keys, bool causal);
+int attention_q_tiles(int max_keys, bool causal);
 void launch_attention(const AttnArgs& a, hipStream_t s);
 
 // ---- k_moe.hip

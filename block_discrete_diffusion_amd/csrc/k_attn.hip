@@ -1,9 +1,9 @@
 // Canvas attention (bidirectional, no mask) and causal prefill attention on MFMA, plus the
 // RoPE/scatter step that turns the QKV projection into rotated bf16 Q and K/V rows.
 //
-// Each work-group serves one (request, KV head) and four or eight (query head, 32-row) tasks of
-// that head's query group, one per wave, so every K/V tile staged in LDS is reused by all of
-// them (GQA).
+// Each work-group serves one (request, KV head) and four or eight (query head, 16- or 32-row)
+// tasks of that head's query group, one per wave, so every K/V tile staged in LDS is reused by
+// all of them (GQA).
 // Keys are the request's cached prefix followed by the canvas keys; the key range can be split
 // across work-groups (split-KV) so that a 256-row canvas still fills the chip; the splits are
 // merged in a fixed order afterwards (deterministic).
@@ -137,7 +137,7 @@ struct AttnSmem {
 // waves per SIMD: with 4 waves two work-groups share a CU (one group's MFMAs overlap the other's
 // softmax and staging), with 8 waves each block is staged once for twice the queries (less
 // staging per MFMA, used for long key ranges).
-template <int D, int NW>
+template <int D, int NW, int QT>  // QT: 16-row query tiles per wave (1 or 2)
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_kernel(AttnArgs a) {
   constexpr int NT = 64 * NW;
@@ -152,12 +152,13 @@ void attention_kernel(AttnArgs a) {
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int group = a.Hq / a.Hkv;
   const int rows = a.rows_per_req;
-  const int n_rb = (rows + 31) / 32;
+  constexpr int RW = 16 * QT;  // query rows per wave task
+  const int n_rb = (rows + RW - 1) / RW;
   const int task = blockIdx.x * NW + wave;
   const bool active = task < group * n_rb;
   const int hq = g * group + (active ? task % group : 0);
   const int rb = active ? task / group : 0;
-  const int row0 = rb * 32;  // first query row (within the request) of this wave
+  const int row0 = rb * RW;  // first query row (within the request) of this wave
 
   const int n_cache = a.n_cache[b];
   const int n_keys = n_cache + a.n_extra;
@@ -166,15 +167,15 @@ void attention_kernel(AttnArgs a) {
   int k_hi = min(n_keys, k_lo + a.split_keys);
   if (a.causal) {
     const int last_task = min(blockIdx.x * NW + NW - 1, group * n_rb - 1);
-    const int last_row = min(rows - 1, (last_task / group) * 32 + 31);
+    const int last_row = min(rows - 1, (last_task / group) * RW + RW - 1);
     k_hi = min(k_hi, a.q_pos0[b] + last_row + 1);
   }
   const long qrow_base = static_cast<long>(b) * rows;
 
   // queries (B operand): lane holds Q[qt*16 + l16][ks*32 + 8*j4 .. +8]
-  u32x4_t qf[2][NKS];
+  u32x4_t qf[QT][NKS];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int qr = row0 + qt * 16 + l16;
     const bool ok = active && qr < rows;
     const uint16_t* qp = a.q + (qrow_base + qr) * a.Hq * D + hq * D;
@@ -182,21 +183,26 @@ void attention_kernel(AttnArgs a) {
     for (int ks = 0; ks < NKS; ++ks)
       qf[qt][ks] = ok ? ld16(qp + ks * 32 + 8 * j4) : u32x4_t{0u, 0u, 0u, 0u};
   }
-  int qpos[2];
+  int qpos[QT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) qpos[qt] = a.q_pos0[b] + row0 + qt * 16 + l16;
+  for (int qt = 0; qt < QT; ++qt) qpos[qt] = a.q_pos0[b] + row0 + qt * 16 + l16;
   const int qmin = a.q_pos0[b] + row0;  // smallest query position of this wave
 
-  floatx4_t o[NDT][2];
+  floatx4_t o[NDT][QT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < QT; ++qt) o[dt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   // running max (in log2 units, scale folded in) per query; the running sum of P is one more
   // MFMA per step with an all-ones A operand (every row of that tile is the column sum of P^T,
   // i.e. this lane's query sum over the step's keys, of the same bf16 P that multiplies V)
-  float m_run[2] = {-INFINITY, -INFINITY};
-  floatx4_t l_acc[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
+  float m_run[QT];
+  floatx4_t l_acc[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_acc[qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
   const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const float sl2 = a.scale * 1.4426950408889634f;
 
@@ -205,28 +211,28 @@ void attention_kernel(AttnArgs a) {
   u32x4_t rk[KCH], rv[KCH];
 
   // S^T of one 64-key block for both query tiles (raw dot products)
-  auto qk = [&](floatx4_t (&sc)[4][2]) {
+  auto qk = [&](floatx4_t (&sc)[4][QT]) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) sc[kt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < QT; ++qt) sc[kt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const u32x4_t kf = ld16(&sm.k[kt * 16 + l16][ks * 32 + 8 * j4]);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) sc[kt][qt] = mfma16(kf, qf[qt][ks], sc[kt][qt]);
+        for (int qt = 0; qt < QT; ++qt) sc[kt][qt] = mfma16(kf, qf[qt][ks], sc[kt][qt]);
       }
     }
   };
   // online softmax per lane (= per query), in place: p = 2^(s*sl2 - m), one FMA + one exp each;
   // returns whether some lane's running max moved (O^T and the sum then need rescaling)
-  auto softmax = [&](floatx4_t (&sc)[4][2], int kb0, int kb_hi, float (&alpha)[2]) {
+  auto softmax = [&](floatx4_t (&sc)[4][QT], int kb0, int kb_hi, float (&alpha)[QT]) {
     // mask only blocks that cross the range end or the causal diagonal (uniform branch)
     if ((kb0 + KB > kb_hi) || (a.causal && kb0 + KB - 1 > qmin)) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -237,7 +243,7 @@ void attention_kernel(AttnArgs a) {
     }
     bool rescale = false;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -257,22 +263,22 @@ void attention_kernel(AttnArgs a) {
   };
   // P as the bf16 B operand of the two 32-key MFMA steps: lane holds the 8 keys
   // {4 j4 .. 4 j4 + 3} of two 16-key sub-blocks for its query
-  auto pack_p = [&](const floatx4_t (&sc)[4][2], u32x4_t (&pf)[2][2]) {
+  auto pack_p = [&](const floatx4_t (&sc)[4][QT], u32x4_t (&pf)[2][QT]) {
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         const floatx4_t p0 = sc[2 * kk2][qt], p1 = sc[2 * kk2 + 1][qt];
         pf[kk2][qt] = u32x4_t{pack_bf2(p0[0], p0[1]), pack_bf2(p0[2], p0[3]), pack_bf2(p1[0], p1[1]),
                               pack_bf2(p1[2], p1[3])};
       }
   };
   // O^T = alpha O^T + V^T P^T over two 32-key steps (and the sum of P alongside)
-  auto pv = [&](const u32x4_t (&pf)[2][2], bool rescale, const float (&alpha)[2]) {
+  auto pv = [&](const u32x4_t (&pf)[2][QT], bool rescale, const float (&alpha)[QT]) {
     // rescaling by alpha == 1 is exact, so it is skipped when no lane of the wave needs it
     if (__any(rescale)) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha[qt];
         l_acc[qt] *= alpha[qt];
@@ -289,10 +295,10 @@ void attention_kernel(AttnArgs a) {
         const u32x2_t hi = read_tr16(&sm.v[kr + 16][dc]);
         const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma16(vf, pf[kk2][qt], o[dt][qt]);
+        for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16(vf, pf[kk2][qt], o[dt][qt]);
       }
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) l_acc[qt] = mfma16(ones, pf[kk2][qt], l_acc[qt]);
+      for (int qt = 0; qt < QT; ++qt) l_acc[qt] = mfma16(ones, pf[kk2][qt], l_acc[qt]);
     }
   };
 
@@ -335,9 +341,9 @@ void attention_kernel(AttnArgs a) {
       gload(blk + 1 < n_blk ? kb0 + KB : kb0);  // unconditional: exact wait counts
       sched_fence();
       if (!active) continue;
-      floatx4_t sc[4][2];
-      u32x4_t pf[2][2];
-      float alpha[2];
+      floatx4_t sc[4][QT];
+      u32x4_t pf[2][QT];
+      float alpha[QT];
       qk(sc);
       const bool rescale = softmax(sc, kb0, kb_hi, alpha);
       pack_p(sc, pf);
@@ -350,10 +356,12 @@ void attention_kernel(AttnArgs a) {
     run_range(a.kx + kx_head * a.xcap * D, a.vx + kx_head * a.xcap * D, n_cache, max(k_lo, n_cache), k_hi);
 
   if (!active) return;
-  const float l_run[2] = {l_acc[0][0], l_acc[1][0]};
+  float l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) l_run[qt] = l_acc[qt][0];
   // write: lane owns query qt*16+l16, dims dt*16 + 4*j4 + i; partial maxima are in log2 units
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int qr = row0 + qt * 16 + l16;
     if (qr >= rows) continue;
     const long orow = qrow_base + qr;
@@ -422,9 +430,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 template <int D, int NW>
 void launch_attn_w(const AttnArgs& a, hipStream_t s) {
   const int group = a.Hq / a.Hkv;
-  const int tasks = group * ((a.rows_per_req + 31) / 32);
+  const int qt = a.q_tiles == 1 ? 1 : 2;
+  const int tasks = group * ((a.rows_per_req + 16 * qt - 1) / (16 * qt));
   dim3 grid((tasks + NW - 1) / NW, a.n_split, a.n_req * a.Hkv);
-  hipLaunchKernelGGL((attention_kernel<D, NW>), grid, dim3(64 * NW), 0, s, a);
+  if (qt == 1) hipLaunchKernelGGL((attention_kernel<D, NW, 1>), grid, dim3(64 * NW), 0, s, a);
+  else hipLaunchKernelGGL((attention_kernel<D, NW, 2>), grid, dim3(64 * NW), 0, s, a);
 }
 
 template <int D>
@@ -441,7 +451,8 @@ void launch_attn_d(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int attention_waves(int max_keys) { return max_keys >= 8192 ? 8 : 4; }
+int attention_waves(int max_keys, bool causal) { return max_keys >= (causal ? 8192 : 2048) ? 8 : 4; }
+int attention_q_tiles(int max_keys, bool causal) { return (!causal && max_keys < 8192) ? 1 : 2; }
 
 void launch_rope_table(const RowMap& map, int rows, int D, float theta, float* table, hipStream_t s) {
   const long n = static_cast<long>(rows) * (D / 2);

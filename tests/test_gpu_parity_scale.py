@@ -38,8 +38,9 @@ def full_env():
 @pytest.mark.parametrize("prefix", [2048, 4096, 777, 8192])
 def test_full_shape_layer_with_shared_ffn(full_env, prefix):
     """One layer at the full shape with the shared FFN: attention over `prefix` cached keys plus
-    the canvas, routed experts, shared FFN; all 256 rows against the oracle.  8192 cached keys
-    take the long-range attention variant (8 waves per staged block)."""
+    the canvas, routed experts, shared FFN; all 256 rows against the oracle.  The prefixes take
+    every canvas attention shape: 16-row tasks with 4 waves (777) or 8 waves (2048, 4096), and
+    the long-range variant with 32-row tasks (8192)."""
     dg, w, m, host = full_env
     check_layer(dg, m, host, FULL1, prefix, SEED + prefix, prefix + 256)
 
