@@ -58,7 +58,6 @@ struct dg_ctx {
   // workspace
   float* h = nullptr;          // [r_max][d]
   uint16_t* a = nullptr;       // [r_max][d]
-  float* qkv = nullptr;        // [r_max][(Hq+2Hkv)D]
   uint16_t* q = nullptr;       // [r_max][Hq D]
   uint16_t* attn = nullptr;    // [r_max][Hq D]
   float* part_o = nullptr;     // [part_cap][D]
@@ -79,6 +78,7 @@ struct dg_ctx {
   std::vector<int32_t> last_slots;  // slots of the requests whose canvas K/V the workspace holds
   uint16_t* ck = nullptr;      // [L][max_batch][Hkv][C][D]
   uint16_t* cv = nullptr;
+  std::vector<uint16_t*> wqkv;  // per layer: QKV weight in rotation-pair row order
   std::vector<uint16_t*> pk1;  // per layer: packed gate/up expert weights
   std::vector<uint16_t*> pk2;  // per layer: packed down expert weights
   // E4M3 experts (desc.expert_fp8): packed bytes and per-channel scales [E][N] per matrix
@@ -205,20 +205,13 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   const int nqkv = (Hq + 2 * Hkv) * D;
   const RowMap map = make_map(rows_per_req, n_req, len);
 
-  // c->a holds this layer's normed input (written by the embedding or the previous combine)
+  // c->a holds this layer's normed input (written by the embedding or the previous combine).
+  // QKV projection with RoPE and the scatter of Q, K, V fused into its epilogue.
   GemmArgs g{};
-  g.part = c->gpart;
   g.x = c->a; g.ldx = d; g.n_tok = rows;
-  g.seg_w[0] = lw.wq; g.seg_w[1] = lw.wk; g.seg_w[2] = lw.wv;
-  g.seg_start[0] = 0; g.seg_start[1] = Hq * D; g.seg_start[2] = (Hq + Hkv) * D; g.seg_start[3] = nqkv;
-  g.n_seg = 3; g.K = d; g.N = nqkv; g.out_f32 = c->qkv; g.ldo = nqkv;
-  g.split = gemm_split(g, EPI_STORE_F32, kGemmPartFloats);
-  g.part_stride = static_cast<long>(rows) * nqkv;
-  timed(c, "gemm_qkv", s, [&] { launch_gemm(g, EPI_STORE_F32, s); });
-
-  RopeArgs ra{};
-  ra.qkv = g.split > 1 ? c->gpart : c->qkv; ra.rows = rows; ra.Hq = Hq; ra.Hkv = Hkv; ra.D = D;
-  ra.n_part = g.split; ra.part_stride = g.part_stride;
+  g.w0 = c->wqkv[l]; g.K = d; g.N = nqkv; g.split = 1;
+  RopeArgs& ra = g.rope;
+  ra.Hq = Hq; ra.Hkv = Hkv; ra.D = D;
   ra.table = m.rope_theta != 0.f ? c->rope : nullptr;  // filled by the caller for these rows
   ra.q = c->q; ra.map = map;
   const long ck_layer = static_cast<long>(l) * c->max_batch * Hkv * m.canvas * D;
@@ -229,7 +222,7 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
     ra.k_dst = c->ck + ck_layer; ra.v_dst = c->cv + ck_layer; ra.kv_cap = m.canvas;
     for (int b = 0; b < n_req; ++b) ra.slot0[b] = 0;
   }
-  timed(c, "rope_scatter", s, [&] { launch_rope_scatter(ra, s); });
+  timed(c, "gemm_qkv_rope", s, [&] { launch_gemm(g, EPI_ROPE_QKV, s); });
 
   AttnArgs at{};
   at.q = c->q; at.out = c->attn; at.kc = kc_l; at.vc = vc_l; at.cap = cap;
@@ -394,7 +387,7 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
   const long R = c->r_max, d = m.d_model, HD = m.n_q_heads * m.head_dim;
   const long nqkv = (m.n_q_heads + 2L * m.n_kv_heads) * m.head_dim;
   const long ckv = static_cast<long>(m.n_layers) * max_batch * m.n_kv_heads * m.canvas * m.head_dim;
-  bool ok = c->alloc(&c->h, R * d) && c->alloc(&c->a, R * d) && c->alloc(&c->qkv, R * nqkv) &&
+  bool ok = c->alloc(&c->h, R * d) && c->alloc(&c->a, R * d) && 
             c->alloc(&c->q, R * HD) && c->alloc(&c->attn, R * HD) &&
             c->alloc(&c->part_o, static_cast<long>(c->part_cap) * m.head_dim) &&
             c->alloc(&c->part_ml, static_cast<long>(c->part_cap) * 2) &&
@@ -446,6 +439,14 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
       const dg_layer_weights& lw = c->layers[l];
       launch_moe_pack(lw.w_gate, lw.w_up, c->pk1[l], E, F, m.d_model, kGroupTiles1, nullptr);
       launch_moe_pack(lw.w_down, nullptr, c->pk2[l], E, m.d_model, F, kGroupTiles2, nullptr);
+    }
+  }
+  c->wqkv.assign(m.n_layers, nullptr);
+  for (int l = 0; ok && l < m.n_layers; ++l) {
+    ok = c->alloc(&c->wqkv[l], static_cast<long>(nqkv) * m.d_model);
+    if (ok) {
+      const dg_layer_weights& lw = c->layers[l];
+      launch_pack_qkv(lw.wq, lw.wk, lw.wv, c->wqkv[l], m.n_q_heads, m.n_kv_heads, m.head_dim, m.d_model, nullptr);
     }
   }
   if (ok) ok = hipDeviceSynchronize() == hipSuccess && hipGetLastError() == hipSuccess;

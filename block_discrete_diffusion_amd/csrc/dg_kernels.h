@@ -37,8 +37,21 @@ void launch_norm_router(float* h, const float* part, int n_part, long part_strid
                         int n_exp, int top_k, uint16_t* b_out, int32_t* idx, float* gates,
                         hipStream_t s);
 
+// Destination of the fused QKV projection (EPI_ROPE_QKV): q heads and k heads rotated with
+// the table (rotate-half; null table = no rotation), q -> q [rows][Hq*D] bf16, k / v ->
+// k_dst / v_dst + ((b*Hkv + g)*kv_cap + slot0[b] + i)*D bf16 for row i of request b.
+struct RopeArgs {
+  int Hq; int Hkv; int D;
+  const float* table;
+  uint16_t* q; uint16_t* k_dst; uint16_t* v_dst; int kv_cap;  // per-layer base
+  RowMap map; int32_t slot0[kMaxBatch];
+};
+
 // ---- k_gemm.hip : C[t][f] = sum_k X[t][k] * W[f][k]
-enum GemmEpi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU_BF16 = 2, EPI_STORE_BF16 = 3 };
+// EPI_ROPE_QKV: W is the QKV weight with the rows of every q and k head in the order
+// {j, j + D/2, j + 1, j + 1 + D/2} for j = 0, 2, 4, ... (launch_pack_qkv), so the four
+// consecutive outputs a lane holds are two rotation pairs; the products go through RopeArgs.
+enum GemmEpi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU_BF16 = 2, EPI_STORE_BF16 = 3, EPI_ROPE_QKV = 4 };
 struct GemmArgs {
   const uint16_t* x; int ldx; int n_tok;
   const uint16_t* w0; const uint16_t* w1;  // w1: up matrix for SwiGLU
@@ -50,7 +63,12 @@ struct GemmArgs {
   // fp32 product to part + z * part_stride (+ part_stride / 2 for the up matrix of the SwiGLU
   // pair), row-major [n_tok][N]; the consumer sums the slices in z order.
   int split; float* part; long part_stride;
+  RopeArgs rope;  // EPI_ROPE_QKV only (split 1)
 };
+// QKV weight for EPI_ROPE_QKV: rows of wq (Hq heads) then wk (Hkv heads) in the rotation-pair
+// order above, then wv unchanged; out [(Hq+2Hkv)*D][d] bf16.
+void launch_pack_qkv(const uint16_t* wq, const uint16_t* wk, const uint16_t* wv, uint16_t* out,
+                     int Hq, int Hkv, int D, int d, hipStream_t s);
 // Largest split (1, 2 or 4) that keeps >= 16 k-tiles of 64 per slice and stays within `cap`
 // partial floats while the grid stays within ~512 work-groups.
 int gemm_split(const GemmArgs& a, int epi, long cap);
@@ -86,17 +104,7 @@ constexpr int kMaxParts = 4;  // largest split-K slice count a consumer sums
 // and rounded to float32: table[r][j] = {cos, sin}.  Built once per step (all layers share it).
 void launch_rope_table(const RowMap& map, int rows, int D, float theta, float* table, hipStream_t s);
 
-// qkv holds n_part split-K slices (row-major [rows][(Hq+2Hkv)*D], part_stride apart) summed in
-// order; q heads and k heads are rotated with the table (rotate-half), q -> q [rows][Hq*D] bf16,
-// k / v -> kv_dst + ((b*Hkv + g)*kv_cap + slot0[b] + i)*D bf16.
-struct RopeArgs {
-  const float* qkv; int rows; int Hq; int Hkv; int D;
-  int n_part; long part_stride;
-  const float* table;  // null = no rotation
-  uint16_t* q; uint16_t* k_dst; uint16_t* v_dst; int kv_cap;  // per-layer base
-  RowMap map; int32_t slot0[kMaxBatch];
-};
-void launch_rope_scatter(const RopeArgs& a, hipStream_t s);
+
 
 struct AttnArgs {
   const uint16_t* q;       // [rows][Hq*D]

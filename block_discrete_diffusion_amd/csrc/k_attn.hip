@@ -1,5 +1,5 @@
 // Canvas attention (bidirectional, no mask) and causal prefill attention on MFMA, plus the
-// RoPE/scatter step that turns the QKV projection into rotated bf16 Q and K/V rows.
+// RoPE angle table (the rotation itself is applied in the QKV projection's epilogue).
 //
 // Each work-group serves one (request, KV head) and four or eight (query head, 16- or 32-row)
 // tasks of that head's query group, one per wave, so every K/V tile staged in LDS is reused by
@@ -38,60 +38,6 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RowMap map, int rows, i
   sincos(pos * pow(static_cast<double>(theta), -2.0 * j / D), &sn, &cs);
   table[2 * i] = static_cast<float>(cs);
   table[2 * i + 1] = static_cast<float>(sn);
-}
-
-// One thread per (row, item): items [0, (Hq+Hkv)*D/2) are rotation pairs (head h, j), the rest
-// are pairs of V elements.  Split-K slices are summed with all loads issued up front.
-__global__ __launch_bounds__(256) void rope_scatter_kernel(RopeArgs a) {
-  const int r = blockIdx.y;
-  const int D = a.D, half = D / 2;
-  const int n_rot = (a.Hq + a.Hkv) * half, n_items = n_rot + a.Hkv * half;
-  const int it = blockIdx.x * 256 + threadIdx.x;
-  if (it >= n_items) return;
-  const int b = r / a.map.rows_per_req, i = r - b * a.map.rows_per_req;
-  const long slot = a.slot0[b] + i;
-  const float* row = a.qkv + static_cast<long>(r) * (a.Hq + 2 * a.Hkv) * D;
-  int o1, o2;  // element offsets within the row
-  if (it < n_rot) {
-    const int h = it / half, j = it - h * half;
-    o1 = h * D + j;
-    o2 = o1 + half;
-  } else {
-    const int e = (it - n_rot) * 2;  // V element pair
-    o1 = (a.Hq + a.Hkv) * D + e;
-    o2 = o1 + 1;
-  }
-  float x1[kMaxParts], x2[kMaxParts];
-#pragma unroll
-  for (int z = 0; z < kMaxParts; ++z) {
-    if (z < a.n_part) {
-      x1[z] = row[z * a.part_stride + o1];
-      x2[z] = row[z * a.part_stride + o2];
-    }
-  }
-  float v1 = 0.f, v2 = 0.f;
-#pragma unroll
-  for (int z = 0; z < kMaxParts; ++z)
-    if (z < a.n_part) { v1 += x1[z]; v2 += x2[z]; }
-  if (it < n_rot) {
-    const int h = it / half, j = it - h * half;
-    float y1 = v1, y2 = v2;
-    if (a.table) {
-      const float cs = a.table[(static_cast<long>(r) * half + j) * 2];
-      const float sn = a.table[(static_cast<long>(r) * half + j) * 2 + 1];
-      y1 = v1 * cs - v2 * sn;
-      y2 = v2 * cs + v1 * sn;
-    }
-    uint16_t* dst = (h < a.Hq)
-        ? a.q + static_cast<long>(r) * a.Hq * D + h * D
-        : a.k_dst + ((static_cast<long>(b) * a.Hkv + (h - a.Hq)) * a.kv_cap + slot) * D;
-    dst[j] = f2bf(y1);
-    dst[j + half] = f2bf(y2);
-  } else {
-    const int e = (it - n_rot) * 2, g = e / D, dd = e - g * D;
-    *reinterpret_cast<uint32_t*>(a.v_dst + ((static_cast<long>(b) * a.Hkv + g) * a.kv_cap + slot) * D + dd) =
-        pack_bf2(v1, v2);
-  }
 }
 
 // ---------------------------------------------------------------------------- attention
@@ -457,11 +403,6 @@ int attention_q_tiles(int max_keys, bool causal) { return (!causal && max_keys <
 void launch_rope_table(const RowMap& map, int rows, int D, float theta, float* table, hipStream_t s) {
   const long n = static_cast<long>(rows) * (D / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, map, rows, D, theta, table);
-}
-
-void launch_rope_scatter(const RopeArgs& a, hipStream_t s) {
-  const int n_items = (a.Hq + 2 * a.Hkv) * (a.D / 2);
-  hipLaunchKernelGGL(rope_scatter_kernel, dim3((n_items + 255) / 256, a.rows), dim3(256), 0, s, a);
 }
 
 void launch_attention(const AttnArgs& a, hipStream_t s) {

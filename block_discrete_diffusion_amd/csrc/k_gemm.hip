@@ -1,5 +1,6 @@
-// Dense projections on MFMA (QKV, O-proj + residual, shared SwiGLU FFN) and the fused vocab
-// head (projection + temperature + log-sum-exp + entropy + Gumbel-max; logits stay on chip).
+// Dense projections on MFMA (QKV with RoPE and the K/V scatter fused into its epilogue, O-proj
+// + residual, shared SwiGLU FFN) and the fused vocab head (projection + temperature +
+// log-sum-exp + entropy + Gumbel-max; logits stay on chip).
 //
 // C[t][f] = sum_k X[t][k] * W[f][k]: both operands are k-contiguous ("NT"), which is the
 // natural MFMA operand layout.  The weight tile is the A operand (rows = output features) and
@@ -143,6 +144,35 @@ struct Mainloop {
   }
 };
 
+// Fused QKV epilogue: the lane's four consecutive outputs f..f+3 of token t.  For q and k heads
+// they are the rotation pairs (j, j + D/2) and (j + 1, j + 1 + D/2) of one head (packed weight
+// row order), rotated with the table entries of (t, j) and (t, j + 1) (one 16-byte load) and
+// stored as two bf16 pairs; for v heads they are four consecutive elements of one row.
+DG_DEVICE void rope_store(const RopeArgs& r, int t, int f, const floatx4_t& v) {
+  const int D = r.D, qk = (r.Hq + r.Hkv) * D;
+  const int b = t / r.map.rows_per_req, i = t - b * r.map.rows_per_req;
+  if (f < qk) {
+    const int h = f / D, j = ((f - h * D) >> 2) * 2;
+    float y0 = v[0], y1 = v[1], y2 = v[2], y3 = v[3];
+    if (r.table) {
+      const floatx4_t cs = *reinterpret_cast<const floatx4_t*>(r.table + (static_cast<long>(t) * (D / 2) + j) * 2);
+      y0 = v[0] * cs[0] - v[1] * cs[1];
+      y1 = v[1] * cs[0] + v[0] * cs[1];
+      y2 = v[2] * cs[2] - v[3] * cs[3];
+      y3 = v[3] * cs[2] + v[2] * cs[3];
+    }
+    uint16_t* dst = (h < r.Hq)
+        ? r.q + static_cast<long>(t) * r.Hq * D + h * D
+        : r.k_dst + ((static_cast<long>(b) * r.Hkv + (h - r.Hq)) * r.kv_cap + r.slot0[b] + i) * D;
+    *reinterpret_cast<uint32_t*>(dst + j) = pack_bf2(y0, y2);
+    *reinterpret_cast<uint32_t*>(dst + j + D / 2) = pack_bf2(y1, y3);
+  } else {
+    const int p = f - qk, g = p / D, dd = p - g * D;
+    *reinterpret_cast<u32x2_t*>(r.v_dst + ((static_cast<long>(b) * r.Hkv + g) * r.kv_cap + r.slot0[b] + i) * D + dd) =
+        u32x2_t{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+  }
+}
+
 // Split-K: grid = tiles x S.  With S > 1 work-group (tile, z) multiplies the z-th K / S slice
 // and stores the raw fp32 product to its own slice of the partial buffer; the consuming kernel
 // adds the S slices in z order (a kernel boundary is the only synchronisation).
@@ -192,6 +222,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, int S) {
         floatx4_t o = *p;
         o += v;
         *p = o;
+      } else if constexpr (EPI == EPI_ROPE_QKV) {
+        rope_store(a.rope, t, f, v);
       } else if constexpr (EPI == EPI_SWIGLU_BF16) {
         const floatx4_t u = ml.acc1[DUAL ? fm : 0][DUAL ? tn : 0];
         float y[4];
@@ -451,6 +483,7 @@ int split_for(const GemmArgs& a, long cap) {
 
 int gemm_split(const GemmArgs& a, int epi, long cap) {
   switch (epi) {
+    case EPI_ROPE_QKV: return 1;  // the epilogue needs the finished sums
     case EPI_STORE_F32: return split_for<EPI_STORE_F32>(a, cap);
     case EPI_ADD_F32: return split_for<EPI_ADD_F32>(a, cap);
     case EPI_SWIGLU_BF16: return 1;  // measured: the extra reduce pass costs more than it saves
@@ -463,6 +496,7 @@ void launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
     case EPI_STORE_F32: launch_epi<EPI_STORE_F32>(a, s); break;
     case EPI_ADD_F32: launch_epi<EPI_ADD_F32>(a, s); break;
     case EPI_SWIGLU_BF16: launch_epi<EPI_SWIGLU_BF16>(a, s); break;
+    case EPI_ROPE_QKV: launch_epi<EPI_ROPE_QKV>(a, s); break;
     default: launch_epi<EPI_STORE_BF16>(a, s); break;
   }
 }
@@ -491,6 +525,32 @@ void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
                        float* lse, float* ent, const RowMap& map, hipStream_t s) {
   hipLaunchKernelGGL(head_merge_kernel, dim3(n_rows), dim3(256), 0, s, part, n_rows, n_slices,
                      slice_w, cur_tok, cand, t_cand, t_cur, lse, ent, map);
+}
+
+// One work-group per output row: row r of head h (q heads, then k heads) takes source row
+// h*D + (e odd ? D/2 : 0) + 2*(w/4) + e/2 with w = r - h*D, e = w % 4; v rows are copied as is.
+__global__ __launch_bounds__(256) void pack_qkv_kernel(const uint16_t* __restrict__ wq,
+                                                       const uint16_t* __restrict__ wk,
+                                                       const uint16_t* __restrict__ wv,
+                                                       uint16_t* __restrict__ out, int Hq, int Hkv,
+                                                       int D, int d) {
+  const int r = blockIdx.x;
+  const int qk = (Hq + Hkv) * D;
+  const uint16_t* src;
+  if (r < qk) {
+    const int h = r / D, w = r - h * D, e = w & 3;
+    const int sr = ((e & 1) ? D / 2 : 0) + 2 * (w >> 2) + (e >> 1);
+    src = (h < Hq) ? wq + (static_cast<long>(h) * D + sr) * d : wk + (static_cast<long>(h - Hq) * D + sr) * d;
+  } else {
+    src = wv + static_cast<long>(r - qk) * d;
+  }
+  for (int c = threadIdx.x; c < d; c += 256) out[static_cast<long>(r) * d + c] = src[c];
+}
+
+void launch_pack_qkv(const uint16_t* wq, const uint16_t* wk, const uint16_t* wv, uint16_t* out,
+                     int Hq, int Hkv, int D, int d, hipStream_t s) {
+  hipLaunchKernelGGL(pack_qkv_kernel, dim3((Hq + 2 * Hkv) * D), dim3(256), 0, s, wq, wk, wv, out, Hq,
+                     Hkv, D, d);
 }
 
 // Canvas tokens of this call's requests, compacted: dst[b][i] = src[slot[b]][i].
