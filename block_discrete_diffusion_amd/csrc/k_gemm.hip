@@ -508,16 +508,14 @@ void launch_swiglu_reduce(const float* part, long part_stride, int split, uint16
                      split, act, n4);
 }
 
-// 128 vocab entries x 64 rows per work-group for one canvas; 128 x 128 from 1024 rows (half the
-// LDS fragment traffic per MFMA, and still one work-group per CU or more)
+// 128 vocab entries x 128 rows per work-group: each vocab tile is streamed by half as many
+// work-groups as with 64-row tiles, and each K fragment read from LDS feeds twice the MFMAs
+// (measured at one canvas with cold weights: 128 x 128 is about 15 % faster than 128 x 64; a
+// weight-streaming variant with all 256 rows per work-group was no faster).  The statistics do
+// not depend on the tiling (same k order, same 64-entry slices).
 void launch_head(const HeadArgs& a, hipStream_t s) {
-  if (a.n_rows >= 1024) {
-    const int G = ((a.n_rows + 127) / 128) * (a.V / 128);
-    hipLaunchKernelGGL((head_kernel<128, 128>), dim3(G), dim3(256), 0, s, a);
-  } else {
-    const int G = ((a.n_rows + 63) / 64) * (a.V / 128);
-    hipLaunchKernelGGL((head_kernel<128, 64>), dim3(G), dim3(256), 0, s, a);
-  }
+  const int G = ((a.n_rows + 127) / 128) * (a.V / 128);
+  hipLaunchKernelGGL((head_kernel<128, 128>), dim3(G), dim3(256), 0, s, a);
 }
 
 void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
