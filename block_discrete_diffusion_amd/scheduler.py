@@ -110,9 +110,18 @@ class ContinuousBatcher:
             return
         slots = [r.slot for r in new]
         toks = np.concatenate([r.prompt for r in new]) if any(len(r.prompt) for r in new) else np.zeros(1, np.int32)
-        dev = torch.from_numpy(toks).to(self.m.device)
-        self.m.prefill(dev, [len(r.prompt) for r in new], self.kv, slots=slots)
-        self.m.canvas_init(self.state, self.kv, self.cfg, slots=slots)
+        try:
+            dev = torch.from_numpy(toks).to(self.m.device)
+            self.m.prefill(dev, [len(r.prompt) for r in new], self.kv, slots=slots)
+            self.m.canvas_init(self.state, self.kv, self.cfg, slots=slots)
+        except Exception:
+            # put the requests back at the head of the queue and free their slots, so the
+            # batcher is left as it was before this admission
+            for r in reversed(new):
+                self.free.appendleft(r.slot)
+                r.slot, r.admitted_at = -1, -1
+                self.queue.appendleft(r)
+            raise
         for r in new:
             r.step = 0
             self.active[r.slot] = r

@@ -185,3 +185,18 @@ def test_rejects_bad_requests_and_settings():
     with pytest.raises(ValueError):
         b.submit([1, 2], 0)
     assert b.idle()
+
+
+def test_failed_admission_leaves_queue_and_slots_unchanged():
+    class Failing(FakeModel):
+        def prefill(self, tokens, n_new, kv, slots=None):
+            raise RuntimeError("device error")
+
+    fm = Failing(synth.TINY, max_batch=4)
+    kv = dg.KV(synth.TINY, 3, 2000, device="cpu", fill=None)
+    b = ContinuousBatcher(fm, kv, dg.sampler_cfg(seed=1), max_active=2)
+    rids = [b.submit(p, n) for p, n in REQS]
+    with pytest.raises(RuntimeError):
+        b.step()
+    assert [r.rid for r in b.queue] == rids and sorted(b.free) == [0, 1, 2] and not b.active
+    assert all(r.slot == -1 for r in b.queue)
