@@ -276,9 +276,17 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
                          sizeof(float) * rows * m.top_k, hipMemcpyDeviceToDevice, s);
 
   const int routes = rows * m.top_k;
-  timed(c, "moe_permute", s, [&] { launch_moe_permute(c->eidx, routes, m.n_experts, c->offs, c->perm, c->inv, s); });
+  // up to kFusedRoutes routes the gate/up GEMM ranks its own expert's routes (one launch less);
+  // beyond that a separate permutation pass does
+  const bool fused_rank = routes <= kFusedRoutes;
+  if (!fused_rank)
+    timed(c, "moe_permute", s, [&] { launch_moe_permute(c->eidx, routes, m.n_experts, c->offs, c->perm, c->inv, s); });
   MoeArgs g1{};
   g1.x = c->a; g1.ldx = d; g1.perm = c->perm; g1.top_k = m.top_k; g1.offs = c->offs;
+  if (fused_rank) {
+    g1.idx = c->eidx; g1.n_routes = routes;
+    g1.offs_w = c->offs; g1.perm_w = c->perm; g1.inv_w = c->inv;
+  }
   g1.wp = c->pk1[l]; g1.K = d; g1.N = m.d_ff_expert;
   if (m.expert_fp8) { g1.wp8 = c->pk1_8[l]; g1.wscale0 = c->sc_gate[l]; g1.wscale1 = c->sc_up[l]; }
   g1.out_bf16 = c->act; g1.ldo = m.d_ff_expert; g1.n_exp = m.n_experts;

@@ -146,7 +146,14 @@ struct MoeArgs {
   int n_exp;
   // E4M3 experts (instead of wp): packed bytes and per-channel scales [E][N] of matrix q
   const uint8_t* wp8; const float* wscale0; const float* wscale1;
+  // GEMM1 only, optional: rank the routes itself from the router's choices idx [n_routes]
+  // (n_routes <= kFusedRoutes) instead of reading offs / perm; the work-groups with
+  // blockIdx.x = blockIdx.z = 0 then write offs_w [E+1], perm_w and inv_w [n_routes] for the
+  // down projection and the combine.
+  const int32_t* idx; int n_routes;
+  int32_t* offs_w; int32_t* perm_w; int32_t* inv_w;
 };
+constexpr int kFusedRoutes = 2048;
 // Packed expert weights: for expert e, 16-row tile ft and 32-wide k-step s, the MFMA A-operand
 // fragment of every matrix q (GEMM1: q = gate, up; GEMM2: q = down) is 64 lanes x 16 B, lane l
 // holding W_q[e][16 ft + l % 16][32 s + 8 (l / 16) .. + 8].  Order:

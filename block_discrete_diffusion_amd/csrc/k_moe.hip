@@ -101,16 +101,83 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
   constexpr int KC = 32 * KS, ROWS = TT * 16, LDX = KC + 8, CPR = KC / 8;
   constexpr int PIECES = ROWS * CPR, PPT = (PIECES + 255) / 256;
   __shared__ uint16_t xs[2][ROWS * LDX];
+  __shared__ int rl[GATED ? kFusedRoutes : 1];  // this expert's routes, in route order
+  __shared__ int wc[2][4];
   const int e = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j4 = lane >> 4, l16 = lane & 15;
-  const int p0 = a.offs[e], n_e = a.offs[e + 1] - p0;
-  if (n_e == 0) return;  // uniform over the work-group
   const int ft0 = blockIdx.x * GT + w * FPW;
   const int S = a.K / 32, nch = S / KS;
   const long wgrp = static_cast<long>(e) * (a.N / (16 * GT)) + blockIdx.x;  // packed tile group
   const uint16_t* wp = F8 ? nullptr : a.wp + (wgrp * S * GT + w * FPW) * NA * 512 + lane * 8;
   const uint8_t* wp8 = F8 ? a.wp8 + ((wgrp * (S / 2) * GT + w * FPW) * NA * 64 + lane) * 16 : nullptr;
+  // bf16: one 16-byte fragment per (k-step, tile, matrix); E4M3: one 16-byte load holds the
+  // fragments of both k-steps of the chunk, widened to bf16 (exactly) right before the MFMA
+  constexpr int WS = F8 ? 1 : KS;
+  u32x4_t fw[2][WS][FPW][NA];
+  auto load_w = [&](int b, int c) {
+#pragma unroll
+    for (int ks = 0; ks < WS; ++ks)
+#pragma unroll
+      for (int f = 0; f < FPW; ++f)
+#pragma unroll
+        for (int q = 0; q < NA; ++q) {
+          if constexpr (F8) fw[b][ks][f][q] = ld16_nt(wp8 + ((c * GT + f) * NA + q) * 1024);
+          else fw[b][ks][f][q] = ld16_nt(wp + (((c * KS + ks) * GT + f) * NA + q) * 512);
+        }
+  };
+  int p0, n_e;
+  const bool fused = GATED && a.idx != nullptr;  // uniform
+  if (fused) {
+    // rank this expert's routes from the router's choices: p0 = routes of lower experts, and
+    // the routes of expert e in route order, i.e. the order of a stable sort by (expert,
+    // route).  Wave w owns routes [64 PER w, 64 PER (w+1)); all its loads are issued at once,
+    // then ballots count and place them (two barriers in all)
+    constexpr int PER = kFusedRoutes / 256;
+    const unsigned long long below_lane = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int ex[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int r = (w * PER + i) * 64 + lane;
+      ex[i] = (r < a.n_routes) ? a.idx[r] : 0x7fffffff;
+    }
+    int c_eq = 0, c_lt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      c_eq += __popcll(__ballot(ex[i] == e));
+      c_lt += __popcll(__ballot(ex[i] < e));
+    }
+    if (lane == 0) {
+      wc[0][w] = c_eq;
+      wc[1][w] = c_lt;
+    }
+    __syncthreads();
+    int run = 0;
+    for (int v = 0; v < w; ++v) run += wc[0][v];
+    n_e = (wc[0][0] + wc[0][1]) + (wc[0][2] + wc[0][3]);
+    p0 = (wc[1][0] + wc[1][1]) + (wc[1][2] + wc[1][3]);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const unsigned long long eq = __ballot(ex[i] == e);
+      if (ex[i] == e) rl[run + __popcll(eq & below_lane)] = (w * PER + i) * 64 + lane;
+      run += __popcll(eq);
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && blockIdx.z == 0) {
+      if (tid == 0) {
+        a.offs_w[e] = p0;
+        if (e == a.n_exp - 1) a.offs_w[a.n_exp] = a.n_routes;
+      }
+      for (int j = tid; j < n_e; j += 256) {
+        a.perm_w[p0 + j] = rl[j];
+        a.inv_w[rl[j]] = p0 + j;
+      }
+    }
+  } else {
+    p0 = a.offs[e];
+    n_e = a.offs[e + 1] - p0;
+  }
+  if (n_e == 0) return;  // uniform over the work-group
 
   // passes of ROWS rows: work-group z takes passes z, z + Z, ... (Z = gridDim.z), so an expert
   // with more rows than one pass holds is covered by parallel work-groups, not a serial pass
@@ -125,7 +192,7 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
       const int piece = tid + 256 * j, pc = min(piece, PIECES - 1);
       const int r = pc / CPR, col = (pc % CPR) * 8;
       const int rr = min(ps + r, n_e - 1);
-      const long row = GATED ? (a.perm[p0 + rr] / a.top_k) : static_cast<long>(p0 + rr);
+      const long row = GATED ? ((fused ? rl[rr] : a.perm[p0 + rr]) / a.top_k) : static_cast<long>(p0 + rr);
       src[j] = a.x + row * a.ldx + col;
       dst[j] = r * LDX + col;
       keep[j] = piece < PIECES;
@@ -137,21 +204,7 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
       for (int q = 0; q < NA; ++q)
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[f][q][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    // bf16: one 16-byte fragment per (k-step, tile, matrix); E4M3: one 16-byte load holds the
-    // fragments of both k-steps of the chunk, widened to bf16 (exactly) right before the MFMA
-    constexpr int WS = F8 ? 1 : KS;
-    u32x4_t fw[2][WS][FPW][NA], xr[PPT];
-    auto load_w = [&](int b, int c) {
-#pragma unroll
-      for (int ks = 0; ks < WS; ++ks)
-#pragma unroll
-        for (int f = 0; f < FPW; ++f)
-#pragma unroll
-          for (int q = 0; q < NA; ++q) {
-            if constexpr (F8) fw[b][ks][f][q] = ld16_nt(wp8 + ((c * GT + f) * NA + q) * 1024);
-            else fw[b][ks][f][q] = ld16_nt(wp + (((c * KS + ks) * GT + f) * NA + q) * 512);
-          }
-    };
+    u32x4_t xr[PPT];
     auto frag = [&](int b, int ks, int f, int q) -> u32x4_t {
       if constexpr (F8) {
         const u32x4_t v = fw[b][0][f][q];
