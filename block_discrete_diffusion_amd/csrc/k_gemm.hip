@@ -173,6 +173,37 @@ DG_DEVICE void rope_store(const RopeArgs& r, int t, int f, const floatx4_t& v) {
   }
 }
 
+// One lane's four consecutive outputs f..f+3 of token t (u: the up-projection sums of the
+// SwiGLU pair).  With S > 1 the raw fp32 sums go to slice z of the partial buffer.
+template <int EPI>
+DG_DEVICE void store_out(const GemmArgs& a, int S, int z, int t, int f, const floatx4_t& v,
+                         const floatx4_t& u) {
+  constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
+  if (S > 1) {
+    float* p = a.part + z * a.part_stride + static_cast<long>(t) * a.N + f;
+    *reinterpret_cast<floatx4_t*>(p) = v;
+    if constexpr (DUAL) *reinterpret_cast<floatx4_t*>(p + a.part_stride / 2) = u;
+  } else if constexpr (EPI == EPI_STORE_F32) {
+    *reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(t) * a.ldo + f) = v;
+  } else if constexpr (EPI == EPI_ADD_F32) {
+    floatx4_t* p = reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(t) * a.ldo + f);
+    floatx4_t o = *p;
+    o += v;
+    *p = o;
+  } else if constexpr (EPI == EPI_ROPE_QKV) {
+    rope_store(a.rope, t, f, v);
+  } else if constexpr (EPI == EPI_SWIGLU_BF16) {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = v[i] / (1.0f + expf(-v[i])) * u[i];
+    *reinterpret_cast<u32x2_t*>(a.out_bf16 + static_cast<long>(t) * a.ldo + f) =
+        u32x2_t{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
+  } else {
+    *reinterpret_cast<u32x2_t*>(a.out_bf16 + static_cast<long>(t) * a.ldo + f) =
+        u32x2_t{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+  }
+}
+
 // Split-K: grid = tiles x S.  With S > 1 work-group (tile, z) multiplies the z-th K / S slice
 // and stores the raw fp32 product to its own slice of the partial buffer; the consuming kernel
 // adds the S slices in z order (a kernel boundary is the only synchronisation).
@@ -209,32 +240,169 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, int S) {
       const int t = t0 + wt * ML::WT + tn * 16 + (lane & 15);
       const int f = f0 + wf * ML::WF + fm * 16 + 4 * (lane >> 4);
       if (t >= a.n_tok) continue;
-      const floatx4_t v = ml.acc[fm][tn];
-      if (S > 1) {
-        float* p = a.part + z * a.part_stride + static_cast<long>(t) * a.N + f;
-        *reinterpret_cast<floatx4_t*>(p) = v;
-        if constexpr (DUAL)
-          *reinterpret_cast<floatx4_t*>(p + a.part_stride / 2) = ml.acc1[DUAL ? fm : 0][DUAL ? tn : 0];
-      } else if constexpr (EPI == EPI_STORE_F32) {
-        *reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(t) * a.ldo + f) = v;
-      } else if constexpr (EPI == EPI_ADD_F32) {
-        floatx4_t* p = reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(t) * a.ldo + f);
-        floatx4_t o = *p;
-        o += v;
-        *p = o;
-      } else if constexpr (EPI == EPI_ROPE_QKV) {
-        rope_store(a.rope, t, f, v);
-      } else if constexpr (EPI == EPI_SWIGLU_BF16) {
-        const floatx4_t u = ml.acc1[DUAL ? fm : 0][DUAL ? tn : 0];
-        float y[4];
+      store_out<EPI>(a, S, z, t, f, ml.acc[fm][tn], ml.acc1[DUAL ? fm : 0][DUAL ? tn : 0]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Large-tile path (from 1024 tokens).  A work-group of 8 waves owns 256 weight rows (for the
+// SwiGLU pair: 128 gate rows + the same 128 up rows) x 128 tokens; wave (wa, wt) = (w & 3,
+// w >> 2) multiplies 64 weight rows (32 gate + 32 up) by 64 tokens.
+//
+// Both operands go from global memory straight into LDS with gfx950's global_load_lds_dwordx4:
+// lane l's 16 bytes land at the instruction's LDS base + 16 l, so one instruction fills a 1 KB
+// block of 8 rows x 128 bytes (64 k).  Whole 128-byte row segments per instruction matter: on
+// this part, instructions that touch 16 rows x 64 bytes at a 4 KB pitch read L2 about 4x slower
+// than 8 rows x 128 bytes.  Inside a block, row r's 16-byte chunk c sits at slot c ^ ((r16 >> 1)
+// & 7), r16 being the row's index within its 16-row MFMA fragment (the lane loading slot s of
+// row r fetches chunk s ^ ((r16 >> 1) & 7)): the 16 lanes of each ds_read_b128 phase then hit
+// 16 distinct 4-bank groups, so fragment reads are conflict-free.  No VGPRs or LDS write
+// instructions stage the tiles.
+//
+// A stage is one k-step of 64 (32 weight blocks + 16 token blocks = 48 KB); a ring of NS = 3
+// stages keeps the next k-step in flight while one is multiplied, with one barrier per k-step.
+// The wait before the barrier names the number of this wave's loads allowed to stay in flight
+// (6 per later stage); every stage is issued unconditionally (the tile index is clamped, so the
+// last stages re-load the final k-step into buffers nobody reads again), which keeps that
+// count exact.
+// ------------------------------------------------------------------------------------------
+constexpr int DL_RA = 256;  // weight rows per tile
+constexpr int DL_BK = 64;   // k per stage
+
+// BT tokens per tile (128 or 256), NW waves (8 or 16: 4 along the weight rows x NW / 4 along
+// the tokens); NS stages in the ring, as many as fit the 160 KB of LDS
+template <int BT, int NW>
+struct DlShape {
+  static constexpr int BLK = (DL_RA + BT) / 8;  // 1 KB blocks (8 rows x 128 B) per stage
+  static_assert(BLK % NW == 0, "blocks per stage must split evenly over the waves");
+  static constexpr int PW = BLK / NW;           // blocks each wave loads per stage
+  static constexpr int NS = (160 * 1024) / (BLK * 1024);
+  static constexpr int WT = BT / (NW / 4);      // tokens per wave
+  static constexpr int TN = WT / 16;            // 16-token fragments per wave
+};
+
+template <int BT>
+struct DlSmem {
+  uint16_t b[DlShape<BT, 8>::NS][DlShape<BT, 8>::BLK][512];
+};
+
+// s_waitcnt with vmcnt = n (< 64) and lgkmcnt = 0 (expcnt not waited on).
+template <int n>
+DG_DEVICE void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | ((n >> 4) << 14));
+}
+
+template <int BT, bool DUAL, int NW = 8>
+struct DlMainloop {
+  using SH = DlShape<BT, NW>;
+  static constexpr int NS = SH::NS, DL_PW = SH::PW;
+  static constexpr int FM = 4, TN = SH::TN;  // 16-row fragments per wave (DUAL: 0-1 gate, 2-3 up)
+  floatx4_t acc[FM][TN];
+
+  DG_DEVICE void run(DlSmem<BT>& sm, const uint16_t* w0, const uint16_t* w1, const uint16_t* x,
+                     int ldx, int n_tok, int t0, int K, int ldw) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wa = wave & 3, wt = wave >> 2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = v[i] / (1.0f + expf(-v[i])) * u[i];
-        *reinterpret_cast<u32x2_t*>(a.out_bf16 + static_cast<long>(t) * a.ldo + f) =
-            u32x2_t{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // source of this lane in each block its wave loads: blocks 0-31 hold weight rows 8 j ..
+    // 8 j + 7 (DUAL: 0-15 gate, 16-31 up), the others tokens 8 (j - 32) ..
+    const uint16_t* src[DL_PW];
+#pragma unroll
+    for (int i = 0; i < DL_PW; ++i) {
+      const int j = wave * DL_PW + i;
+      const int r16 = (j & 1) * 8 + (lane >> 3);
+      const int kof = 8 * ((lane & 7) ^ ((r16 >> 1) & 7));
+      if (j < DL_RA / 8) {
+        const int r = j * 8 + (lane >> 3);
+        src[i] = (DUAL && r >= DL_RA / 2) ? w1 + static_cast<long>(r - DL_RA / 2) * ldw + kof
+                                          : w0 + static_cast<long>(r) * ldw + kof;
       } else {
-        *reinterpret_cast<u32x2_t*>(a.out_bf16 + static_cast<long>(t) * a.ldo + f) =
-            u32x2_t{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+        // rows past n_tok re-read the last row; their outputs are never stored
+        const int t = min(t0 + (j - DL_RA / 8) * 8 + (lane >> 3), n_tok - 1);
+        src[i] = x + static_cast<long>(t) * ldx + kof;
       }
+    }
+    // fragment read offset (elements) of this lane inside a 16-row pair of blocks, per k half
+    const int r16 = lane & 15;
+    int fofs[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      fofs[h] = (r16 >> 3) * 512 + (r16 & 7) * 64 + 8 * ((4 * h + (lane >> 4)) ^ ((r16 >> 1) & 7));
+    const int nk = K / DL_BK;
+    auto issue = [&](int st, int kt) {
+#pragma unroll
+      for (int i = 0; i < DL_PW; ++i)
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void*>(src[i] + kt * DL_BK),
+            (__attribute__((address_space(3))) void*)(&sm.b[st][wave * DL_PW + i][0]), 16, 0, 0);
+    };
+    auto compute = [&](int st) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4_t af[FM], bx[TN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          // 16-row weight fragment index (pairs of blocks)
+          const int g = DUAL ? (i < 2 ? wa * 2 + i : DL_RA / 32 + wa * 2 + (i - 2)) : wa * FM + i;
+          af[i] = ld16(&sm.b[st][2 * g][fofs[h]]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bx[j] = ld16(&sm.b[st][DL_RA / 8 + 2 * (wt * TN + j)][fofs[h]]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[i], bx[j], acc[i][j]);
+      }
+    };
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) issue(st, min(st, nk - 1));
+    for (int kt = 0; kt < nk; ++kt) {
+      // this wave's loads of stage kt have landed (NS - 2 later stages may still be in
+      // flight) and its fragment reads of stage kt - 1 are done; after the barrier the same
+      // holds for every wave, so stage kt is complete and buffer (kt - 1) % NS is free
+      wait_vm_lgkm0<DL_PW * (NS - 2)>();
+      __builtin_amdgcn_s_barrier();
+      issue((kt + NS - 1) % NS, min(kt + NS - 1, nk - 1));
+      compute(kt % NS);
+    }
+    // no load may still be writing this work-group's LDS when it exits
+    wait_vm_lgkm0<0>();
+  }
+};
+
+template <int BT, int NW, int EPI>
+__global__ __launch_bounds__(64 * NW) void gemm_dl_kernel(GemmArgs a, int S) {
+  constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
+  constexpr int BF = DUAL ? DL_RA / 2 : DL_RA;  // output features per tile
+  constexpr int WF = BF / 4;                    // per wave
+  using ML = DlMainloop<BT, DUAL, NW>;
+  __shared__ DlSmem<BT> sm;
+  const int n_tt = (a.n_tok + BT - 1) / BT, n_ft = a.N / BF;
+  const int L = xcd_remap(blockIdx.x, n_tt * n_ft * S);
+  const int tile = L / S, z = L % S;
+  const int ft = tile / n_tt, tt = tile % n_tt;
+  const int f0 = ft * BF, t0 = tt * BT;
+  const int kz = a.K / S, k0 = z * kz;
+  const uint16_t* w0 = a.w0 + static_cast<long>(f0) * a.K + k0;
+  const uint16_t* w1 = DUAL ? a.w1 + static_cast<long>(f0) * a.K + k0 : nullptr;
+  ML ml;
+  ml.run(sm, w0, w1, a.x + k0, a.ldx, a.n_tok, t0, kz, a.K);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wa = wave & 3, wt = wave >> 2;
+  constexpr int NF = DUAL ? ML::FM / 2 : ML::FM;
+#pragma unroll
+  for (int fm = 0; fm < NF; ++fm)
+#pragma unroll
+    for (int tn = 0; tn < ML::TN; ++tn) {
+      const int t = t0 + wt * ML::SH::WT + tn * 16 + (lane & 15);
+      const int f = f0 + wa * WF + fm * 16 + 4 * (lane >> 4);
+      if (t >= a.n_tok) continue;
+      store_out<EPI>(a, S, z, t, f, ml.acc[fm][tn], ml.acc[DUAL ? fm + 2 : fm][tn]);
     }
 }
 
@@ -304,43 +472,34 @@ DG_DEVICE Stat shfl_stat(const Stat& a, int o) {
   return r;
 }
 
-template <int BF, int BT>
-__global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
-  using ML = Mainloop<BF, BT, false>;
-  __shared__ Smem<BF, BT, false> sm;
-  const int n_tt = (a.n_rows + BT - 1) / BT, n_ft = a.V / BF;
-  const int L = xcd_remap(blockIdx.x, n_tt * n_ft);
-  const int ft = L / n_tt, tt = L % n_tt;
-  const int f0 = ft * BF, t0 = tt * BT;
-  ML ml;
-  ml.run(sm, a.w + static_cast<long>(f0) * a.K, nullptr, a.f, a.K, a.n_rows, t0, a.K, a.K);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wf = wave & 1, wt = wave >> 1;
-  const int n_slices = a.V / ML::WF;
-  const int slice = (f0 + wf * ML::WF) / ML::WF;
+// Statistics of one wave's logits: FM 16-entry vocab fragments from v_base (64 entries, one
+// slice) x TN 16-row token fragments from t_base.
+template <int FM, int TN>
+DG_DEVICE void head_stats(const HeadArgs& a, const floatx4_t (&acc)[FM][TN], int v_base, int t_base,
+                          int slice, int n_slices) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int tn = 0; tn < ML::TN; ++tn) {
-    const int t = t0 + wt * ML::WT + tn * 16 + (lane & 15);
+  for (int tn = 0; tn < TN; ++tn) {
+    const int t = t_base + tn * 16 + (lane & 15);
     const bool ok = t < a.n_rows;
     const int tc = ok ? t : 0;
     const int b = tc / a.map.rows_per_req;
     const int pos = a.map.pos0[b] + (tc - b * a.map.rows_per_req);
     const int cur = ok ? a.cur_tok[tc] : -1;
     const float temp_b = a.temp[b];
-    float tv[ML::FM][4];
+    float tv[FM][4];
     Stat st;
     st.m = -INFINITY; st.s = 0.f; st.st = 0.f; st.bs = -INFINITY; st.bt = 0.f; st.tc = NAN;
     st.bi = 0x7fffffff;
 #pragma unroll
-    for (int fm = 0; fm < ML::FM; ++fm) {
-      const int v0 = f0 + wf * ML::WF + fm * 16 + 4 * (lane >> 4);
+    for (int fm = 0; fm < FM; ++fm) {
+      const int v0 = v_base + fm * 16 + 4 * (lane >> 4);
       const philox_out rnd = philox4x32_10(static_cast<uint32_t>(v0 >> 2), static_cast<uint32_t>(pos),
                                            static_cast<uint32_t>(a.step[b]),
                                            (static_cast<uint32_t>(a.map.slot[b]) << 8) | kStreamGumbel, a.k0, a.k1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float z = ml.acc[fm][tn][i];
+        const float z = acc[fm][tn][i];
         const float t_ = z / temp_b;
         tv[fm][i] = t_;
         const float sc = t_ + gumbel(rnd.x[i]);
@@ -351,7 +510,7 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
       }
     }
 #pragma unroll
-    for (int fm = 0; fm < ML::FM; ++fm)
+    for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e = expf(tv[fm][i] - st.m);
@@ -366,6 +525,38 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
       *reinterpret_cast<floatx4_t*>(p + 4) = floatx4_t{__int_as_float(st.bi), st.bt, st.tc, 0.f};
     }
   }
+}
+
+template <int BF, int BT>
+__global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
+  using ML = Mainloop<BF, BT, false>;
+  __shared__ Smem<BF, BT, false> sm;
+  const int n_tt = (a.n_rows + BT - 1) / BT, n_ft = a.V / BF;
+  const int L = xcd_remap(blockIdx.x, n_tt * n_ft);
+  const int ft = L / n_tt, tt = L % n_tt;
+  const int f0 = ft * BF, t0 = tt * BT;
+  ML ml;
+  ml.run(sm, a.w + static_cast<long>(f0) * a.K, nullptr, a.f, a.K, a.n_rows, t0, a.K, a.K);
+  const int wave = threadIdx.x >> 6, wf = wave & 1, wt = wave >> 1;
+  static_assert(ML::WF == 64, "one statistics slice per wave");
+  head_stats(a, ml.acc, f0 + wf * ML::WF, t0 + wt * ML::WT, (f0 + wf * ML::WF) / ML::WF, a.V / ML::WF);
+}
+
+// The same head on the large-tile direct-to-LDS mainloop: 256 vocab entries x BT rows per
+// work-group, 64 vocab entries (one statistics slice) x BT / (NW / 4) rows per wave.  Same k order and
+// slices, so the statistics are bit-identical to the kernel above.
+template <int BT, int NW>
+__global__ __launch_bounds__(64 * NW) void head_dl_kernel(HeadArgs a) {
+  using ML = DlMainloop<BT, false, NW>;
+  __shared__ DlSmem<BT> sm;
+  const int n_tt = (a.n_rows + BT - 1) / BT, n_ft = a.V / DL_RA;
+  const int L = xcd_remap(blockIdx.x, n_tt * n_ft);
+  const int ft = L / n_tt, tt = L % n_tt;
+  const int f0 = ft * DL_RA, t0 = tt * BT;
+  ML ml;
+  ml.run(sm, a.w + static_cast<long>(f0) * a.K, nullptr, a.f, a.K, a.n_rows, t0, a.K, a.K);
+  const int wave = threadIdx.x >> 6, wa = wave & 3, wt = wave >> 2;
+  head_stats(a, ml.acc, f0 + wa * 64, t0 + wt * ML::SH::WT, (f0 + wa * 64) / 64, a.V / 64);
 }
 
 // One work-group (4 waves) per row: thread t merges slices t, t + 256, ... (two 16-byte loads
@@ -453,8 +644,45 @@ void pick_tile(const GemmArgs& a, int* bf, int* bt) {
   else { *bf = 32; *bt = 64; }
 }
 
+// From 1024 tokens the large-tile direct-to-LDS kernel, where the weights come in whole tiles
+// (256 rows; 128 for the SwiGLU pair), unsegmented, and the grid fills the chip: one
+// work-group per CU (its LDS ring takes most of the CU), so below 256 work-groups the LDS-tiled
+// kernel, which runs two per CU, is faster.  256-token tiles (1.5x the MFMAs per staged byte)
+// where there are 256 of them, else 128-token tiles.  Measured at 2048 tokens: QKV 54.6 ->
+// 43.5 us (128-token tiles), shared gate/up 100 -> 70 us (256-token tiles).
+template <int EPI>
+bool dl_eligible(const GemmArgs& a) {
+  constexpr int BF = (EPI == EPI_SWIGLU_BF16) ? DL_RA / 2 : DL_RA;
+  return a.n_tok >= 1024 && a.n_seg == 0 && a.N % BF == 0 && a.K % DL_BK == 0;
+}
+
+template <int EPI, int BT>
+int dl_tiles(const GemmArgs& a) {
+  constexpr int BF = (EPI == EPI_SWIGLU_BF16) ? DL_RA / 2 : DL_RA;
+  return ((a.n_tok + BT - 1) / BT) * (a.N / BF);
+}
+
+// 0: LDS-tiled kernel; else the large-tile kernel's token tile for split S
+template <int EPI>
+int dl_choice(const GemmArgs& a, int S) {
+  if (!dl_eligible<EPI>(a)) return 0;
+  if (S == 1 && dl_tiles<EPI, 256>(a) >= 256) return 256;
+  if (dl_tiles<EPI, 128>(a) * S >= 256) return 128;
+  return 0;
+}
+
 template <int EPI>
 void launch_epi(const GemmArgs& a, hipStream_t s) {
+  const int S = a.split > 1 ? a.split : 1;
+  const int dl = dl_choice<EPI>(a, S);
+  if (dl == 256) {
+    hipLaunchKernelGGL((gemm_dl_kernel<256, 16, EPI>), dim3(dl_tiles<EPI, 256>(a) * S), dim3(1024), 0, s, a, S);
+    return;
+  }
+  if (dl == 128) {
+    hipLaunchKernelGGL((gemm_dl_kernel<128, 16, EPI>), dim3(dl_tiles<EPI, 128>(a) * S), dim3(1024), 0, s, a, S);
+    return;
+  }
   int bf, bt;
   pick_tile<EPI>(a, &bf, &bt);
   if constexpr (EPI != EPI_SWIGLU_BF16) {
@@ -468,12 +696,24 @@ void launch_epi(const GemmArgs& a, hipStream_t s) {
 template <int EPI>
 int split_for(const GemmArgs& a, long cap) {
   constexpr int NA = (EPI == EPI_SWIGLU_BF16) ? 2 : 1;
+  // the large-tile kernel: unsplit when it has a chip's worth of tiles, else split K until
+  // its 128-token tiles do (one work-group per CU)
+  if (dl_choice<EPI>(a, 1) == 256) return 1;
+  if (dl_eligible<EPI>(a)) {
+    const int t128 = dl_tiles<EPI, 128>(a);
+    int S = 1;
+    while (S < kMaxParts && t128 * S < 256 && (a.K / BK) % (S * 2) == 0 && a.K / (S * 2) >= 16 * BK &&
+           static_cast<long>(S) * 2 * NA * a.n_tok * a.N <= cap)
+      S *= 2;
+    if (dl_choice<EPI>(a, S) != 0) return S;
+  }
   int bf, bt;
   pick_tile<EPI>(a, &bf, &bt);
   const int tiles = ((a.n_tok + bt - 1) / bt) * (a.N / bf);
   // split K while the grid stays within ~2 work-groups per CU and each slice keeps >= 16 k-tiles
+  const int max_wg = 512;
   int S = 1;
-  while (S < kMaxParts && tiles * S * 2 <= 512 && (a.K / BK) % (S * 2) == 0 && a.K / (S * 2) >= 16 * BK &&
+  while (S < kMaxParts && tiles * S * 2 <= max_wg && (a.K / BK) % (S * 2) == 0 && a.K / (S * 2) >= 16 * BK &&
          static_cast<long>(S) * 2 * NA * a.n_tok * a.N <= cap)
     S *= 2;
   return S;
@@ -508,12 +748,18 @@ void launch_swiglu_reduce(const float* part, long part_stride, int split, uint16
                      split, act, n4);
 }
 
-// 128 vocab entries x 128 rows per work-group: each vocab tile is streamed by half as many
-// work-groups as with 64-row tiles, and each K fragment read from LDS feeds twice the MFMAs
-// (measured at one canvas with cold weights: 128 x 128 is about 15 % faster than 128 x 64; a
-// weight-streaming variant with all 256 rows per work-group was no faster).  The statistics do
-// not depend on the tiling (same k order, same 64-entry slices).
+// The head runs on the large-tile mainloop (256 vocab entries x 256 rows per work-group; with
+// V 65536 there are at least 256 tiles at any row count).  Measured at 256 rows against the
+// LDS-tiled 128 x 128 kernel: 87.5 against about 120 us; at 2048 rows 521 against about 900 us.
+// Shapes the large tile does not divide use the LDS-tiled kernel (128 x 128: each vocab tile is
+// streamed by half as many work-groups as with 64-row tiles).  The statistics do not depend on
+// the tiling (same k order, same 64-entry slices).
 void launch_head(const HeadArgs& a, hipStream_t s) {
+  if (a.V % DL_RA == 0 && a.K % DL_BK == 0) {
+    const int G = ((a.n_rows + 255) / 256) * (a.V / DL_RA);
+    hipLaunchKernelGGL((head_dl_kernel<256, 16>), dim3(G), dim3(1024), 0, s, a);
+    return;
+  }
   const int G = ((a.n_rows + 127) / 128) * (a.V / 128);
   hipLaunchKernelGGL((head_kernel<128, 128>), dim3(G), dim3(256), 0, s, a);
 }

@@ -243,3 +243,31 @@ def test_long_causal_prefill(chunk):
             close(bf16_to_np(kv.v[l, 0, :, :n]), cv[l][:, :n], what=f"prefill V layer {l}", bf16_out=True)
     finally:
         m.close()
+
+
+def test_prefill_2048_rows_on_the_large_tile_gemms():
+    """A 2048-row causal prefill at width 2048 with the shared FFN 4096: the QKV projection (RoPE
+    epilogue), the split O-projection, the shared gate/up pair and the split shared down
+    projection all take the large-tile direct-to-LDS GEMMs (2048 rows give them a full chip of
+    tiles).  Both layers' caches are compared with the oracle's prefill; all experts are active
+    (top-k = E) so no router near-tie can move the second layer's inputs."""
+    dg = need_gpu()
+    shape = synth.ModelShape(n_layers=2, d_model=2048, n_q_heads=16, n_kv_heads=8, head_dim=128,
+                             n_experts=4, top_k=4, d_ff_expert=256, d_ff_shared=4096, vocab=1024)
+    w = synth.model_weights(shape, SEED + 9)
+    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=2048)
+    try:
+        n = 2048
+        toks = synth.tokens(n, shape.vocab, SEED, 900)
+        kv = dg.KV(shape, 1, n + 256)
+        print("prefill 2048 rows, d 2048, shared FFN 4096", flush=True)
+        m.prefill(torch.from_numpy(toks).cuda(), [n], kv)
+        torch.cuda.synchronize()
+        ck = [np.zeros((shape.n_kv_heads, n + 256, shape.head_dim)) for _ in range(shape.n_layers)]
+        cv = [np.zeros((shape.n_kv_heads, n + 256, shape.head_dim)) for _ in range(shape.n_layers)]
+        omodel.prefill(w, shape, toks, ck, cv, 0)
+        for l in range(shape.n_layers):
+            close(bf16_to_np(kv.k[l, 0, :, :n]), ck[l][:, :n], what=f"prefill K layer {l}", bf16_out=True)
+            close(bf16_to_np(kv.v[l, 0, :, :n]), cv[l][:, :n], what=f"prefill V layer {l}", bf16_out=True)
+    finally:
+        m.close()
