@@ -266,24 +266,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, int S) {
 // last stages re-load the final k-step into buffers nobody reads again), which keeps that
 // count exact.
 // ------------------------------------------------------------------------------------------
-constexpr int DL_RA = 256;  // weight rows per tile
-constexpr int DL_BK = 64;   // k per stage
+constexpr int DL_BK = 64;  // k per stage
 
-// BT tokens per tile (128 or 256), NW waves (8 or 16: 4 along the weight rows x NW / 4 along
-// the tokens); NS stages in the ring, as many as fit the 160 KB of LDS
-template <int BT, int NW>
-struct DlShape {
-  static constexpr int BLK = (DL_RA + BT) / 8;  // 1 KB blocks (8 rows x 128 B) per stage
+// Tile of RA weight rows (DUAL: RA / 2 gate + RA / 2 up rows) x BT tokens; NWA x NWT waves, each
+// multiplying RA / NWA weight rows by BT / NWT tokens; a ring of NS stages of (RA + BT) / 8 1 KB
+// blocks each (at most the 160 KB of LDS).
+template <int RA_, int BT_, int NWA_, int NWT_, int NS_>
+struct DlCfg {
+  static constexpr int RA = RA_, BT = BT_, NWA = NWA_, NWT = NWT_, NW = NWA_ * NWT_, NS = NS_;
+  static constexpr int BLK = (RA + BT) / 8;  // 1 KB blocks (8 rows x 128 B) per stage
   static_assert(BLK % NW == 0, "blocks per stage must split evenly over the waves");
-  static constexpr int PW = BLK / NW;           // blocks each wave loads per stage
-  static constexpr int NS = (160 * 1024) / (BLK * 1024);
-  static constexpr int WT = BT / (NW / 4);      // tokens per wave
-  static constexpr int TN = WT / 16;            // 16-token fragments per wave
+  static_assert(NS >= 2 && NS * BLK <= 160, "the ring must fit the LDS");
+  static constexpr int PW = BLK / NW;        // blocks each wave loads per stage
+  static constexpr int FM = RA / NWA / 16;   // 16-row weight fragments per wave
+  static constexpr int WT = BT / NWT;        // tokens per wave
+  static constexpr int TN = WT / 16;         // 16-token fragments per wave
 };
+// many rows: one work-group per CU, 256 x 128 (3 stages) or 256 x 256 (2 stages)
+using DlBig128 = DlCfg<256, 128, 4, 4, 3>;
+using DlBig256 = DlCfg<256, 256, 4, 4, 2>;
 
-template <int BT>
+template <class C>
 struct DlSmem {
-  uint16_t b[DlShape<BT, 8>::NS][DlShape<BT, 8>::BLK][512];
+  uint16_t b[C::NS][C::BLK][512];
 };
 
 // s_waitcnt with vmcnt = n (< 64) and lgkmcnt = 0 (expcnt not waited on).
@@ -293,36 +298,36 @@ DG_DEVICE void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | ((n >> 4) << 14));
 }
 
-template <int BT, bool DUAL, int NW = 8>
+template <class C, bool DUAL>
 struct DlMainloop {
-  using SH = DlShape<BT, NW>;
-  static constexpr int NS = SH::NS, DL_PW = SH::PW;
-  static constexpr int FM = 4, TN = SH::TN;  // 16-row fragments per wave (DUAL: 0-1 gate, 2-3 up)
+  static constexpr int NS = C::NS, PW = C::PW, FM = C::FM, TN = C::TN;
+  static_assert(!DUAL || FM % 2 == 0, "gate and up fragments in pairs");
+  // acc[i][j]: weight fragment i (DUAL: the first FM / 2 gate, the rest up) x token fragment j
   floatx4_t acc[FM][TN];
 
-  DG_DEVICE void run(DlSmem<BT>& sm, const uint16_t* w0, const uint16_t* w1, const uint16_t* x,
+  DG_DEVICE void run(DlSmem<C>& sm, const uint16_t* w0, const uint16_t* w1, const uint16_t* x,
                      int ldx, int n_tok, int t0, int K, int ldw) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wa = wave & 3, wt = wave >> 2;
+    const int wa = wave % C::NWA, wt = wave / C::NWA;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    // source of this lane in each block its wave loads: blocks 0-31 hold weight rows 8 j ..
-    // 8 j + 7 (DUAL: 0-15 gate, 16-31 up), the others tokens 8 (j - 32) ..
-    const uint16_t* src[DL_PW];
+    // source of this lane in each block its wave loads: blocks below RA / 8 hold weight rows
+    // 8 j .. 8 j + 7 (DUAL: the first half gate, the second up), the others tokens
+    const uint16_t* src[PW];
 #pragma unroll
-    for (int i = 0; i < DL_PW; ++i) {
-      const int j = wave * DL_PW + i;
+    for (int i = 0; i < PW; ++i) {
+      const int j = wave * PW + i;
       const int r16 = (j & 1) * 8 + (lane >> 3);
       const int kof = 8 * ((lane & 7) ^ ((r16 >> 1) & 7));
-      if (j < DL_RA / 8) {
+      if (j < C::RA / 8) {
         const int r = j * 8 + (lane >> 3);
-        src[i] = (DUAL && r >= DL_RA / 2) ? w1 + static_cast<long>(r - DL_RA / 2) * ldw + kof
+        src[i] = (DUAL && r >= C::RA / 2) ? w1 + static_cast<long>(r - C::RA / 2) * ldw + kof
                                           : w0 + static_cast<long>(r) * ldw + kof;
       } else {
         // rows past n_tok re-read the last row; their outputs are never stored
-        const int t = min(t0 + (j - DL_RA / 8) * 8 + (lane >> 3), n_tok - 1);
+        const int t = min(t0 + (j - C::RA / 8) * 8 + (lane >> 3), n_tok - 1);
         src[i] = x + static_cast<long>(t) * ldx + kof;
       }
     }
@@ -335,10 +340,10 @@ struct DlMainloop {
     const int nk = K / DL_BK;
     auto issue = [&](int st, int kt) {
 #pragma unroll
-      for (int i = 0; i < DL_PW; ++i)
+      for (int i = 0; i < PW; ++i)
         __builtin_amdgcn_global_load_lds(
             static_cast<const void*>(src[i] + kt * DL_BK),
-            (__attribute__((address_space(3))) void*)(&sm.b[st][wave * DL_PW + i][0]), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(&sm.b[st][wave * PW + i][0]), 16, 0, 0);
     };
     auto compute = [&](int st) {
 #pragma unroll
@@ -347,11 +352,12 @@ struct DlMainloop {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           // 16-row weight fragment index (pairs of blocks)
-          const int g = DUAL ? (i < 2 ? wa * 2 + i : DL_RA / 32 + wa * 2 + (i - 2)) : wa * FM + i;
+          constexpr int HF = FM / 2;
+          const int g = DUAL ? (i < HF ? wa * HF + i : C::RA / 32 + wa * HF + (i - HF)) : wa * FM + i;
           af[i] = ld16(&sm.b[st][2 * g][fofs[h]]);
         }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bx[j] = ld16(&sm.b[st][DL_RA / 8 + 2 * (wt * TN + j)][fofs[h]]);
+        for (int j = 0; j < TN; ++j) bx[j] = ld16(&sm.b[st][C::RA / 8 + 2 * (wt * TN + j)][fofs[h]]);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -364,7 +370,7 @@ struct DlMainloop {
       // this wave's loads of stage kt have landed (NS - 2 later stages may still be in
       // flight) and its fragment reads of stage kt - 1 are done; after the barrier the same
       // holds for every wave, so stage kt is complete and buffer (kt - 1) % NS is free
-      wait_vm_lgkm0<DL_PW * (NS - 2)>();
+      wait_vm_lgkm0<PW * (NS - 2)>();
       __builtin_amdgcn_s_barrier();
       issue((kt + NS - 1) % NS, min(kt + NS - 1, nk - 1));
       compute(kt % NS);
@@ -374,18 +380,18 @@ struct DlMainloop {
   }
 };
 
-template <int BT, int NW, int EPI>
-__global__ __launch_bounds__(64 * NW) void gemm_dl_kernel(GemmArgs a, int S) {
+template <class C, int EPI>
+__global__ __launch_bounds__(64 * C::NW) void gemm_dl_kernel(GemmArgs a, int S) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
-  constexpr int BF = DUAL ? DL_RA / 2 : DL_RA;  // output features per tile
-  constexpr int WF = BF / 4;                    // per wave
-  using ML = DlMainloop<BT, DUAL, NW>;
-  __shared__ DlSmem<BT> sm;
-  const int n_tt = (a.n_tok + BT - 1) / BT, n_ft = a.N / BF;
+  constexpr int BF = DUAL ? C::RA / 2 : C::RA;  // output features per tile
+  constexpr int WF = BF / C::NWA;               // per wave
+  using ML = DlMainloop<C, DUAL>;
+  __shared__ DlSmem<C> sm;
+  const int n_tt = (a.n_tok + C::BT - 1) / C::BT, n_ft = a.N / BF;
   const int L = xcd_remap(blockIdx.x, n_tt * n_ft * S);
   const int tile = L / S, z = L % S;
   const int ft = tile / n_tt, tt = tile % n_tt;
-  const int f0 = ft * BF, t0 = tt * BT;
+  const int f0 = ft * BF, t0 = tt * C::BT;
   const int kz = a.K / S, k0 = z * kz;
   const uint16_t* w0 = a.w0 + static_cast<long>(f0) * a.K + k0;
   const uint16_t* w1 = DUAL ? a.w1 + static_cast<long>(f0) * a.K + k0 : nullptr;
@@ -393,16 +399,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_dl_kernel(GemmArgs a, int S) {
   ml.run(sm, w0, w1, a.x + k0, a.ldx, a.n_tok, t0, kz, a.K);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wa = wave & 3, wt = wave >> 2;
+  const int wa = wave % C::NWA, wt = wave / C::NWA;
   constexpr int NF = DUAL ? ML::FM / 2 : ML::FM;
 #pragma unroll
   for (int fm = 0; fm < NF; ++fm)
 #pragma unroll
     for (int tn = 0; tn < ML::TN; ++tn) {
-      const int t = t0 + wt * ML::SH::WT + tn * 16 + (lane & 15);
+      const int t = t0 + wt * C::WT + tn * 16 + (lane & 15);
       const int f = f0 + wa * WF + fm * 16 + 4 * (lane >> 4);
       if (t >= a.n_tok) continue;
-      store_out<EPI>(a, S, z, t, f, ml.acc[fm][tn], ml.acc[DUAL ? fm + 2 : fm][tn]);
+      store_out<EPI>(a, S, z, t, f, ml.acc[fm][tn], ml.acc[DUAL ? fm + NF : fm][tn]);
     }
 }
 
@@ -542,21 +548,22 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   head_stats(a, ml.acc, f0 + wf * ML::WF, t0 + wt * ML::WT, (f0 + wf * ML::WF) / ML::WF, a.V / ML::WF);
 }
 
-// The same head on the large-tile direct-to-LDS mainloop: 256 vocab entries x BT rows per
-// work-group, 64 vocab entries (one statistics slice) x BT / (NW / 4) rows per wave.  Same k order and
-// slices, so the statistics are bit-identical to the kernel above.
-template <int BT, int NW>
-__global__ __launch_bounds__(64 * NW) void head_dl_kernel(HeadArgs a) {
-  using ML = DlMainloop<BT, false, NW>;
-  __shared__ DlSmem<BT> sm;
-  const int n_tt = (a.n_rows + BT - 1) / BT, n_ft = a.V / DL_RA;
+// The same head on the direct-to-LDS mainloop: 256 vocab entries x BT rows per work-group, 64
+// vocab entries (one statistics slice) x BT / NWT rows per wave.  Same k order and slices, so
+// the statistics are bit-identical to the kernel above.
+template <class C>
+__global__ __launch_bounds__(64 * C::NW) void head_dl_kernel(HeadArgs a) {
+  static_assert(C::RA / C::NWA == 64, "one statistics slice per wave");
+  using ML = DlMainloop<C, false>;
+  __shared__ DlSmem<C> sm;
+  const int n_tt = (a.n_rows + C::BT - 1) / C::BT, n_ft = a.V / C::RA;
   const int L = xcd_remap(blockIdx.x, n_tt * n_ft);
   const int ft = L / n_tt, tt = L % n_tt;
-  const int f0 = ft * DL_RA, t0 = tt * BT;
+  const int f0 = ft * C::RA, t0 = tt * C::BT;
   ML ml;
   ml.run(sm, a.w + static_cast<long>(f0) * a.K, nullptr, a.f, a.K, a.n_rows, t0, a.K, a.K);
-  const int wave = threadIdx.x >> 6, wa = wave & 3, wt = wave >> 2;
-  head_stats(a, ml.acc, f0 + wa * 64, t0 + wt * ML::SH::WT, (f0 + wa * 64) / 64, a.V / 64);
+  const int wave = threadIdx.x >> 6, wa = wave % C::NWA, wt = wave / C::NWA;
+  head_stats(a, ml.acc, f0 + wa * 64, t0 + wt * C::WT, (f0 + wa * 64) / 64, a.V / 64);
 }
 
 // One work-group (4 waves) per row: thread t merges slices t, t + 256, ... (two 16-byte loads
@@ -644,44 +651,52 @@ void pick_tile(const GemmArgs& a, int* bf, int* bt) {
   else { *bf = 32; *bt = 64; }
 }
 
-// From 1024 tokens the large-tile direct-to-LDS kernel, where the weights come in whole tiles
-// (256 rows; 128 for the SwiGLU pair), unsegmented, and the grid fills the chip: one
-// work-group per CU (its LDS ring takes most of the CU), so below 256 work-groups the LDS-tiled
-// kernel, which runs two per CU, is faster.  256-token tiles (1.5x the MFMAs per staged byte)
-// where there are 256 of them, else 128-token tiles.  Measured at 2048 tokens: QKV 54.6 ->
-// 43.5 us (128-token tiles), shared gate/up 100 -> 70 us (256-token tiles).
-template <int EPI>
-bool dl_eligible(const GemmArgs& a) {
-  constexpr int BF = (EPI == EPI_SWIGLU_BF16) ? DL_RA / 2 : DL_RA;
-  return a.n_tok >= 1024 && a.n_seg == 0 && a.N % BF == 0 && a.K % DL_BK == 0;
-}
+// Which direct-to-LDS configuration runs a GEMM (or none: the LDS-tiled kernel).
+//  * From 1024 tokens the large tiles, where the weights come in whole tiles (256 rows; 128 for
+//    the SwiGLU pair) and the grid fills the chip: one work-group per CU (its LDS ring takes
+//    most of the CU), so below 256 work-groups the LDS-tiled kernel, which runs two per CU, is
+//    faster.  256-token tiles (1.5x the MFMAs per staged byte) where there are 256 of them,
+//    else 128-token tiles.  Measured at 2048 tokens: QKV 54.6 -> 42.4 us (128-token tiles),
+//    shared gate/up 100 -> 72 us (256-token tiles).
+//  * Up to 256 tokens (one canvas) the QKV projection on 64 x 64 tiles with 8 waves and 8
+//    stages (in the step: 15.7 -> 14.2 us).  The other projections stay on the LDS-tiled
+//    kernel: 64 x 64 direct-to-LDS tiles with 4 waves and 4 stages were faster with the weights
+//    warm in the last-level cache (shared gate/up 21.6 -> 17.2 us, shared down at split 4
+//    14.6 -> 12.9 us) but not with cold weights inside the step (20.5 -> 21.0, 11.0 -> 11.4).
+using DlSmallW8 = DlCfg<64, 64, 2, 4, 8>;
+enum DlKind { DL_NONE = 0, DL_BIG128, DL_BIG256, DL_SMALL_W8 };
 
-template <int EPI, int BT>
+template <int EPI, class C>
 int dl_tiles(const GemmArgs& a) {
-  constexpr int BF = (EPI == EPI_SWIGLU_BF16) ? DL_RA / 2 : DL_RA;
-  return ((a.n_tok + BT - 1) / BT) * (a.N / BF);
+  constexpr int BF = (EPI == EPI_SWIGLU_BF16) ? C::RA / 2 : C::RA;
+  return ((a.n_tok + C::BT - 1) / C::BT) * (a.N / BF);
 }
 
-// 0: LDS-tiled kernel; else the large-tile kernel's token tile for split S
 template <int EPI>
-int dl_choice(const GemmArgs& a, int S) {
-  if (!dl_eligible<EPI>(a)) return 0;
-  if (S == 1 && dl_tiles<EPI, 256>(a) >= 256) return 256;
-  if (dl_tiles<EPI, 128>(a) * S >= 256) return 128;
-  return 0;
+int dl_kind(const GemmArgs& a, int S) {
+  constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
+  constexpr bool F32 = (EPI == EPI_ADD_F32 || EPI == EPI_STORE_F32);
+  if (a.n_seg != 0 || a.K % (DL_BK * S) != 0) return DL_NONE;
+  if (a.n_tok <= 256) return (!DUAL && !F32 && a.N % 64 == 0) ? DL_SMALL_W8 : DL_NONE;
+  if (a.n_tok < 1024 || a.N % (DUAL ? 128 : 256) != 0) return DL_NONE;
+  if (S == 1 && dl_tiles<EPI, DlBig256>(a) >= 256) return DL_BIG256;
+  if (dl_tiles<EPI, DlBig128>(a) * S >= 256) return DL_BIG128;
+  return DL_NONE;
+}
+
+template <int EPI, class C>
+void launch_dl(const GemmArgs& a, int S, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_dl_kernel<C, EPI>), dim3(dl_tiles<EPI, C>(a) * S), dim3(64 * C::NW), 0, s, a, S);
 }
 
 template <int EPI>
 void launch_epi(const GemmArgs& a, hipStream_t s) {
   const int S = a.split > 1 ? a.split : 1;
-  const int dl = dl_choice<EPI>(a, S);
-  if (dl == 256) {
-    hipLaunchKernelGGL((gemm_dl_kernel<256, 16, EPI>), dim3(dl_tiles<EPI, 256>(a) * S), dim3(1024), 0, s, a, S);
-    return;
-  }
-  if (dl == 128) {
-    hipLaunchKernelGGL((gemm_dl_kernel<128, 16, EPI>), dim3(dl_tiles<EPI, 128>(a) * S), dim3(1024), 0, s, a, S);
-    return;
+  switch (dl_kind<EPI>(a, S)) {
+    case DL_BIG256: launch_dl<EPI, DlBig256>(a, S, s); return;
+    case DL_BIG128: launch_dl<EPI, DlBig128>(a, S, s); return;
+    case DL_SMALL_W8: launch_dl<EPI, DlSmallW8>(a, S, s); return;
+    default: break;
   }
   int bf, bt;
   pick_tile<EPI>(a, &bf, &bt);
@@ -698,14 +713,14 @@ int split_for(const GemmArgs& a, long cap) {
   constexpr int NA = (EPI == EPI_SWIGLU_BF16) ? 2 : 1;
   // the large-tile kernel: unsplit when it has a chip's worth of tiles, else split K until
   // its 128-token tiles do (one work-group per CU)
-  if (dl_choice<EPI>(a, 1) == 256) return 1;
-  if (dl_eligible<EPI>(a)) {
-    const int t128 = dl_tiles<EPI, 128>(a);
+  if (dl_kind<EPI>(a, 1) == DL_BIG256) return 1;
+  if (a.n_tok >= 1024) {
+    const int t128 = dl_tiles<EPI, DlBig128>(a);
     int S = 1;
     while (S < kMaxParts && t128 * S < 256 && (a.K / BK) % (S * 2) == 0 && a.K / (S * 2) >= 16 * BK &&
            static_cast<long>(S) * 2 * NA * a.n_tok * a.N <= cap)
       S *= 2;
-    if (dl_choice<EPI>(a, S) != 0) return S;
+    if (dl_kind<EPI>(a, S) != DL_NONE) return S;
   }
   int bf, bt;
   pick_tile<EPI>(a, &bf, &bt);
@@ -755,9 +770,9 @@ void launch_swiglu_reduce(const float* part, long part_stride, int split, uint16
 // streamed by half as many work-groups as with 64-row tiles).  The statistics do not depend on
 // the tiling (same k order, same 64-entry slices).
 void launch_head(const HeadArgs& a, hipStream_t s) {
-  if (a.V % DL_RA == 0 && a.K % DL_BK == 0) {
-    const int G = ((a.n_rows + 255) / 256) * (a.V / DL_RA);
-    hipLaunchKernelGGL((head_dl_kernel<256, 16>), dim3(G), dim3(1024), 0, s, a);
+  if (a.V % DlBig256::RA == 0 && a.K % DL_BK == 0) {
+    const int G = ((a.n_rows + 255) / 256) * (a.V / DlBig256::RA);
+    hipLaunchKernelGGL((head_dl_kernel<DlBig256>), dim3(G), dim3(64 * DlBig256::NW), 0, s, a);
     return;
   }
   const int G = ((a.n_rows + 127) / 128) * (a.V / 128);
