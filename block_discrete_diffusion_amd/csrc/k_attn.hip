@@ -251,11 +251,6 @@ void attention_kernel(AttnArgs a) {
   // Keys come in two ranges with one base pointer each (uniform, so addresses are a scalar
   // base plus a lane offset): the cached prefix [0, n_cache) and the canvas [n_cache, n_keys).
   // Keys past a range end re-read its last key (every load is unconditional, so wait counts
-  // stay exact) and are masked to -inf.
-  //
-  // Keys come in two ranges with one base pointer each (uniform, so addresses are a scalar
-  // base plus a lane offset): the cached prefix [0, n_cache) and the canvas [n_cache, n_keys).
-  // Keys past a range end re-read its last key (every load is unconditional, so wait counts
   // stay exact) and are masked to -inf.  The next block's global loads are in flight while
   // the current one is computed from LDS.
   auto run_range = [&](const uint16_t* kbase, const uint16_t* vbase, int key0, int kb_lo, int kb_hi) {
