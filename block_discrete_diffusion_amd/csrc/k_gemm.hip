@@ -658,11 +658,13 @@ void pick_tile(const GemmArgs& a, int* bf, int* bt) {
 //    faster.  256-token tiles (1.5x the MFMAs per staged byte) where there are 256 of them,
 //    else 128-token tiles.  Measured at 2048 tokens: QKV 54.6 -> 42.4 us (128-token tiles),
 //    shared gate/up 100 -> 72 us (256-token tiles).
-//  * Up to 256 tokens (one canvas) the QKV projection on 64 x 64 tiles with 8 waves and 8
-//    stages (in the step: 15.7 -> 14.2 us).  The other projections stay on the LDS-tiled
-//    kernel: 64 x 64 direct-to-LDS tiles with 4 waves and 4 stages were faster with the weights
-//    warm in the last-level cache (shared gate/up 21.6 -> 17.2 us, shared down at split 4
-//    14.6 -> 12.9 us) but not with cold weights inside the step (20.5 -> 21.0, 11.0 -> 11.4).
+//  * Up to 256 tokens (one canvas) 64 x 64 tiles with 8 waves and 8 stages for the QKV
+//    projection (in the step: 15.7 -> 14.2 us) and, split in two K slices, for the fp32
+//    projections (O-projection 11.1 -> 10.6 us, shared down at split 2 instead of 4
+//    15.7 -> 15.1 us, and the combine, which then adds two slices fewer, 9.2 -> 8.3 us).  The
+//    SwiGLU pair stays on the LDS-tiled kernel: 64 x 64 direct-to-LDS tiles with 4 waves and 4
+//    stages were faster with the weights warm in the last-level cache (21.6 -> 17.2 us) but not
+//    with the cold weights inside the step (20.5 -> 21.0 us).
 using DlSmallW8 = DlCfg<64, 64, 2, 4, 8>;
 enum DlKind { DL_NONE = 0, DL_BIG128, DL_BIG256, DL_SMALL_W8 };
 
@@ -675,9 +677,8 @@ int dl_tiles(const GemmArgs& a) {
 template <int EPI>
 int dl_kind(const GemmArgs& a, int S) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
-  constexpr bool F32 = (EPI == EPI_ADD_F32 || EPI == EPI_STORE_F32);
   if (a.n_seg != 0 || a.K % (DL_BK * S) != 0) return DL_NONE;
-  if (a.n_tok <= 256) return (!DUAL && !F32 && a.N % 64 == 0) ? DL_SMALL_W8 : DL_NONE;
+  if (a.n_tok <= 256) return (!DUAL && a.N % 64 == 0) ? DL_SMALL_W8 : DL_NONE;
   if (a.n_tok < 1024 || a.N % (DUAL ? 128 : 256) != 0) return DL_NONE;
   if (S == 1 && dl_tiles<EPI, DlBig256>(a) >= 256) return DL_BIG256;
   if (dl_tiles<EPI, DlBig128>(a) * S >= 256) return DL_BIG128;
@@ -711,6 +712,8 @@ void launch_epi(const GemmArgs& a, hipStream_t s) {
 template <int EPI>
 int split_for(const GemmArgs& a, long cap) {
   constexpr int NA = (EPI == EPI_SWIGLU_BF16) ? 2 : 1;
+  // one canvas: the split fp32 projections on the small tiles, in two K slices
+  if (a.n_tok <= 256 && dl_kind<EPI>(a, 2) == DL_SMALL_W8 && 2L * NA * a.n_tok * a.N <= cap) return 2;
   // the large-tile kernel: unsplit when it has a chip's worth of tiles, else split K until
   // its 128-token tiles do (one work-group per CU)
   if (dl_kind<EPI>(a, 1) == DL_BIG256) return 1;
