@@ -662,11 +662,12 @@ void pick_tile(const GemmArgs& a, int* bf, int* bt) {
 //    projection (in the step: 15.7 -> 14.2 us) and, split in two K slices, for the fp32
 //    projections (O-projection 11.1 -> 10.6 us, shared down at split 2 instead of 4
 //    15.7 -> 15.1 us, and the combine, which then adds two slices fewer, 9.2 -> 8.3 us).  The
-//    SwiGLU pair stays on the LDS-tiled kernel: 64 x 64 direct-to-LDS tiles with 4 waves and 4
-//    stages were faster with the weights warm in the last-level cache (21.6 -> 17.2 us) but not
-//    with the cold weights inside the step (20.5 -> 21.0 us).
+//    SwiGLU pair on 64 + 64 gate/up rows x 64 tokens with 8 waves (4 x 2) and 6 stages:
+//    22.5 -> 20.2 us in the step; 64 x 64 tiles were faster only with the weights warm in the
+//    last-level cache.
 using DlSmallW8 = DlCfg<64, 64, 2, 4, 8>;
-enum DlKind { DL_NONE = 0, DL_BIG128, DL_BIG256, DL_SMALL_W8 };
+using DlSmallPair = DlCfg<128, 64, 4, 2, 6>;
+enum DlKind { DL_NONE = 0, DL_BIG128, DL_BIG256, DL_SMALL_W8, DL_SMALL_PAIR };
 
 template <int EPI, class C>
 int dl_tiles(const GemmArgs& a) {
@@ -678,7 +679,7 @@ template <int EPI>
 int dl_kind(const GemmArgs& a, int S) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
   if (a.n_seg != 0 || a.K % (DL_BK * S) != 0) return DL_NONE;
-  if (a.n_tok <= 256) return (!DUAL && a.N % 64 == 0) ? DL_SMALL_W8 : DL_NONE;
+  if (a.n_tok <= 256) return (a.N % 64 != 0) ? DL_NONE : DUAL ? DL_SMALL_PAIR : DL_SMALL_W8;
   if (a.n_tok < 1024 || a.N % (DUAL ? 128 : 256) != 0) return DL_NONE;
   if (S == 1 && dl_tiles<EPI, DlBig256>(a) >= 256) return DL_BIG256;
   if (dl_tiles<EPI, DlBig128>(a) * S >= 256) return DL_BIG128;
@@ -697,6 +698,7 @@ void launch_epi(const GemmArgs& a, hipStream_t s) {
     case DL_BIG256: launch_dl<EPI, DlBig256>(a, S, s); return;
     case DL_BIG128: launch_dl<EPI, DlBig128>(a, S, s); return;
     case DL_SMALL_W8: launch_dl<EPI, DlSmallW8>(a, S, s); return;
+    case DL_SMALL_PAIR: launch_dl<EPI, DlSmallPair>(a, S, s); return;
     default: break;
   }
   int bf, bt;
