@@ -697,8 +697,12 @@ void launch_epi(const GemmArgs& a, hipStream_t s) {
   switch (dl_kind<EPI>(a, S)) {
     case DL_BIG256: launch_dl<EPI, DlBig256>(a, S, s); return;
     case DL_BIG128: launch_dl<EPI, DlBig128>(a, S, s); return;
-    case DL_SMALL_W8: launch_dl<EPI, DlSmallW8>(a, S, s); return;
-    case DL_SMALL_PAIR: launch_dl<EPI, DlSmallPair>(a, S, s); return;
+    case DL_SMALL_W8:
+      if constexpr (EPI != EPI_SWIGLU_BF16) { launch_dl<EPI, DlSmallW8>(a, S, s); return; }
+      break;
+    case DL_SMALL_PAIR:
+      if constexpr (EPI == EPI_SWIGLU_BF16) { launch_dl<EPI, DlSmallPair>(a, S, s); return; }
+      break;
     default: break;
   }
   int bf, bt;
