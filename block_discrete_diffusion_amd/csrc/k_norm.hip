@@ -109,7 +109,11 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
 
 // Residual update + FFN norm + router + top-k, one work-group (8 waves) per R rows.
 //  - the router weights of the wave's experts (first round of columns) are requested before
-//    anything else, so their latency hides behind the norm;
+//    the norm, so their latency hides behind it; with one row per group the row's residual and
+//    slices are requested first (the wait for them then leaves the weights in flight), and no
+//    global store precedes a barrier (a barrier after a store waits for every memory
+//    operation of the wave, the weight loads included): h and the bf16 x are written after
+//    the last one;
 //  - per row, every load (residual, its split-K slices) is issued before the reduction;
 //    h += slices (z order, written back); x = h * rsqrt(mean h^2 + eps) * gain in float32;
 //    the bf16 copy of x feeds the experts and the float32 x is kept in LDS;
@@ -147,23 +151,54 @@ __global__ __launch_bounds__(512) void norm_router_kernel(
         wv[jj][e] = ld16(wr + static_cast<long>(ee) * d + c);
       }
   };
-  load_w(0);
-
+  // residual and slices of row rr, chunk i (uniform row guard; lanes past d load nothing)
   floatx4_t v[R][NCH];
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    if (rr >= nr) break;
-    float* hr = h + static_cast<long>(r0 + rr) * d;
-    floatx4_t pz[kMaxParts][NCH];
+  constexpr int EP = (R == 1) ? kMaxParts : 1;  // one row: its slices are loaded up front
+  floatx4_t pe[EP][NCH];
+  auto load_row = [&](int rr, floatx4_t (&pz)[EP][NCH]) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = (tid + 512 * i) * 4;
       const bool ok = c < d;
-      v[rr][i] = ok ? *reinterpret_cast<const floatx4_t*>(hr + c) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+      v[rr][i] = ok ? *reinterpret_cast<const floatx4_t*>(h + static_cast<long>(r0 + rr) * d + c)
+                    : floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int z = 0; z < kMaxParts; ++z)
+      for (int z = 0; z < EP; ++z)
         if (z < n_part && ok)
           pz[z][i] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + static_cast<long>(r0 + rr) * d + c);
+    }
+  };
+  // the norm gain, also ahead of the weights (a wait for a load waits for every older one)
+  floatx4_t gv[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (tid + 512 * i) * 4;
+    gv[i] = c < d ? *reinterpret_cast<const floatx4_t*>(gain + c) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if constexpr (R == 1) load_row(0, pe);
+  load_w(0);
+
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    if (rr >= nr) break;
+    floatx4_t pz[kMaxParts][NCH];
+    if constexpr (R == 1) {
+#pragma unroll
+      for (int z = 0; z < kMaxParts; ++z)
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) pz[z][i] = pe[z][i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = (tid + 512 * i) * 4;
+        const bool ok = c < d;
+        v[rr][i] = ok ? *reinterpret_cast<const floatx4_t*>(h + static_cast<long>(r0 + rr) * d + c)
+                      : floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int z = 0; z < kMaxParts; ++z)
+          if (z < n_part && ok)
+            pz[z][i] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + static_cast<long>(r0 + rr) * d + c);
+      }
     }
     if (n_part > 0) {
 #pragma unroll
@@ -173,7 +208,6 @@ __global__ __launch_bounds__(512) void norm_router_kernel(
 #pragma unroll
         for (int z = 0; z < kMaxParts; ++z)
           if (z < n_part) v[rr][i] += pz[z][i];
-        *reinterpret_cast<floatx4_t*>(hr + c) = v[rr][i];
       }
     }
     float ss = 0.f;
@@ -185,6 +219,7 @@ __global__ __launch_bounds__(512) void norm_router_kernel(
     if (lane == 0) red[rr][w] = ss;
   }
   __syncthreads();
+  u32x2_t xb[R][NCH];
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     if (rr >= nr) break;
@@ -195,16 +230,26 @@ __global__ __launch_bounds__(512) void norm_router_kernel(
     for (int i = 0; i < NCH; ++i) {
       const int c = (tid + 512 * i) * 4;
       if (c >= d) continue;
-      const floatx4_t g = *reinterpret_cast<const floatx4_t*>(gain + c);
       floatx4_t x;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = v[rr][i][q] * inv * g[q];
-      *reinterpret_cast<u32x2_t*>(bout + static_cast<long>(r0 + rr) * d + c) =
-          u32x2_t{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])};
+      for (int q = 0; q < 4; ++q) x[q] = v[rr][i][q] * inv * gv[i][q];
+      xb[rr][i] = u32x2_t{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])};
       *reinterpret_cast<floatx4_t*>(&xs[rr][c]) = x;
     }
   }
   __syncthreads();
+  // global stores only now: the updated residual (when slices were added) and the bf16 x
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    if (rr >= nr) break;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = (tid + 512 * i) * 4;
+      if (c >= d) continue;
+      if (n_part > 0) *reinterpret_cast<floatx4_t*>(h + static_cast<long>(r0 + rr) * d + c) = v[rr][i];
+      *reinterpret_cast<u32x2_t*>(bout + static_cast<long>(r0 + rr) * d + c) = xb[rr][i];
+    }
+  }
 
   // router: 8 experts per wave, JR row chunks of 512 elements per round of loads
   float p[R][8];
