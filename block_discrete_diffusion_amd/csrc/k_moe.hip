@@ -395,7 +395,9 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const uint16_t* __re
 // Un-permute + residual, one work-group (8 waves) per row t:
 // h[t] += sum_z part_z[t] + sum_j gate[t][j] * y[inv[t*k+j]]   (z then j in order);
 // with a gain it also writes the next block's normed input out = bf16(rmsnorm(h[t]) * gain),
-// which saves a pass over h.  All of a thread's loads are issued before any arithmetic.
+// which saves a pass over h.  All of a thread's loads (the gain too) are issued before any
+// arithmetic, and with a gain h is stored after the norm's barrier: a barrier after a global
+// store waits for that store.
 template <int NCH>  // 4-element chunks per thread: ceil(d / 2048)
 __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
                                                           const float* __restrict__ part,
@@ -409,25 +411,31 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float* hr = h + static_cast<long>(t) * d;
   constexpr int KJ = 8;  // routed slots held in registers; more are read in the second loop
+  // every load is unconditional (slots past top_k and slices past n_part re-read the last
+  // valid one and are not added): loads under a condition would each get a wait of their own
+  const int kl = min(top_k, KJ) - 1;
   int pj[KJ];
   float gj[KJ];
 #pragma unroll
-  for (int j = 0; j < KJ; ++j)
-    if (j < top_k) {
-      pj[j] = inv[static_cast<long>(t) * top_k + j];
-      gj[j] = gates[static_cast<long>(t) * top_k + j];
-    }
-  floatx4_t v[NCH], pz[kMaxParts][NCH], yj[KJ][NCH];
+  for (int j = 0; j < KJ; ++j) {
+    pj[j] = inv[static_cast<long>(t) * top_k + min(j, kl)];
+    gj[j] = gates[static_cast<long>(t) * top_k + min(j, kl)];
+  }
+  const float* zp[kMaxParts];
+#pragma unroll
+  for (int z = 0; z < kMaxParts; ++z)
+    zp[z] = n_part > 0 ? part + min(z, n_part - 1) * part_stride + static_cast<long>(t) * d : hr;
+  const float* gsrc = gain ? gain : hr;
+  floatx4_t v[NCH], pz[kMaxParts][NCH], yj[KJ][NCH], gv[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = min((tid + 512 * i) * 4, d - 4);  // clamped; chunks past d are not stored
     v[i] = *reinterpret_cast<const floatx4_t*>(hr + c);
+    gv[i] = *reinterpret_cast<const floatx4_t*>(gsrc + c);
 #pragma unroll
-    for (int z = 0; z < kMaxParts; ++z)
-      if (z < n_part) pz[z][i] = *reinterpret_cast<const floatx4_t*>(part + z * part_stride + static_cast<long>(t) * d + c);
+    for (int z = 0; z < kMaxParts; ++z) pz[z][i] = *reinterpret_cast<const floatx4_t*>(zp[z] + c);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j)
-      if (j < top_k) yj[j][i] = *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(pj[j]) * d + c);
+    for (int j = 0; j < KJ; ++j) yj[j][i] = *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(pj[j]) * d + c);
   }
   float ss = 0.f;
 #pragma unroll
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
     }
     v[i] += acc;
     if (c < d) {
-      *reinterpret_cast<floatx4_t*>(hr + c) = v[i];
+      if (!gain) *reinterpret_cast<floatx4_t*>(hr + c) = v[i];
       ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
     }
   }
@@ -461,7 +469,8 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
   for (int i = 0; i < NCH; ++i) {
     const int c = (tid + 512 * i) * 4;
     if (c >= d) continue;
-    const floatx4_t g = *reinterpret_cast<const floatx4_t*>(gain + c);
+    *reinterpret_cast<floatx4_t*>(hr + c) = v[i];
+    const floatx4_t g = gv[i];
     *reinterpret_cast<u32x2_t*>(out + static_cast<long>(t) * d + c) =
         u32x2_t{pack_bf2(v[i][0] * rinv * g[0], v[i][1] * rinv * g[1]), pack_bf2(v[i][2] * rinv * g[2], v[i][3] * rinv * g[3])};
   }
