@@ -24,7 +24,7 @@ DG_STEP_HIDDEN_IN, DG_STEP_NO_HEAD, DG_STEP_HEAD_ONLY = 1, 2, 4
 
 EXPORTS = ["dg_create", "dg_destroy", "dg_last_error", "dg_temperature", "dg_prefill_causal",
            "dg_canvas_init", "dg_denoise_step", "dg_sample_commit", "dg_commit_block",
-           "dg_timing_enable", "dg_timing_read", "dg_debug_set_canvas_kv"]
+           "dg_timing_enable", "dg_timing_read", "dg_debug_set_canvas_kv", "dg_quantize_e4m3_rows"]
 
 vp = C.c_void_p
 

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "dg.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dg_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary_calls():

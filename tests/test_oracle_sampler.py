@@ -104,8 +104,10 @@ def test_commit_count_and_fixed_committed_invariants():
         return z
 
     c = cfg()
+    pos = 64 + np.arange(256)  # _run's positions
     _, _, hist = _run(z_fn, c, V=V)
-    for x0, c0, x1, c1, status, st in hist:
+    n_dropped = 0
+    for step, (x0, c0, x1, c1, status, st) in enumerate(hist):
         U = int((~c0).sum())
         renoised_committed = int((c0 & ~c1).sum())
         assert c1.sum() == c0.sum() - renoised_committed + min(16, U)
@@ -114,12 +116,14 @@ def test_commit_count_and_fixed_committed_invariants():
         assert np.array_equal(x0[kept], x1[kept])
         # re-noised committed positions got the step's fresh token
         drop = c0 & ~c1
-        if drop.any():
-            s = status
+        fresh = philox.token_draw(c.seed, 0, pos, step, philox.RENOISE, V)
+        assert np.array_equal(x1[drop], fresh[drop])
+        n_dropped += int(drop.sum())
         # newly committed positions hold their candidate
         new = ~c0 & c1
         assert np.array_equal(x1[new], st["cand"][new])
         assert new.sum() == min(16, U)
+    assert n_dropped > 0  # the mixed logits do re-noise some committed positions
 
 
 def test_selection_is_topm_by_confidence():
