@@ -75,6 +75,7 @@ struct dg_ctx {
   float* gpart = nullptr;      // split-K partial slices of the dense GEMMs
   float* rope = nullptr;       // [r_max][D/2][2] cos/sin of the rows of the current step
   int32_t* tok = nullptr;      // [r_canvas] canvas tokens of a slot-mapped call, in call order
+  uint32_t* dev_err = nullptr; // sticky device-side error bits (kDevErr*), read by dg_device_errors
   std::vector<int32_t> last_slots;  // slots of the requests whose canvas K/V the workspace holds
   uint16_t* ck = nullptr;      // [L][max_batch][Hkv][C][D]
   uint16_t* cv = nullptr;
@@ -291,6 +292,16 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   if (m.expert_fp8) { g1.wp8 = c->pk1_8[l]; g1.wscale0 = c->sc_gate[l]; g1.wscale1 = c->sc_up[l]; }
   g1.out_bf16 = c->act; g1.ldo = m.d_ff_expert; g1.n_exp = m.n_experts;
   timed(c, "moe_gemm1_swiglu", s, [&] { launch_moe_gemm1(g1, routes / m.n_experts, s); });
+  // the route tables are complete once the gate/up GEMM has run (it writes them when it ranks)
+  if (dbg && dbg->route_offs)
+    (void)hipMemcpyAsync(dbg->route_offs + static_cast<long>(l) * (m.n_experts + 1), c->offs,
+                         sizeof(int32_t) * (m.n_experts + 1), hipMemcpyDeviceToDevice, s);
+  if (dbg && dbg->route_perm)
+    (void)hipMemcpyAsync(dbg->route_perm + static_cast<long>(l) * routes, c->perm, sizeof(int32_t) * routes,
+                         hipMemcpyDeviceToDevice, s);
+  if (dbg && dbg->route_inv)
+    (void)hipMemcpyAsync(dbg->route_inv + static_cast<long>(l) * routes, c->inv, sizeof(int32_t) * routes,
+                         hipMemcpyDeviceToDevice, s);
   MoeArgs g2{};
   g2.x = c->act; g2.ldx = m.d_ff_expert; g2.perm = c->perm; g2.top_k = m.top_k; g2.offs = c->offs;
   g2.wp = c->pk2[l]; g2.K = m.d_ff_expert; g2.N = d; g2.out_f32 = c->y; g2.ldo = d;
@@ -408,7 +419,8 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
             c->alloc(&c->head_part, static_cast<long>(c->r_canvas) * (m.vocab / kHeadSlice) * 8) &&
             c->alloc(&c->ck, ckv) && c->alloc(&c->cv, ckv) &&
             c->alloc(&c->gpart, kGemmPartFloats) &&
-            c->alloc(&c->rope, R * m.head_dim) && c->alloc(&c->tok, c->r_canvas);
+            c->alloc(&c->rope, R * m.head_dim) && c->alloc(&c->tok, c->r_canvas) &&
+            c->alloc(&c->dev_err, 1) && hipMemset(c->dev_err, 0, sizeof(uint32_t)) == hipSuccess;
   // expert banks, repacked once into the MFMA fragment order the expert GEMMs stream
   const long ew = static_cast<long>(m.n_experts) * m.d_ff_expert * m.d_model;
   const int E = m.n_experts, F = m.d_ff_expert;
@@ -512,8 +524,8 @@ int dg_prefill_causal(dg_ctx* c, const int32_t* tokens, const int32_t* n_new, in
   for (int b = 0; b < batch; ++b) {
     for (int done = 0; done < n_new[b];) {
       const int n = std::min(c->max_prefill, n_new[b] - done);
-      launch_embed(tokens + tok_ofs + done, c->w.embed, c->h, n, m.d_model, c->layers[0].attn_norm,
-                   m.rms_eps, c->a, s);
+      launch_embed(tokens + tok_ofs + done, c->w.embed, c->h, n, m.d_model, m.vocab, c->dev_err,
+                   c->layers[0].attn_norm, m.rms_eps, c->a, s);
       const int32_t len_b = kv->len[b] + done;
       if (m.rope_theta != 0.f) launch_rope_table(make_map(n, 1, &len_b), n, m.head_dim, m.rope_theta, c->rope, s);
       for (int l = 0; l < m.n_layers; ++l) {
@@ -565,7 +577,8 @@ static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
       launch_rmsnorm(c->h, c->layers[0].attn_norm, m.rms_eps, c->a, rows, d, s);
     } else {
       timed(c, "embed_norm", s, [&] {
-        launch_embed(canvas, c->w.embed, c->h, rows, d, c->layers[0].attn_norm, m.rms_eps, c->a, s);
+        launch_embed(canvas, c->w.embed, c->h, rows, d, m.vocab, c->dev_err, c->layers[0].attn_norm,
+                     m.rms_eps, c->a, s);
       });
     }
     if (m.rope_theta != 0.f)
@@ -611,8 +624,8 @@ static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
   ha.part = c->head_part;
   ha.dbg_logits = dbg ? dbg->logits : nullptr;
   timed(c, "head_lse_gumbel", s, [&] { launch_head(ha, s); });
-  timed(c, "head_merge", s, [&] { launch_head_merge(c->head_part, rows, m.vocab / kHeadSlice, kHeadSlice, canvas, out->cand,
-                    out->t_cand, out->t_cur, out->lse, out->entropy, ha.map, s); });
+  timed(c, "head_merge", s, [&] { launch_head_merge(c->head_part, rows, m.vocab / kHeadSlice, kHeadSlice, canvas,
+                    c->dev_err, out->cand, out->t_cand, out->t_cur, out->lse, out->entropy, ha.map, s); });
   return DG_OK;
 }
 
@@ -767,6 +780,19 @@ int dg_timing_read(dg_ctx* c, dg_kernel_time* out, int32_t max) {
   const int n = std::min<int>(max, static_cast<int>(acc.size()));
   for (int i = 0; i < n; ++i) out[i] = acc[i];
   return n;
+}
+
+int dg_device_errors(dg_ctx* c, uint32_t* flags, hipStream_t s) {
+  if (!c) return DG_ERR_ARG;
+  if (!flags) return c->fail(DG_ERR_ARG, "device_errors: null pointer");
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, c->dev_err, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return c->fail(DG_ERR_HIP, "device_errors: read failed");
+  if (v != 0 && hipMemsetAsync(c->dev_err, 0, sizeof v, s) != hipSuccess)
+    return c->fail(DG_ERR_HIP, "device_errors: clear failed");
+  *flags = v;
+  return check_hip(c, "device_errors");
 }
 
 int dg_debug_set_canvas_kv(dg_ctx* c, const uint16_t* k, const uint16_t* v, int32_t batch,

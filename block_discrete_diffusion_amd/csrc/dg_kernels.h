@@ -19,10 +19,14 @@ struct RowMap {
   int32_t slot[kMaxBatch];
 };
 
+// Bits of the sticky device-side error word (the workspace's err, read by dg_device_errors).
+constexpr uint32_t kDevErrTokenRange = 1u;  // a token id outside [0, vocab) was clamped
+
 // ---- k_norm.hip
-// h = E[tok] as float32; with a gain also out = bf16(rmsnorm(h) * gain) (the first layer's input)
-void launch_embed(const int32_t* tok, const uint16_t* embed, float* h, int rows, int d,
-                  const float* gain, float eps, uint16_t* out, hipStream_t s);
+// h = E[tok] as float32; with a gain also out = bf16(rmsnorm(h) * gain) (the first layer's
+// input).  Ids outside [0, vocab) are clamped and set kDevErrTokenRange in *err.
+void launch_embed(const int32_t* tok, const uint16_t* embed, float* h, int rows, int d, int vocab,
+                  uint32_t* err, const float* gain, float eps, uint16_t* out, hipStream_t s);
 void launch_rmsnorm(const float* h, const float* gain, float eps, uint16_t* out, int rows, int d,
                     hipStream_t s);
 void launch_f32_to_bf16(const float* in, uint16_t* out, long n, hipStream_t s);
@@ -91,9 +95,10 @@ struct HeadArgs {
   float* dbg_logits;                  // optional [rows][V]
 };
 void launch_head(const HeadArgs& a, hipStream_t s);
+// cur_tok ids outside [0, n_slices * slice_w) are clamped and set kDevErrTokenRange in *err
 void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
-                       const int32_t* cur_tok, int32_t* cand, float* t_cand, float* t_cur,
-                       float* lse, float* ent, const RowMap& map, hipStream_t s);
+                       const int32_t* cur_tok, uint32_t* err, int32_t* cand, float* t_cand,
+                       float* t_cur, float* lse, float* ent, const RowMap& map, hipStream_t s);
 // dst[b][i] = src[map.slot[b]][i] for the map's requests (rows_per_req ints each)
 void launch_gather_rows(const int32_t* src, int32_t* dst, const RowMap& map, hipStream_t s);
 

@@ -572,6 +572,7 @@ __global__ __launch_bounds__(64 * C::NW) void head_dl_kernel(HeadArgs a) {
 __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict__ part, int n_rows,
                                                          int n_slices, int slice_w,
                                                          const int32_t* __restrict__ cur_tok,
+                                                         uint32_t* __restrict__ err,
                                                          int32_t* cand, float* t_cand, float* t_cur,
                                                          float* lse, float* ent, RowMap map) {
   constexpr int PER = 8;  // slices per thread held in registers (n_slices <= 2048)
@@ -619,7 +620,11 @@ __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict
   ent[orow] = l - r.st / r.s;
   cand[orow] = r.bi;
   t_cand[orow] = r.bt;
-  const int x = cur_tok[row];
+  int x = cur_tok[row];
+  if (static_cast<unsigned>(x) >= static_cast<unsigned>(n_slices * slice_w)) {  // never read past the row
+    *err = kDevErrTokenRange;
+    x = x < 0 ? 0 : n_slices * slice_w - 1;
+  }
   t_cur[orow] = part[(static_cast<long>(row) * n_slices + x / slice_w) * 8 + 6];
 }
 
@@ -789,10 +794,10 @@ void launch_head(const HeadArgs& a, hipStream_t s) {
 }
 
 void launch_head_merge(const float* part, int n_rows, int n_slices, int slice_w,
-                       const int32_t* cur_tok, int32_t* cand, float* t_cand, float* t_cur,
-                       float* lse, float* ent, const RowMap& map, hipStream_t s) {
+                       const int32_t* cur_tok, uint32_t* err, int32_t* cand, float* t_cand,
+                       float* t_cur, float* lse, float* ent, const RowMap& map, hipStream_t s) {
   hipLaunchKernelGGL(head_merge_kernel, dim3(n_rows), dim3(256), 0, s, part, n_rows, n_slices,
-                     slice_w, cur_tok, cand, t_cand, t_cur, lse, ent, map);
+                     slice_w, cur_tok, err, cand, t_cand, t_cur, lse, ent, map);
 }
 
 // One work-group per output row: row r of head h (q heads, then k heads) takes source row

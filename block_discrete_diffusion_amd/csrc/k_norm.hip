@@ -12,15 +12,23 @@ namespace {
 
 // Embedding gather h = E[tok] (bf16 rows widened to float32), one work-group per row; with a
 // gain it also writes the first layer's normed input out = bf16(h * rsqrt(mean h^2 + eps) * gain).
+// A token id outside [0, vocab) is clamped into range (the table is never read out of bounds)
+// and raises bit kDevErrTokenRange of the sticky error word.
 template <int NCH>  // 8-element chunks per thread: ceil(d / 2048)
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok,
                                                     const uint16_t* __restrict__ embed,
-                                                    float* __restrict__ h, int d,
+                                                    float* __restrict__ h, int d, int vocab,
+                                                    uint32_t* __restrict__ err,
                                                     const float* __restrict__ gain, float eps,
                                                     uint16_t* __restrict__ out) {
   __shared__ float red[4];
   const int r = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const long src = static_cast<long>(tok[r]) * d;
+  int t = tok[r];
+  if (static_cast<unsigned>(t) >= static_cast<unsigned>(vocab)) {
+    if (threadIdx.x == 0) *err = kDevErrTokenRange;
+    t = t < 0 ? 0 : vocab - 1;
+  }
+  const long src = static_cast<long>(t) * d;
   u32x4_t raw[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -329,12 +337,12 @@ __global__ __launch_bounds__(512) void norm_router_kernel(
 
 }  // namespace
 
-void launch_embed(const int32_t* tok, const uint16_t* embed, float* h, int rows, int d,
-                  const float* gain, float eps, uint16_t* out, hipStream_t s) {
+void launch_embed(const int32_t* tok, const uint16_t* embed, float* h, int rows, int d, int vocab,
+                  uint32_t* err, const float* gain, float eps, uint16_t* out, hipStream_t s) {
   const int nch = (d + 2047) / 2048;
-  if (nch <= 1) hipLaunchKernelGGL(embed_kernel<1>, dim3(rows), dim3(256), 0, s, tok, embed, h, d, gain, eps, out);
-  else if (nch <= 2) hipLaunchKernelGGL(embed_kernel<2>, dim3(rows), dim3(256), 0, s, tok, embed, h, d, gain, eps, out);
-  else hipLaunchKernelGGL(embed_kernel<4>, dim3(rows), dim3(256), 0, s, tok, embed, h, d, gain, eps, out);
+  if (nch <= 1) hipLaunchKernelGGL(embed_kernel<1>, dim3(rows), dim3(256), 0, s, tok, embed, h, d, vocab, err, gain, eps, out);
+  else if (nch <= 2) hipLaunchKernelGGL(embed_kernel<2>, dim3(rows), dim3(256), 0, s, tok, embed, h, d, vocab, err, gain, eps, out);
+  else hipLaunchKernelGGL(embed_kernel<4>, dim3(rows), dim3(256), 0, s, tok, embed, h, d, vocab, err, gain, eps, out);
 }
 
 void launch_rmsnorm(const float* h, const float* gain, float eps, uint16_t* out, int rows, int d,

@@ -24,7 +24,9 @@ DG_STEP_HIDDEN_IN, DG_STEP_NO_HEAD, DG_STEP_HEAD_ONLY = 1, 2, 4
 
 EXPORTS = ["dg_create", "dg_destroy", "dg_last_error", "dg_temperature", "dg_prefill_causal",
            "dg_canvas_init", "dg_denoise_step", "dg_sample_commit", "dg_commit_block",
-           "dg_timing_enable", "dg_timing_read", "dg_debug_set_canvas_kv", "dg_quantize_e4m3_rows"]
+           "dg_timing_enable", "dg_timing_read", "dg_debug_set_canvas_kv", "dg_quantize_e4m3_rows",
+           "dg_device_errors"]
+DG_DEVERR_TOKEN_RANGE = 1
 
 vp = C.c_void_p
 
@@ -67,7 +69,8 @@ class SamplerCfg(C.Structure):
 
 class Debug(C.Structure):
     _fields_ = [(n, vp) for n in ("hidden_out", "attn_out", "h_mid", "expert_idx", "gates", "logits",
-                                  "canvas_k", "canvas_v", "layer_out")]
+                                  "canvas_k", "canvas_v", "layer_out", "route_offs", "route_perm",
+                                  "route_inv")]
 
 
 class StepParams(C.Structure):
@@ -100,8 +103,9 @@ _lib.dg_debug_set_canvas_kv.argtypes = [vp, vp, vp, C.c_int32, vp]
 _lib.dg_timing_enable.argtypes = [vp, C.c_int32]
 _lib.dg_timing_read.argtypes = [vp, C.POINTER(KernelTime), C.c_int32]
 _lib.dg_quantize_e4m3_rows.argtypes = [vp, C.c_int64, C.c_int32, vp, vp, vp]
+_lib.dg_device_errors.argtypes = [vp, C.POINTER(C.c_uint32), vp]
 for _n in ("dg_timing_enable", "dg_timing_read", "dg_prefill_causal", "dg_canvas_init", "dg_denoise_step", "dg_sample_commit",
-           "dg_commit_block", "dg_debug_set_canvas_kv", "dg_quantize_e4m3_rows"):
+           "dg_commit_block", "dg_debug_set_canvas_kv", "dg_quantize_e4m3_rows", "dg_device_errors"):
     getattr(_lib, _n).restype = C.c_int
 
 
@@ -126,6 +130,23 @@ def to_device_bf16(x, device) -> torch.Tensor:
     a = np.ascontiguousarray(x, dtype=np.float32)
     bits = (a.view(np.uint32) >> 16).astype(np.uint16)
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device).contiguous()
+
+
+def check_token_range(tokens, vocab: int, what: str = "tokens") -> None:
+    """Raise ValueError unless every id in `tokens` (numpy array, or torch tensor on any device)
+    lies in [0, vocab): the precondition of dg_prefill_causal and dg_denoise_step.  A device
+    tensor is checked with one reduction on the device and a host read."""
+    if isinstance(tokens, torch.Tensor):
+        if tokens.numel() == 0:
+            return
+        lo, hi = (int(v) for v in torch.aminmax(tokens.reshape(-1)))
+    else:
+        a = np.asarray(tokens)
+        if a.size == 0:
+            return
+        lo, hi = int(a.min()), int(a.max())
+    if lo < 0 or hi >= int(vocab):
+        raise ValueError(f"{what}: token ids must lie in [0, {int(vocab)}), got [{lo}, {hi}]")
 
 
 SELECT_TOP_M, SELECT_ENTROPY = 0, 1
@@ -296,6 +317,7 @@ class Model:
     # ---------------------------------------------------------------- entry points
     # `slots`: run the call on those slots of kv (and of the per-slot arrays) only; None = all.
     def prefill(self, tokens: torch.Tensor, n_new: Sequence[int], kv: KV, slots=None):
+        check_token_range(tokens[:sum(int(v) for v in n_new)], self.shape.vocab, "prefill tokens")
         n = (C.c_int32 * len(n_new))(*[int(v) for v in n_new])
         view = kv.view(slots)
         self._check(_lib.dg_prefill_causal(self.ctx, _ptr(tokens), n, len(n_new), C.byref(view.c), _stream()))
@@ -337,6 +359,12 @@ class Model:
         view = kv.view(slots)
         self._check(_lib.dg_commit_block(self.ctx, _ptr(canvas), C.byref(view.c), int(refresh), _stream()))
         view.done()
+
+    def device_errors(self) -> int:
+        """Sticky device-side error bits since the last read (DG_DEVERR_*); waits for the stream."""
+        v = C.c_uint32(0)
+        self._check(_lib.dg_device_errors(self.ctx, C.byref(v), _stream()))
+        return int(v.value)
 
     def timing(self, enable: bool):
         self._check(_lib.dg_timing_enable(self.ctx, int(bool(enable))))

@@ -169,6 +169,11 @@ typedef struct {
   uint16_t* canvas_v;      /* same */
   float* layer_out;        /* [n_layers][rows][d_model] residual after each layer (the next
                               layer's input; the last one equals hidden_out) */
+  /* The token permutation of every layer's routed experts.  Route r = row * top_k + j is the
+   * j-th expert pick of row `row`; routes are ordered by (expert, r), a stable sort by expert. */
+  int32_t* route_offs;     /* [n_layers][n_experts + 1] first sorted position of each expert */
+  int32_t* route_perm;     /* [n_layers][rows * top_k] route at each sorted position */
+  int32_t* route_inv;      /* [n_layers][rows * top_k] sorted position of each route */
 } dg_debug;
 
 enum {
@@ -216,7 +221,8 @@ int dg_quantize_e4m3_rows(const uint16_t* w, int64_t rows, int32_t cols, uint8_t
                           float* scale, hipStream_t stream);
 
 /* Causal prefill ([GUIDE] "Arquitetura em Detalhes"; [NEWS] 2nd ¶; [DOCS] autoregressive
- * encoder): request b's n_new[b] tokens (packed back to back in `tokens`, device int32) are
+ * encoder): request b's n_new[b] tokens (packed back to back in `tokens`, device int32, each in
+ * [0, vocab); an id outside is clamped and reported by dg_device_errors) are
  * placed at positions len[b] .. len[b]+n_new[b]-1; each attends to its cached history and to
  * itself and earlier new tokens.  Every layer's K (after RoPE) and V are written into the cache
  * and len[b] advances by n_new[b].  Needs len[b] + n_new[b] <= cap.  n_new: (host) [batch]. */
@@ -229,7 +235,8 @@ int dg_prefill_causal(dg_ctx* ctx, const int32_t* tokens, const int32_t* n_new, 
 int dg_canvas_init(dg_ctx* ctx, dg_canvas_state* state, const dg_kv_cache* kv,
                    const dg_sampler_cfg* cfg, hipStream_t stream);
 
-/* One denoise forward pass over the canvases `canvas` ([batch][canvas] device int32) of the
+/* One denoise forward pass over the canvases `canvas` ([batch][canvas] device int32, ids in
+ * [0, vocab); an id outside is clamped and reported by dg_device_errors) of the
  * kv->batch requests: canvas slot i sits at position len[b]+i and attends, with no mask, to
  * cache[0:len[b]] and to all canvas slots; top-k MoE FFN; final norm; vocab projection fused
  * with temperature, log-sum-exp, entropy and the Gumbel-max draw (logits never reach HBM).
@@ -277,6 +284,16 @@ typedef struct {
 } dg_kernel_time;
 int dg_timing_enable(dg_ctx* ctx, int32_t enable);
 int dg_timing_read(dg_ctx* ctx, dg_kernel_time* out, int32_t max);
+
+/* Sticky device-side error bits, set by kernels instead of reading out of bounds:
+ *   DG_DEVERR_TOKEN_RANGE: a token id passed to dg_prefill_causal or dg_denoise_step (or a
+ *     canvas token read by the head) lay outside [0, vocab); it was clamped into range, so the
+ *     results of that call are not meaningful.
+ * Waits for `stream`, writes the bits accumulated since the last read to *flags (host) and
+ * clears them.  Token ids must lie in [0, vocab): this is the callers' precondition, the flag
+ * only reports its violation. */
+enum { DG_DEVERR_TOKEN_RANGE = 1 };
+int dg_device_errors(dg_ctx* ctx, uint32_t* flags, hipStream_t stream);
 
 /* Test hook: load canvas K/V ([n_layers][batch][n_kv_heads][canvas][head_dim] bf16) into the
  * workspace, as if a denoise step had produced them. */

@@ -123,3 +123,18 @@ def test_binding_structs_match_the_header_layout(tmp_path):
         assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
         for f in py._fields_:
             assert got[(cname, f[0])] == getattr(py, f[0]).offset, (cname, f[0])
+
+
+def test_binding_rejects_token_ids_outside_the_vocabulary():
+    """The binding checks the token-range precondition of dg_prefill_causal / dg_denoise_step
+    before anything reaches the device: host arrays and CPU tensors here."""
+    import torch
+    dg = pytest.importorskip("block_discrete_diffusion_amd.dg")
+    dg.check_token_range(np.array([0, 5, 1023]), 1024)
+    dg.check_token_range(torch.tensor([0, 1023], dtype=torch.int32), 1024)
+    dg.check_token_range(np.zeros(0, np.int32), 1024)
+    for bad in ([0, 1024], [-1, 3], [2 ** 31 - 1]):
+        with pytest.raises(ValueError):
+            dg.check_token_range(np.array(bad, np.int64), 1024)
+        with pytest.raises(ValueError):
+            dg.check_token_range(torch.tensor(bad, dtype=torch.int64), 1024)

@@ -192,6 +192,90 @@ def test_fp8_expert_layer_parity(env):
         m1.close()
 
 
+def _peaked_stats(V, target, T, seed, pos, step, x):
+    z = np.zeros((256, V))
+    z[np.arange(256), target] = 50.0
+    return osampler.row_stats(z, x, T, seed, 0, pos, step)
+
+
+@pytest.mark.parametrize("select_mode", [0, 1])
+def test_entropy_stop_on_peaked_logits(env, select_mode):
+    """DiffusionGemma docs, table "Configuração de exibição recomendada", adaptive-stop row: with
+    the mean-entropy stop on (0.005), the peaked-logits fixture (z = 50 onehot(target): every
+    draw is the target, entropy ~0) ends after exactly two steps, one step before the stable-run
+    rule would, under both selection rules.  The GPU sampler is fed the oracle's row statistics
+    of the same fixture each step and must follow the oracle's trajectory bit for bit."""
+    dg, w, m = env
+    V = SHAPE.vocab
+    kv, _, _ = _kv(dg)
+    cfg = dg.sampler_cfg(seed=31, select_mode=select_mode, entropy_stop=0.005)
+    oc = oracle_cfg(cfg)
+    target = synth.tokens(256, V, SEED, 60)
+    pos = L + np.arange(256)
+    st = dg.Canvas(1, 256)
+    m.canvas_init(st, kv, cfg)
+    stats = dg.Stats(1, 256)
+    status = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    x, com, sr = osampler.canvas_init(cfg.seed, 0, pos, V), np.zeros(256, bool), 0
+    n_steps = 0
+    for s in range(cfg.max_steps):
+        rs = _peaked_stats(V, target, osampler.temperature(oc, s), cfg.seed, pos, s, x)
+        for k in ("cand", "t_cand", "t_cur", "lse", "entropy"):
+            getattr(stats, k)[0].copy_(torch.from_numpy(np.ascontiguousarray(rs[k])))
+        m.sample_commit(st, stats, cfg, s, kv, status)
+        torch.cuda.synchronize()
+        x, com, sr, ost = osampler.sample_commit(rs, x, com, sr, oc, s, 0, pos, V)
+        got = dg.status_dict(status)[0]
+        assert np.array_equal(st.tokens[0].cpu().numpy(), x), s
+        assert np.array_equal(st.committed[0].cpu().numpy().astype(bool), com), s
+        for k in ("changed", "n_committed", "n_new", "n_renoised", "stable_run", "stop"):
+            assert got[k] == ost[k], (s, k)
+        n_steps += 1
+        if got["stop"]:
+            break
+    assert n_steps == 2
+    assert np.array_equal(x, target)
+
+
+def test_entropy_stop_decision_around_the_threshold(env):
+    """Mean entropies just below and just above the 0.005 threshold: the GPU's float32 sum in
+    a fixed tree and the oracle's float64 mean take the same stop decision wherever the oracle's
+    mean is more than 1e-7 (2e-5 relative) from the threshold; the reported mean agrees to
+    1e-6 relative.  Candidates equal the current tokens at full confidence, so no step changes
+    the canvas and only the entropy condition can stop it (stable-run limit set out of reach)."""
+    dg, w, m = env
+    V = SHAPE.vocab
+    kv, _, _ = _kv(dg)
+    cfg = dg.sampler_cfg(seed=32, entropy_stop=0.005, stable_steps=1000)
+    oc = oracle_cfg(cfg)
+    pos = L + np.arange(256)
+    stats = dg.Stats(1, 256)
+    status = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    decided = 0
+    for i, rel in enumerate([0.5, 0.99, 0.9999, 1.0001, 1.01, 2.0, 0.99995, 1.00005]):
+        st = dg.Canvas(1, 256)
+        m.canvas_init(st, kv, cfg)
+        torch.cuda.synchronize()
+        x = st.tokens[0].cpu().numpy()
+        ent = synth.uniform((256,), 0.0, 2.0, SEED, 80 + i)
+        ent = (ent * np.float32(0.005 * rel / float(np.mean(ent.astype(np.float64))))).astype(np.float32)
+        rs = {"cand": x.astype(np.int32), "t_cand": np.zeros(256, np.float32), "t_cur": np.zeros(256, np.float32),
+              "lse": np.zeros(256, np.float32), "entropy": ent}
+        for k, val in rs.items():
+            getattr(stats, k)[0].copy_(torch.from_numpy(np.ascontiguousarray(val)))
+        m.sample_commit(st, stats, cfg, 3, kv, status)
+        torch.cuda.synchronize()
+        _, _, _, ost = osampler.sample_commit(rs, x, np.zeros(256, bool), 0, oc, 3, 0, pos, V)
+        got = dg.status_dict(status)[0]
+        assert got["changed"] == 0 == ost["changed"]
+        assert abs(got["mean_entropy"] - ost["mean_entropy"]) <= 1e-6 * ost["mean_entropy"]
+        if abs(ost["mean_entropy"] - 0.005) > 1e-7:
+            assert got["stop"] == ost["stop"] == int(rel < 1), (rel, got, ost["mean_entropy"])
+            decided += 1
+    assert decided >= 6
+
+
 def test_full_step_parity(env):
     """Tokens → 2 layers → head: continuous row statistics within the parity bar; decisions
     compared where the oracle margin is safely away from a tie."""
