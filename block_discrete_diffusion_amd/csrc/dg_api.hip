@@ -248,6 +248,7 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   at.n_split = (max_keys + at.split_keys - 1) / at.split_keys;
   at.part_o = c->part_o; at.part_ml = c->part_ml;
   timed(c, "attention", s, [&] { launch_attention(at, s); });
+  if (at.n_split > 1) timed(c, "attn_split_combine", s, [&] { launch_attention_combine(at, s); });
   if (dbg && dbg->attn_out)
     (void)hipMemcpyAsync(dbg->attn_out + static_cast<long>(l) * rows * Hq * D, c->attn,
                          sizeof(uint16_t) * rows * Hq * D, hipMemcpyDeviceToDevice, s);

@@ -136,7 +136,10 @@ struct AttnArgs {
 // the chip (fewer split partials to write and merge) at fewer registers per wave.
 int attention_waves(int max_keys, bool causal);
 int attention_q_tiles(int max_keys, bool causal);
+// The attention kernel (with n_split > 1 it writes split partials), then the fixed-order merge
+// of the partials into `out` (nothing to do for one split).
 void launch_attention(const AttnArgs& a, hipStream_t s);
+void launch_attention_combine(const AttnArgs& a, hipStream_t s);
 
 // ---- k_moe.hip
 void launch_moe_permute(const int32_t* idx, int n_routes, int n_exp, int32_t* offs,

@@ -382,12 +382,14 @@ template <int D>
 void launch_attn_d(const AttnArgs& a, hipStream_t s) {
   if (a.n_waves == 8) launch_attn_w<D, 8>(a, s);
   else launch_attn_w<D, 4>(a, s);
-  if (a.n_split > 1) {
-    const int n_rh = a.n_req * a.rows_per_req * a.Hq;
-    const int per = 256 / (D / 4);
-    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((n_rh + per - 1) / per), dim3(256), 0, s,
-                       a.part_o, a.part_ml, a.out, n_rh, a.n_split);
-  }
+}
+
+template <int D>
+void launch_combine_d(const AttnArgs& a, hipStream_t s) {
+  const int n_rh = a.n_req * a.rows_per_req * a.Hq;
+  const int per = 256 / (D / 4);
+  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((n_rh + per - 1) / per), dim3(256), 0, s,
+                     a.part_o, a.part_ml, a.out, n_rh, a.n_split);
 }
 
 }  // namespace
@@ -403,6 +405,12 @@ void launch_rope_table(const RowMap& map, int rows, int D, float theta, float* t
 void launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.D == 128) launch_attn_d<128>(a, s);
   else launch_attn_d<64>(a, s);
+}
+
+void launch_attention_combine(const AttnArgs& a, hipStream_t s) {
+  if (a.n_split <= 1) return;
+  if (a.D == 128) launch_combine_d<128>(a, s);
+  else launch_combine_d<64>(a, s);
 }
 
 }  // namespace dg
