@@ -37,6 +37,13 @@ DG_DEVICE floatx4_t mfma16(const u32x4_t& a, const u32x4_t& b, const floatx4_t& 
 // prefetch is issued so the loads stay ahead of the MFMAs that do not need them.
 DG_DEVICE void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// s_waitcnt with vmcnt = n (< 64) and lgkmcnt = 0 (expcnt not waited on).
+template <int n>
+DG_DEVICE void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | ((n >> 4) << 14));
+}
+
 DG_DEVICE u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 DG_DEVICE u32x4_t ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));

@@ -329,6 +329,378 @@ void attention_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ pipelined canvas kernel
+// The canvas attention over long key ranges (no mask) at head_dim 128, 8 waves of two 16-row
+// query tiles each, built so that each wave keeps its matrix unit and its vector unit busy at
+// the same time:
+//  * software pipeline: while the softmax of block n runs (scale, exp, pack to bf16), the
+//    QK^T products of block n + 1 are already issued; while P V of block n runs, the maximum of
+//    block n + 1 is taken.  Two score sets alternate;
+//  * K and V blocks go from global memory straight into LDS (global_load_lds_dwordx4) through
+//    a ring of PS stages, three blocks ahead, one barrier per block; no staging registers.  A
+//    1 KB load is four whole 256-byte key rows, so every instruction reads 1 KB of contiguous
+//    memory; inside a row the 16-byte chunk c is stored at chunk c ^ (row & 15), which makes
+//    both the 16-byte K fragment reads and the transposing 8-byte V reads conflict-free;
+//  * lazy rescaling: the exponent reference of a query only moves when the block maximum
+//    exceeds it by more than kLazy (log2 units), so P stays below 2^kLazy and O and its row
+//    sum are rescaled a handful of times per range instead of whenever the maximum grows; the
+//    result is unchanged (O and the row sum share the reference, which cancels);
+//  * the work-groups that share one (request, KV head, split) range are numbered so that they
+//    land on the same XCD, whose L2 then serves the second reader.
+constexpr int PS = 4;          // LDS ring stages (3 blocks in flight)
+constexpr float kLazy = 8.f;   // lazy-rescale margin, log2 units
+
+template <int S>
+using Stage = std::integral_constant<int, S % PS>;
+
+// Chunk swizzle of an LDS key row (16 chunks of 16 bytes): chunk c of row r is stored at
+// c ^ swz(r).  Measured on gfx950 with 8 waves per CU: the 16-byte K fragment reads (rows 0..15
+// of a tile, one chunk each) run at the full LDS rate when eight consecutive rows hit eight
+// distinct chunk pairs, and the transposing 8-byte V reads (two adjacent chunks 2 m, 2 m + 1 of
+// eight rows per 32 lanes) need the same; swz(r) = 2 (r % 8) gives both (K 253 B per tick and
+// CU, V 208; r itself, the plain diagonal: K 253, V 155).
+DG_DEVICE int swz(int r) { return (r & 7) << 1; }
+
+// One global_load_lds_dwordx4: lane l's 16 bytes at g land at LDS address lds + 16 l.  Issued
+// from inline assembly so that the compiler does not track it: its own tracking of such loads
+// loses the stage of each one at the loop's back edge and then drains every load in flight
+// before the first LDS read of the loop body.  The kernel waits for these loads itself
+// (s_waitcnt vmcnt + barrier before a stage is read; vmcnt(0) before exit).  The instruction
+// has no destination register, and its address registers are read when it issues.
+// The address is a wave-uniform base (scalar registers) plus a 32-bit per-lane byte offset.
+DG_DEVICE void dma16(const uint16_t* base, uint32_t lane_ofs, const uint16_t* lds) {
+  const uint32_t l = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds));
+  // the base is wave-uniform; reading it from the first lane puts it in scalar registers (the
+  // builtin works on int: each half goes back to uint32_t before widening, no sign extension)
+  const uint64_t b64 = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b64 >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b64 & 0xffffffffu)));
+  const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(lane_ofs), "s"(sb)
+               : "memory", "m0");
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attention_pipe_kernel(AttnArgs a) {
+  constexpr int D = 128, QT = 2, NKS = D / 32, NDT = D / 16;
+  constexpr int SEG = 2 * KB * D * 2 / 1024;  // 1 KB segments per stage (K then V)
+  constexpr int LPW = SEG / NW;               // segments each wave loads per stage
+  static_assert(SEG % NW == 0 && LPW * NW == SEG, "segments split evenly over the waves");
+  // one LDS array per stage, [K, V][key][d] with 256-byte rows and XOR-swizzled chunks; stage
+  // indices are compile-time (the loop is unrolled over the ring), so the compiler sees that
+  // reads of one stage never alias the direct-to-LDS writes in flight to the others and does
+  // not drain those loads before each read
+  __shared__ uint16_t st0[2 * KB * D], st1[2 * KB * D], st2[2 * KB * D], st3[2 * KB * D];
+  auto stage = [&](auto S) -> uint16_t* {
+    constexpr int s = decltype(S)::value;
+    if constexpr (s == 0) return st0;
+    else if constexpr (s == 1) return st1;
+    else if constexpr (s == 2) return st2;
+    else return st3;
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
+  const int j4 = lane >> 4, l16 = lane & 15;
+  // work-group -> (task group, split, request x KV head); the dispatcher places work-group lin
+  // on XCD lin % 8, so numbering each XCD's work-groups consecutively puts the task groups of
+  // one key range on one XCD
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int G = nx * ny * gridDim.z;
+  const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const int L = (G % 8 == 0) ? (lin % 8) * (G / 8) + lin / 8 : lin;
+  const int bx = L % nx, by = (L / nx) % ny, bz = L / (nx * ny);
+
+  const int b = bz / a.Hkv, g = bz - b * a.Hkv;
+  const int group = a.Hq / a.Hkv;
+  const int rows = a.rows_per_req;
+  constexpr int RW = 16 * QT;
+  const int n_rb = (rows + RW - 1) / RW;
+  const int task = bx * NW + wave;
+  const bool active = task < group * n_rb;
+  const int hq = g * group + (active ? task % group : 0);
+  const int row0 = (active ? task / group : 0) * RW;
+  const long qrow_base = static_cast<long>(b) * rows;
+
+  // key blocks: the cached prefix [k_lo, hi0) then the canvas [lo1, k_hi), KB keys each
+  const int n_cache = a.n_cache[b];
+  const int n_keys = n_cache + a.n_extra;
+  const int k_lo = by * a.split_keys;
+  const int k_hi = min(n_keys, k_lo + a.split_keys);
+  const int hi0 = min(k_hi, n_cache), lo1 = max(k_lo, n_cache);
+  const int nb0 = hi0 > k_lo ? (hi0 - k_lo + KB - 1) / KB : 0;
+  const int nb = nb0 + (k_hi > lo1 ? (k_hi - lo1 + KB - 1) / KB : 0);
+  const long kv_head = static_cast<long>(a.slot[b]) * a.Hkv + g;
+  const long kx_head = static_cast<long>(b) * a.Hkv + g;
+  const uint16_t* kc = a.kc + kv_head * a.cap * D;
+  const uint16_t* vc = a.vc + kv_head * a.cap * D;
+  const uint16_t* kx = a.kx + kx_head * a.xcap * D;
+  const uint16_t* vx = a.vx + kx_head * a.xcap * D;
+  auto first_key = [&](int bi) { return bi < nb0 ? k_lo + bi * KB : lo1 + (bi - nb0) * KB; };
+  auto end_key = [&](int bi) { return bi < nb0 ? hi0 : k_hi; };
+
+  // this lane's part of the wave's LPW segments: segment s of a stage holds key rows
+  // 4 (s % 16) .. + 3 of K (s < 16) or V; lane i fills LDS chunk i % 16 of row i / 16 with the
+  // global chunk (i % 16) ^ swz(row)
+  // (segment bases are wave-uniform: the cache and canvas arrays of K or V, the canvas one
+  // offset so that both are indexed by the key's position in the request)
+  int seg_row[LPW], seg_chunk[LPW];
+  const uint16_t* seg_cb[LPW];
+  const uint16_t* seg_xb[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int s = wave * LPW + i, r = 4 * (s & 15) + (lane >> 4);
+    seg_row[i] = r;
+    seg_chunk[i] = ((lane & 15) ^ swz(r)) * 8;
+    seg_cb[i] = s < 16 ? kc : vc;
+    seg_xb[i] = (s < 16 ? kx : vx) - static_cast<long>(n_cache) * D;
+  }
+  // block bi into stage S (= bi % PS); past the last block, a copy of it into a stage that is
+  // not read again (or only by the unused scores of the step after the last)
+  auto issue = [&](auto S, int bi) {
+    uint16_t* sp = stage(S);
+    bi = min(bi, nb - 1);
+    const int kb0 = first_key(bi), lim = end_key(bi) - 1 - kb0;  // rows past lim re-read row lim
+    const bool canvas = bi >= nb0;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int s = wave * LPW + i;
+      const uint16_t* base = (canvas ? seg_xb[i] : seg_cb[i]) + static_cast<long>(kb0) * D;
+      const uint32_t ofs = static_cast<uint32_t>(min(seg_row[i], lim) * (D * 2) + seg_chunk[i] * 2);
+      dma16(base, ofs, sp + s * 512);
+    }
+  };
+
+  // queries (B operand): lane holds Q[qt*16 + l16][ks*32 + 8*j4 .. +8]
+  u32x4_t qf[QT][NKS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qr = row0 + qt * 16 + l16;
+    const bool ok = active && qr < rows;
+    const uint16_t* qp = a.q + (qrow_base + qr) * a.Hq * D + hq * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[qt][ks] = ok ? ld16(qp + ks * 32 + 8 * j4) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  // the queries have landed before the first stage load is issued: the compiler does not see
+  // those loads, so a wait it placed for a query register inside the loop would also wait for
+  // the stage loads issued after it
+  wait_vm_lgkm0<0>();
+  floatx4_t o[NDT][QT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) o[dt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  floatx4_t l_acc[QT];
+  float m_ref[QT];  // exponent reference (log2 units, scale folded in) of o and l_acc
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    l_acc[qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m_ref[qt] = -INFINITY;
+  }
+  const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const float sl2 = a.scale * 1.4426950408889634f;
+
+  // fragment read offsets (elements) inside a stage's K and V arrays
+  // row l16 of a 16-key tile, chunk (4 ks + j4) ^ f = 4 (ks ^ (f / 4)) + (j4 ^ (f % 4)), f = swz(l16)
+  const int kf0 = swz(l16);
+  const int kofs0 = l16 * D + 8 * (j4 ^ (kf0 & 3)), kq = kf0 >> 2;  // + kt * 16 * D + 32 (ks ^ kq)
+  // transposing V reads: rows 32 h + 4 j4 + l16 / 4 (+ 16), columns dt * 16 + 4 (l16 % 4)
+  const int vr = 4 * j4 + (l16 >> 2);
+  int vofs[NDT];  // + h * 32 * D (+ 16 * D for the second tile; swz depends on row % 16 only)
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) vofs[dt] = vr * D + (((2 * dt + ((l16 & 3) >> 1)) ^ swz(vr)) * 8) + 4 * (l16 & 1);
+
+  // The pipeline runs over half blocks of 32 keys (two 16-key tiles t of the stage's block):
+  // scores of one half are sc[t][qt], 16 registers, so two of them (the half being turned into
+  // P and the next half being multiplied) fit next to O.
+  auto qk = [&](floatx4_t (&sc)[2][QT], auto S, int h) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) sc[t][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* kb = stage(S) + h * 32 * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4_t kf = ld16(kb + t * 16 * D + kofs0 + 32 * (ks ^ kq));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) sc[t][qt] = mfma16(kf, qf[qt][ks], sc[t][qt]);
+      }
+  };
+  // keys of a partial half past the range end get -inf (uniform branch, a few per range)
+  auto mask = [&](floatx4_t (&sc)[2][QT], int bi, int h) {
+    const int k0 = first_key(bi) + 32 * h, hi = end_key(bi);
+    if (k0 + 32 <= hi) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool out = k0 + t * 16 + 4 * j4 + i >= hi;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          if (out) sc[t][qt][i] = -INFINITY;
+      }
+  };
+  // maximum of a half per query; move the reference (and rescale O and its sum) only when it is
+  // exceeded by more than kLazy
+  // The check uses each lane's own maximum (no lane can exceed the reference by more than kLazy
+  // unless some lane's own maximum does); only then are the query maxima formed across the four
+  // lanes of each query and the references that must move moved.
+  auto rebase = [&](const floatx4_t (&sc)[2][QT]) {
+    float mx[QT];
+    bool need = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float v = fmaxf(fmaxf(fmaxf(sc[0][qt][0], sc[0][qt][1]), fmaxf(sc[0][qt][2], sc[0][qt][3])),
+                            fmaxf(fmaxf(sc[1][qt][0], sc[1][qt][1]), fmaxf(sc[1][qt][2], sc[1][qt][3])));
+      mx[qt] = v * sl2;
+      need |= mx[qt] > m_ref[qt] + kLazy;
+    }
+    if (__any(need)) {  // uniform: every lane takes part in the cross-lane maximum
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        mx[qt] = group_max(mx[qt]);
+        const bool up = mx[qt] > m_ref[qt] + kLazy;
+        const float m_new = up ? mx[qt] : m_ref[qt];
+        const float alpha = up ? fast_exp2(m_ref[qt] - m_new) : 1.f;  // 0 from -inf
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha;
+        l_acc[qt] *= alpha;
+        m_ref[qt] = m_new;
+      }
+    }
+  };
+  // K fragment g of a half (tile g % 2, k-step g / 2), and V^T fragment dt of a half
+  auto kread = [&](const uint16_t* kb, int g) { return ld16(kb + (g & 1) * 16 * D + kofs0 + 32 * ((g >> 1) ^ kq)); };
+  auto vread = [&](const uint16_t* vb, int dt) {
+    const u32x2_t lo = read_tr16(vb + vofs[dt]);
+    const u32x2_t hi = read_tr16(vb + 16 * D + vofs[dt]);
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // One pipeline step on half H of block n (n % PS == R): its scores are in cur; the next half
+  // ((n, 1), or (n + 1, 0) in the next stage) is multiplied into nxt meanwhile.  The step is
+  // written as groups with scheduling fences between them, so that every LDS fragment is
+  // requested three groups before the MFMAs that use it and the current half's softmax sits
+  // between the next half's QK^T products:
+  //   QK group g (8):  the two MFMAs of K fragment g; scale, exp and pack of two P values;
+  //                    request of K fragment g + 3
+  //   PV group dt (8): the two MFMAs of V^T fragment dt; request of V^T fragment dt + 3
+  auto step = [&](auto R, auto H, floatx4_t (&cur)[2][QT], floatx4_t (&nxt)[2][QT], int n) {
+    constexpr int r = decltype(R)::value, h = decltype(H)::value;
+    if constexpr (h == 0) {
+      wait_vm_lgkm0<LPW>();  // this wave's loads of block n + 1 have landed
+      __builtin_amdgcn_s_barrier();
+      issue(Stage<r + 3>{}, n + 3);
+    }
+    if (active) {
+      // past the last block the next half's K is a copy whose scores are never used
+      const uint16_t* kb = h == 0 ? stage(Stage<r>{}) + 32 * D : stage(Stage<r + 1>{});
+      const uint16_t* vb = stage(Stage<r>{}) + KB * D + h * 32 * D;
+      float mu[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) mu[qt] = (m_ref[qt] == -INFINITY) ? 0.f : m_ref[qt];  // no key seen yet
+      u32x4_t pf[QT];
+      u32x4_t kf[3] = {kread(kb, 0), kread(kb, 1), kread(kb, 2)};
+      sched_fence();
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int t = g & 1, ks = g >> 1;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          nxt[t][qt] = mfma16(kf[g % 3], qf[qt][ks], ks == 0 ? floatx4_t{0.f, 0.f, 0.f, 0.f} : nxt[t][qt]);
+        // P values 2 j, 2 j + 1 (of the 8 = keys {16 t' + 4 j4 + i}) of query tile qt
+        const int qt = g >> 2, j = g & 3;
+        const float p0 = fast_exp2(fmaf(cur[j >> 1][qt][2 * (j & 1)], sl2, -mu[qt]));
+        const float p1 = fast_exp2(fmaf(cur[j >> 1][qt][2 * (j & 1) + 1], sl2, -mu[qt]));
+        uint32_t pk = pack_bf2(p0, p1);
+        asm volatile("" : "+v"(pk));  // computed here, in this group (not sunk to its first use)
+        pf[qt][j] = pk;
+        if (g + 3 < 8) kf[g % 3] = kread(kb, g + 3);
+        sched_fence();
+      }
+      const bool has_next = (h == 0) || (n + 1 < nb);
+      if (has_next) mask(nxt, h == 0 ? n : n + 1, 1 - h);
+      u32x4_t vf[3] = {vread(vb, 0), vread(vb, 1), vread(vb, 2)};
+      sched_fence();
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16(vf[dt % 3], pf[qt], o[dt][qt]);
+        if (dt + 3 < NDT) vf[dt % 3] = vread(vb, dt + 3);
+        sched_fence();
+      }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) l_acc[qt] = mfma16(ones, pf[qt], l_acc[qt]);
+      if (has_next) rebase(nxt);
+    }
+  };
+
+  if (nb > 0) {
+    // a first (unused) load into stage 3 makes the loads in flight on entry to the loop the
+    // same stages as on its back edge
+    issue(Stage<3>{}, 0);
+    issue(Stage<0>{}, 0);
+    issue(Stage<1>{}, 1);
+    issue(Stage<2>{}, 2);
+    wait_vm_lgkm0<2 * LPW>();
+    __builtin_amdgcn_s_barrier();
+    floatx4_t sa[2][QT], sb[2][QT];
+    if (active) {
+      qk(sa, Stage<0>{}, 0);
+      mask(sa, 0, 0);
+      rebase(sa);
+    }
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    static_assert(PS == 4, "the loop below is unrolled over a ring of four stages");
+    for (int n = 0; n < nb; n += 4) {
+      step(Stage<0>{}, H0{}, sa, sb, n);
+      step(Stage<0>{}, H1{}, sb, sa, n);
+      if (n + 1 >= nb) break;
+      step(Stage<1>{}, H0{}, sa, sb, n + 1);
+      step(Stage<1>{}, H1{}, sb, sa, n + 1);
+      if (n + 2 >= nb) break;
+      step(Stage<2>{}, H0{}, sa, sb, n + 2);
+      step(Stage<2>{}, H1{}, sb, sa, n + 2);
+      if (n + 3 >= nb) break;
+      step(Stage<3>{}, H0{}, sa, sb, n + 3);
+      step(Stage<3>{}, H1{}, sb, sa, n + 3);
+    }
+    wait_vm_lgkm0<0>();  // no load may still be writing this work-group's LDS at exit
+  }
+
+  if (!active) return;
+  // write: lane owns query qt*16+l16, dims dt*16 + 4*j4 + i; partial references in log2 units
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qr = row0 + qt * 16 + l16;
+    if (qr >= rows) continue;
+    const long orow = qrow_base + qr;
+    const float l_run = l_acc[qt][0];
+    if (a.n_split == 1) {
+      const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
+      uint16_t* op = a.out + orow * a.Hq * D + hq * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const floatx4_t v = o[dt][qt];
+        *reinterpret_cast<u32x2_t*>(op + dt * 16 + 4 * j4) =
+            u32x2_t{pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv)};
+      }
+    } else {
+      const long slot = (orow * a.Hq + hq) * a.n_split + by;
+      float* po = a.part_o + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<floatx4_t*>(po + dt * 16 + 4 * j4) = o[dt][qt];
+      if (j4 == 0) {
+        a.part_ml[slot * 2] = m_ref[qt];
+        a.part_ml[slot * 2 + 1] = l_run;
+      }
+    }
+  }
+}
+
 // Merge split partials in split order: O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
 // Every (max, sum) pair and every partial row of a thread is requested before any arithmetic.
 template <int D>
@@ -374,7 +746,9 @@ void launch_attn_w(const AttnArgs& a, hipStream_t s) {
   const int qt = a.q_tiles == 1 ? 1 : 2;
   const int tasks = group * ((a.rows_per_req + 16 * qt - 1) / (16 * qt));
   dim3 grid((tasks + NW - 1) / NW, a.n_split, a.n_req * a.Hkv);
-  if (qt == 1) hipLaunchKernelGGL((attention_kernel<D, NW, 1>), grid, dim3(64 * NW), 0, s, a);
+  if (D == 128 && NW == 8 && qt == 2 && !a.causal)
+    hipLaunchKernelGGL((attention_pipe_kernel<8>), grid, dim3(64 * NW), 0, s, a);
+  else if (qt == 1) hipLaunchKernelGGL((attention_kernel<D, NW, 1>), grid, dim3(64 * NW), 0, s, a);
   else hipLaunchKernelGGL((attention_kernel<D, NW, 2>), grid, dim3(64 * NW), 0, s, a);
 }
 

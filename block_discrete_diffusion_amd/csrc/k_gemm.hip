@@ -291,12 +291,6 @@ struct DlSmem {
   uint16_t b[C::NS][C::BLK][512];
 };
 
-// s_waitcnt with vmcnt = n (< 64) and lgkmcnt = 0 (expcnt not waited on).
-template <int n>
-DG_DEVICE void wait_vm_lgkm0() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | ((n >> 4) << 14));
-}
 
 template <class C, bool DUAL>
 struct DlMainloop {
