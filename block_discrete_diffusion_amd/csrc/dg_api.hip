@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <mutex>
 #include <vector>
 
 #include "../../include/dg.h"
@@ -14,9 +15,38 @@
 
 using namespace dg;
 
+// Fixed device scratch of the allocation-free head entry point (dg_denoise_head_static): the
+// per-(row, slice) partial statistics of the vocab head, then the call's gathered canvas tokens.
+// Each device the library runs on holds its own copy of this array until the process ends; host
+// code never uses the array's name as an address (it is a host-side stand-in), only the device
+// address hipGetSymbolAddress returns for the current device (scratch_address below).
+constexpr long kStaticScratchBytes = 16L << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 namespace {
 
 thread_local std::string g_create_error;
+
+// Device address of `scratch` on each device, looked up once per device with it current.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[256] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 256) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 struct Buf {
   void* p = nullptr;
@@ -76,6 +106,7 @@ struct dg_ctx {
   float* rope = nullptr;       // [r_max][D/2][2] cos/sin of the rows of the current step
   int32_t* tok = nullptr;      // [r_canvas] canvas tokens of a slot-mapped call, in call order
   uint32_t* dev_err = nullptr; // sticky device-side error bits (kDevErr*), read by dg_device_errors
+  void* static_scratch = nullptr;  // this device's `scratch` (dg_denoise_head_static)
   std::vector<int32_t> last_slots;  // slots of the requests whose canvas K/V the workspace holds
   uint16_t* ck = nullptr;      // [L][max_batch][Hkv][C][D]
   uint16_t* cv = nullptr;
@@ -471,6 +502,12 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
     }
   }
   if (ok) ok = hipDeviceSynchronize() == hipSuccess && hipGetLastError() == hipSuccess;
+  // the static scratch of the allocation-free head call, looked up on this (current) device
+  if (ok && scratch_address(&c->static_scratch) != hipSuccess) {
+    g_create_error = "dg_create: hipGetSymbolAddress of the static scratch failed";
+    delete c;
+    return DG_ERR_HIP;
+  }
   if (!ok) {
     g_create_error = "workspace allocation or weight packing failed";
     delete c;
@@ -558,6 +595,39 @@ int dg_canvas_init(dg_ctx* c, dg_canvas_state* st, const dg_kv_cache* kv,
   return check_hip(c, "canvas_init");
 }
 
+// Vocab projection + row statistics of `rows` normed final states f, with the per-(row, 64-entry
+// slice) partial statistics in `part` ([rows][vocab / 64][8] floats, every entry written by the
+// head kernel before the merge reads it, so nothing needs clearing).
+static void run_head(dg_ctx* c, const uint16_t* f, const int32_t* canvas, const dg_kv_cache* kv,
+                     const dg_sampler_cfg* cfg, const dg_step_params* p, dg_row_stats* out, float* part,
+                     bool time_it, hipStream_t s) {
+  const dg_model_desc& m = c->m;
+  const int B = kv->batch, C = m.canvas, rows = B * C;
+  const dg_debug* dbg = p ? p->debug : nullptr;
+  HeadArgs ha{};
+  ha.f = f; ha.n_rows = rows; ha.w = c->w.lm_head; ha.K = m.d_model; ha.V = m.vocab;
+  ha.k0 = static_cast<uint32_t>(cfg->seed); ha.k1 = static_cast<uint32_t>(cfg->seed >> 32);
+  for (int b = 0; b < B; ++b) {
+    ha.step[b] = (p && p->steps) ? p->steps[b] : (p ? p->step : 0);
+    ha.temp[b] = dg_temperature(cfg, ha.step[b]);
+  }
+  ha.cur_tok = canvas;
+  ha.map = make_map(C, B, kv->len, kv);
+  ha.part = part;
+  ha.dbg_logits = dbg ? dbg->logits : nullptr;
+  auto merge = [&] {
+    launch_head_merge(part, rows, m.vocab / kHeadSlice, kHeadSlice, canvas, c->dev_err, out->cand, out->t_cand,
+                      out->t_cur, out->lse, out->entropy, ha.map, s);
+  };
+  if (time_it) {
+    timed(c, "head_lse_gumbel", s, [&] { launch_head(ha, s); });
+    timed(c, "head_merge", s, merge);
+  } else {
+    launch_head(ha, s);
+    merge();
+  }
+}
+
 static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
                         const dg_sampler_cfg* cfg, const dg_step_params* p, dg_row_stats* out,
                         hipStream_t s) {
@@ -613,27 +683,14 @@ static int denoise_impl(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
   if (no_head) return DG_OK;
   // the final norm was fused into the last layer's combine
   const uint16_t* f = head_only ? static_cast<const uint16_t*>(p->hidden_in) : c->f;
-  HeadArgs ha{};
-  ha.f = f; ha.n_rows = rows; ha.w = c->w.lm_head; ha.K = d; ha.V = m.vocab;
-  ha.k0 = static_cast<uint32_t>(cfg->seed); ha.k1 = static_cast<uint32_t>(cfg->seed >> 32);
-  for (int b = 0; b < B; ++b) {
-    ha.step[b] = (p && p->steps) ? p->steps[b] : (p ? p->step : 0);
-    ha.temp[b] = dg_temperature(cfg, ha.step[b]);
-  }
-  ha.cur_tok = canvas;
-  ha.map = make_map(C, B, kv->len, kv);
-  ha.part = c->head_part;
-  ha.dbg_logits = dbg ? dbg->logits : nullptr;
-  timed(c, "head_lse_gumbel", s, [&] { launch_head(ha, s); });
-  timed(c, "head_merge", s, [&] { launch_head_merge(c->head_part, rows, m.vocab / kHeadSlice, kHeadSlice, canvas,
-                    c->dev_err, out->cand, out->t_cand, out->t_cur, out->lse, out->entropy, ha.map, s); });
+  run_head(c, f, canvas, kv, cfg, p, out, c->head_part, true, s);
   return DG_OK;
 }
 
-int dg_denoise_step(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
-                    const dg_sampler_cfg* cfg, const dg_step_params* p, dg_row_stats* out,
-                    hipStream_t s) {
-  if (!c) return DG_ERR_ARG;
+// Argument checks shared by dg_denoise_step and its allocation-free head variant.
+static int check_step_args(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
+                           const dg_sampler_cfg* cfg, const dg_step_params* p,
+                           const dg_row_stats* out) {
   int rc = check_kv(c, kv);
   if (rc) return rc;
   const uint32_t flags = p ? p->flags : 0u;
@@ -658,9 +715,48 @@ int dg_denoise_step(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
     if (!(cfg->temp_start > 0.f) || !(cfg->temp_end > 0.f))
       return c->fail(DG_ERR_ARG, "denoise: temperatures must be > 0");
   }
+  return DG_OK;
+}
+
+int dg_denoise_step(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
+                    const dg_sampler_cfg* cfg, const dg_step_params* p, dg_row_stats* out,
+                    hipStream_t s) {
+  if (!c) return DG_ERR_ARG;
+  int rc = check_step_args(c, canvas, kv, cfg, p, out);
+  if (rc) return rc;
   rc = denoise_impl(c, canvas, kv, cfg, p, out, s);
   if (rc) return rc;
   return check_hip(c, "denoise_step");
+}
+
+int dg_denoise_head_static(dg_ctx* c, const int32_t* canvas, const dg_kv_cache* kv,
+                           const dg_sampler_cfg* cfg, const dg_step_params* p, dg_row_stats* out,
+                           hipStream_t s) {
+  if (!c) return DG_ERR_ARG;
+  if (!p || p->flags != DG_STEP_HEAD_ONLY)
+    return c->fail(DG_ERR_UNSUPPORTED, "denoise_head_static: params with flags == DG_STEP_HEAD_ONLY required");
+  int rc = check_step_args(c, canvas, kv, cfg, p, out);
+  if (rc) return rc;
+  if (!c->static_scratch) return c->fail(DG_ERR_HIP, "denoise_head_static: no static scratch on this device");
+  const int B = kv->batch, C = c->m.canvas, rows = B * C;
+  const long part_bytes = static_cast<long>(rows) * (c->m.vocab / kHeadSlice) * 8 * sizeof(float);
+  const long need = part_bytes + static_cast<long>(rows) * sizeof(int32_t);
+  if (need > kStaticScratchBytes) {
+    char msg[192];
+    snprintf(msg, sizeof msg,
+             "denoise_head_static: %d rows at vocab %d need %ld bytes of scratch, above the static %ld "
+             "(at most %ld rows at this vocab)", rows, c->m.vocab, need, kStaticScratchBytes,
+             kStaticScratchBytes / (need / rows));
+    return c->fail(DG_ERR_CAPACITY, msg);
+  }
+  float* part = static_cast<float*>(c->static_scratch);
+  if (canvas && !kv_identity(kv)) {  // the rows of this call, in call order, after the partials
+    int32_t* tok = reinterpret_cast<int32_t*>(static_cast<char*>(c->static_scratch) + part_bytes);
+    launch_gather_rows(canvas, tok, make_map(C, B, kv->len, kv), s);
+    canvas = tok;
+  }
+  run_head(c, static_cast<const uint16_t*>(p->hidden_in), canvas, kv, cfg, p, out, part, false, s);
+  return check_hip(c, "denoise_head_static");
 }
 
 int dg_sample_commit(dg_ctx* c, dg_canvas_state* st, const dg_row_stats* rs,

@@ -25,7 +25,7 @@ DG_STEP_HIDDEN_IN, DG_STEP_NO_HEAD, DG_STEP_HEAD_ONLY = 1, 2, 4
 EXPORTS = ["dg_create", "dg_destroy", "dg_last_error", "dg_temperature", "dg_prefill_causal",
            "dg_canvas_init", "dg_denoise_step", "dg_sample_commit", "dg_commit_block",
            "dg_timing_enable", "dg_timing_read", "dg_debug_set_canvas_kv", "dg_quantize_e4m3_rows",
-           "dg_device_errors"]
+           "dg_device_errors", "dg_denoise_head_static"]
 DG_DEVERR_TOKEN_RANGE = 1
 
 vp = C.c_void_p
@@ -104,8 +104,11 @@ _lib.dg_timing_enable.argtypes = [vp, C.c_int32]
 _lib.dg_timing_read.argtypes = [vp, C.POINTER(KernelTime), C.c_int32]
 _lib.dg_quantize_e4m3_rows.argtypes = [vp, C.c_int64, C.c_int32, vp, vp, vp]
 _lib.dg_device_errors.argtypes = [vp, C.POINTER(C.c_uint32), vp]
+_lib.dg_denoise_head_static.argtypes = [vp, vp, C.POINTER(KVCache), C.POINTER(SamplerCfg), C.POINTER(StepParams),
+                                        C.POINTER(RowStats), vp]
 for _n in ("dg_timing_enable", "dg_timing_read", "dg_prefill_causal", "dg_canvas_init", "dg_denoise_step", "dg_sample_commit",
-           "dg_commit_block", "dg_debug_set_canvas_kv", "dg_quantize_e4m3_rows", "dg_device_errors"):
+           "dg_commit_block", "dg_debug_set_canvas_kv", "dg_quantize_e4m3_rows", "dg_device_errors",
+           "dg_denoise_head_static"):
     getattr(_lib, _n).restype = C.c_int
 
 

@@ -246,6 +246,20 @@ int dg_denoise_step(dg_ctx* ctx, const int32_t* canvas, const dg_kv_cache* kv,
                     const dg_sampler_cfg* cfg, const dg_step_params* params,
                     dg_row_stats* out, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): dg_denoise_step restricted to params->flags ==
+ * DG_STEP_HEAD_ONLY (params->hidden_in = bf16 [batch*canvas][d_model] normed final states), with
+ * the same arguments, checks and results, bit for bit.  Its scratch (the per-(row, 64-entry vocab
+ * slice) partial statistics, and the gathered canvas tokens of a slot-mapped call) lives in a
+ * fixed 16 MiB device array inside the library instead of the context's workspace, and the call
+ * allocates nothing: rows * (vocab / 64) * 32 + rows * 4 bytes must fit in 16 MiB (at vocab 65536:
+ * up to 512 rows, two canvases), else DG_ERR_CAPACITY with nothing enqueued.  The array is one
+ * per device and keeps the last call's contents (every entry a call reads is written by that call
+ * first); calls that overlap on one device, from any context or stream, race on it. */
+int dg_denoise_head_static(dg_ctx* ctx, const int32_t* canvas, const dg_kv_cache* kv,
+                           const dg_sampler_cfg* cfg, const dg_step_params* params,
+                           dg_row_stats* out, hipStream_t stream);
+
 /* Sampler step `step` on every canvas ([NEWS] 2nd ¶; [GUIDE] Sudoku demo; [DOCS] table):
  * commit the min(commit_per_step, #uncommitted) uncommitted slots with the highest candidate
  * log-confidence t_cand - lse (lowest slot on ties); re-noise committed slots whose current
