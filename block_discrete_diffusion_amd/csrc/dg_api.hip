@@ -224,6 +224,56 @@ int choose_split(const dg_ctx* c, int base_wgs, int n_keys, int rows, int waves)
   return ns;
 }
 
+// Per-request splits for the pipelined canvas attention: about two work-groups per CU in all,
+// the splits handed out one at a time to the request whose splits are then longest (each split
+// keeps at least 256 keys), split lengths rounded up to 64-key blocks.  The (request, split)
+// pairs are listed longest first: the dispatcher gives each CU its next work-group as the CU
+// frees up, so the CUs that ran the longest ranges first take the shortest ones last.
+void plan_pipe_splits(const dg_ctx* c, AttnArgs& at, int rows) {
+  constexpr int kCUs = 256;
+  const int n_req = at.n_req, Hkv = at.Hkv;
+  const int group = at.Hq / Hkv, n_rb = (at.rows_per_req + 31) / 32;
+  const int per_pair = (group * n_rb + 7) / 8 * Hkv;  // work-groups of one (request, split)
+  const int cap = std::max(1, std::min(kMaxSplit, c->part_cap / std::max(1, rows * at.Hq)));
+  int keys[kMaxBatch], ns[kMaxBatch];
+  for (int b = 0; b < n_req; ++b) {
+    keys[b] = at.n_cache[b] + at.n_extra;
+    ns[b] = 1;
+  }
+  const int want = std::min(kMaxPairs, std::max(n_req, (2 * kCUs + per_pair - 1) / per_pair));
+  for (int p = n_req; p < want; ++p) {
+    int best = -1;
+    long best_num = 0, best_den = 1;  // longest keys[b] / ns[b], compared exactly
+    for (int b = 0; b < n_req; ++b) {
+      if (ns[b] >= cap || keys[b] / (ns[b] + 1) < 256) continue;
+      if (best < 0 || static_cast<long>(keys[b]) * best_den > best_num * ns[b]) {
+        best = b;
+        best_num = keys[b];
+        best_den = ns[b];
+      }
+    }
+    if (best < 0) break;
+    ++ns[best];
+  }
+  struct Pair { int len, b, s; };
+  Pair pairs[kMaxPairs];
+  int n_pairs = 0, stride = 1;
+  for (int b = 0; b < n_req; ++b) {
+    const int sk = ((keys[b] + ns[b] - 1) / ns[b] + 63) / 64 * 64;
+    ns[b] = (keys[b] + sk - 1) / sk;
+    at.req_split[b] = ns[b];
+    at.req_split_keys[b] = sk;
+    stride = std::max(stride, ns[b]);
+    for (int sp = 0; sp < ns[b]; ++sp) pairs[n_pairs++] = Pair{std::min(sk, keys[b] - sp * sk), b, sp};
+  }
+  std::stable_sort(pairs, pairs + n_pairs, [](const Pair& x, const Pair& y) { return x.len > y.len; });
+  at.n_pairs = n_pairs;
+  for (int i = 0; i < n_pairs; ++i) at.pair[i] = static_cast<uint16_t>((pairs[i].b << 8) | pairs[i].s);
+  at.n_split = stride;
+  at.split_keys = 0;
+  at.balanced = 1;
+}
+
 // One decoder layer over `rows` rows (n_req requests of rows_per_req rows each).
 // Denoise mode: K/V of the rows go to the canvas scratch; keys = cache[0:len) + canvas.
 // Prefill mode (one request): K/V go to the cache at len..; keys = cache[0:len+rows), causal.
@@ -273,10 +323,14 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   at.q_tiles = attention_q_tiles(max_keys, prefill);
   const int tasks = (Hq / Hkv) * ((rows_per_req + 16 * at.q_tiles - 1) / (16 * at.q_tiles));
   at.n_waves = attention_waves(max_keys, prefill);
-  const int base = ((tasks + at.n_waves - 1) / at.n_waves) * n_req * Hkv;
-  at.n_split = choose_split(c, base, max_keys, rows, at.n_waves);
-  at.split_keys = (((max_keys + at.n_split - 1) / at.n_split + 63) / 64) * 64;
-  at.n_split = (max_keys + at.split_keys - 1) / at.split_keys;
+  if (attention_pipe_path(at)) {
+    plan_pipe_splits(c, at, rows);
+  } else {
+    const int base = ((tasks + at.n_waves - 1) / at.n_waves) * n_req * Hkv;
+    at.n_split = choose_split(c, base, max_keys, rows, at.n_waves);
+    at.split_keys = (((max_keys + at.n_split - 1) / at.n_split + 63) / 64) * 64;
+    at.n_split = (max_keys + at.split_keys - 1) / at.split_keys;
+  }
   at.part_o = c->part_o; at.part_ml = c->part_ml;
   timed(c, "attention", s, [&] { launch_attention(at, s); });
   if (at.n_split > 1) timed(c, "attn_split_combine", s, [&] { launch_attention_combine(at, s); });

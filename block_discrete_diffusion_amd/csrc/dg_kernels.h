@@ -6,6 +6,7 @@
 namespace dg {
 
 constexpr int kMaxBatch = 64;
+constexpr int kMaxPairs = 128;  // (request, split) pairs of one balanced attention launch
 
 // Per-request row bookkeeping passed by value to kernels: request b owns rows
 // [b*rows_per_req, (b+1)*rows_per_req) and row i of it sits at position pos0[b] + i.
@@ -128,7 +129,19 @@ struct AttnArgs {
   float* part_o; float* part_ml;  // partials when n_split > 1
   int n_waves;                    // query tasks per work-group: 4 or 8 (attention_waves)
   int q_tiles;                    // 16-row query tiles per wave task: 1 or 2 (0 means 2)
+  // Per-request splits (the pipelined canvas kernel, attention_pipe_path): request b's keys
+  // are cut into req_split[b] ranges of req_split_keys[b] keys (n_split is then the largest
+  // count, the stride of the partial slots), and work-groups take the (request, split) pairs
+  // pair[0 .. n_pairs) = request << 8 | split in that order, longest range first.
+  int balanced;
+  int32_t req_split[kMaxBatch];
+  int32_t req_split_keys[kMaxBatch];
+  int32_t n_pairs;
+  uint16_t pair[kMaxPairs];
 };
+// True when launch_attention runs the pipelined canvas kernel for these arguments (head dim
+// 128, 8 waves, two query tiles per wave, no causal mask); it takes per-request splits.
+bool attention_pipe_path(const AttnArgs& a);
 // Work-group shape for a key range of max_keys.  Waves: 8 from 2048 keys on the canvas path
 // and from 8192 in the causal prefill (each staged block serves more queries), else 4.  Query tiles per wave: 2 (32 rows) for long ranges and the
 // causal prefill, where each K fragment read from LDS then feeds two MFMAs; 1 (16 rows) for a

@@ -403,31 +403,34 @@ void attention_pipe_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
   const int j4 = lane >> 4, l16 = lane & 15;
-  // work-group -> (task group, split, request x KV head); the dispatcher places work-group lin
-  // on XCD lin % 8, so numbering each XCD's work-groups consecutively puts the task groups of
-  // one key range on one XCD
-  const int nx = gridDim.x, ny = gridDim.y;
-  const int G = nx * ny * gridDim.z;
-  const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
-  const int L = (G % 8 == 0) ? (lin % 8) * (G / 8) + lin / 8 : lin;
-  const int bx = L % nx, by = (L / nx) % ny, bz = L / (nx * ny);
-
-  const int b = bz / a.Hkv, g = bz - b * a.Hkv;
+  // work-group -> (task group bx, unit u); unit u = (pair p, KV head g) and pair p = (request
+  // b, split by), pairs longest first.  The dispatcher places work-group lin on XCD lin % 8 and
+  // hands each XCD its work-groups in order, so unit u goes to XCD u % 8 with its task groups
+  // next to each other there (the second reader of a key range hits that XCD's L2), and every
+  // XCD starts on the longest ranges.
   const int group = a.Hq / a.Hkv;
   const int rows = a.rows_per_req;
   constexpr int RW = 16 * QT;
   const int n_rb = (rows + RW - 1) / RW;
+  const int nx = (group * n_rb + NW - 1) / NW;
+  const int lin = blockIdx.x;
+  const int bx = (lin / 8) % nx;
+  const int u = (lin / 8 / nx) * 8 + lin % 8;
+  if (u >= a.n_pairs * a.Hkv) return;  // padding of the last row of eight units (uniform)
+  const int pr = a.pair[u / a.Hkv];
+  const int b = pr >> 8, by = pr & 255, g = u % a.Hkv;
   const int task = bx * NW + wave;
   const bool active = task < group * n_rb;
   const int hq = g * group + (active ? task % group : 0);
   const int row0 = (active ? task / group : 0) * RW;
   const long qrow_base = static_cast<long>(b) * rows;
+  const int n_split_b = a.req_split[b];
 
   // key blocks: the cached prefix [k_lo, hi0) then the canvas [lo1, k_hi), KB keys each
   const int n_cache = a.n_cache[b];
   const int n_keys = n_cache + a.n_extra;
-  const int k_lo = by * a.split_keys;
-  const int k_hi = min(n_keys, k_lo + a.split_keys);
+  const int k_lo = by * a.req_split_keys[b];
+  const int k_hi = min(n_keys, k_lo + a.req_split_keys[b]);
   const int hi0 = min(k_hi, n_cache), lo1 = max(k_lo, n_cache);
   const int nb0 = hi0 > k_lo ? (hi0 - k_lo + KB - 1) / KB : 0;
   const int nb = nb0 + (k_hi > lo1 ? (k_hi - lo1 + KB - 1) / KB : 0);
@@ -679,7 +682,7 @@ void attention_pipe_kernel(AttnArgs a) {
     if (qr >= rows) continue;
     const long orow = qrow_base + qr;
     const float l_run = l_acc[qt][0];
-    if (a.n_split == 1) {
+    if (n_split_b == 1) {
       const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
       uint16_t* op = a.out + orow * a.Hq * D + hq * D;
 #pragma unroll
@@ -701,19 +704,28 @@ void attention_pipe_kernel(AttnArgs a) {
   }
 }
 
+struct SplitCounts {
+  int balanced, Hq, rows_per_req;
+  int32_t n[kMaxBatch];
+};
+
 // Merge split partials in split order: O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
 // Every (max, sum) pair and every partial row of a thread is requested before any arithmetic.
+// With per-request splits a row of request b merges its own req_split[b] partials; a request
+// with one split was written by the attention kernel itself.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            uint16_t* __restrict__ out, int n_rh,
-                                                           int n_split) {
+                                                           int stride, SplitCounts sc) {
   constexpr int TPR = D / 4;  // threads per (row, head): 4 dims each
   constexpr int MS = 16;      // most splits a launch uses
   const int rh = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (rh >= n_rh) return;
+  const int n_split = sc.balanced ? sc.n[rh / sc.Hq / sc.rows_per_req] : stride;
+  if (n_split <= 1) return;
   const int d0 = (threadIdx.x % TPR) * 4;
-  const long base = static_cast<long>(rh) * n_split;
+  const long base = static_cast<long>(rh) * stride;
   float2 ml[MS];
   floatx4_t po[MS];
 #pragma unroll
@@ -745,10 +757,15 @@ void launch_attn_w(const AttnArgs& a, hipStream_t s) {
   const int group = a.Hq / a.Hkv;
   const int qt = a.q_tiles == 1 ? 1 : 2;
   const int tasks = group * ((a.rows_per_req + 16 * qt - 1) / (16 * qt));
-  dim3 grid((tasks + NW - 1) / NW, a.n_split, a.n_req * a.Hkv);
-  if (D == 128 && NW == 8 && qt == 2 && !a.causal)
-    hipLaunchKernelGGL((attention_pipe_kernel<8>), grid, dim3(64 * NW), 0, s, a);
-  else if (qt == 1) hipLaunchKernelGGL((attention_kernel<D, NW, 1>), grid, dim3(64 * NW), 0, s, a);
+  const int nx = (tasks + NW - 1) / NW;
+  if (attention_pipe_path(a)) {
+    // rows of eight units, each unit's nx task groups
+    const int units = a.n_pairs * a.Hkv;
+    hipLaunchKernelGGL((attention_pipe_kernel<8>), dim3((units + 7) / 8 * 8 * nx), dim3(64 * NW), 0, s, a);
+    return;
+  }
+  dim3 grid(nx, a.n_split, a.n_req * a.Hkv);
+  if (qt == 1) hipLaunchKernelGGL((attention_kernel<D, NW, 1>), grid, dim3(64 * NW), 0, s, a);
   else hipLaunchKernelGGL((attention_kernel<D, NW, 2>), grid, dim3(64 * NW), 0, s, a);
 }
 
@@ -762,11 +779,20 @@ template <int D>
 void launch_combine_d(const AttnArgs& a, hipStream_t s) {
   const int n_rh = a.n_req * a.rows_per_req * a.Hq;
   const int per = 256 / (D / 4);
+  SplitCounts sc{};
+  sc.balanced = a.balanced;
+  sc.Hq = a.Hq;
+  sc.rows_per_req = a.rows_per_req;
+  for (int b = 0; b < a.n_req; ++b) sc.n[b] = a.req_split[b];
   hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((n_rh + per - 1) / per), dim3(256), 0, s,
-                     a.part_o, a.part_ml, a.out, n_rh, a.n_split);
+                     a.part_o, a.part_ml, a.out, n_rh, a.n_split, sc);
 }
 
 }  // namespace
+
+bool attention_pipe_path(const AttnArgs& a) {
+  return a.D == 128 && a.n_waves == 8 && a.q_tiles != 1 && !a.causal;
+}
 
 int attention_waves(int max_keys, bool causal) { return max_keys >= (causal ? 8192 : 2048) ? 8 : 4; }
 int attention_q_tiles(int max_keys, bool causal) { return (!causal && max_keys < 8192) ? 1 : 2; }
