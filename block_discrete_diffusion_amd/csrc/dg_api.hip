@@ -113,6 +113,7 @@ struct dg_ctx {
   std::vector<uint16_t*> wqkv;  // per layer: QKV weight in rotation-pair row order
   std::vector<uint16_t*> pk1;  // per layer: packed gate/up expert weights
   std::vector<uint16_t*> pk2;  // per layer: packed down expert weights
+  std::vector<uint16_t*> wr_pk;  // per layer: router weights in MFMA fragment order (or empty)
   // E4M3 experts (desc.expert_fp8): packed bytes and per-channel scales [E][N] per matrix
   std::vector<uint8_t*> pk1_8, pk2_8;
   std::vector<float*> sc_gate, sc_up, sc_down;
@@ -349,8 +350,8 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
   // (the attention-output residual lands here when the O-projection was split: h += slices)
   timed(c, "norm_router_topk", s, [&] {
     launch_norm_router(c->h, c->gpart, go.split > 1 ? go.split : 0, go.part_stride, lw.ffn_norm,
-                       m.rms_eps, lw.w_router, rows, d, m.n_experts, m.top_k, c->a, c->eidx,
-                       c->gates, s);
+                       m.rms_eps, lw.w_router, c->wr_pk.empty() ? nullptr : c->wr_pk[l], rows, d,
+                       m.n_experts, m.top_k, c->a, c->eidx, c->gates, s);
   });
   if (dbg && dbg->h_mid)
     (void)hipMemcpyAsync(dbg->h_mid + static_cast<long>(l) * rows * d, c->h,
@@ -545,6 +546,14 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
       const dg_layer_weights& lw = c->layers[l];
       launch_moe_pack(lw.w_gate, lw.w_up, c->pk1[l], E, F, m.d_model, kGroupTiles1, nullptr);
       launch_moe_pack(lw.w_down, nullptr, c->pk2[l], E, m.d_model, F, kGroupTiles2, nullptr);
+    }
+  }
+  // router weights, repacked once into the fragment order of the MFMA router
+  if (router_mfma_path(m.d_model, m.n_experts)) {
+    c->wr_pk.assign(m.n_layers, nullptr);
+    for (int l = 0; ok && l < m.n_layers; ++l) {
+      ok = c->alloc(&c->wr_pk[l], 64L * m.d_model);
+      if (ok) launch_router_pack(c->layers[l].w_router, m.n_experts, m.d_model, c->wr_pk[l], nullptr);
     }
   }
   c->wqkv.assign(m.n_layers, nullptr);

@@ -31,16 +31,18 @@ void launch_embed(const int32_t* tok, const uint16_t* embed, float* h, int rows,
 void launch_rmsnorm(const float* h, const float* gain, float eps, uint16_t* out, int rows, int d,
                     hipStream_t s);
 void launch_f32_to_bf16(const float* in, uint16_t* out, long n, hipStream_t s);
-// ffn norm + router: b = bf16(rms(h)*gain); logits in fp32 from the fp32 normed row;
-// top-k (value desc, index asc); softmax gates over the k picks.
-// Residual update + FFN norm + router, one row per work-group: h += sum_z part_z (n_part
-// split-K slices, z order; written back); x = h * rsqrt(mean h^2 + eps) * gain in float32 and
-// its bf16 copy b (the experts' input); router logits W_router x in float32; top-k (value desc,
-// index asc); softmax gates over the k picks.
+// Residual update + FFN norm + router: h += sum_z part_z (n_part split-K slices, z order;
+// written back); x = h * rsqrt(mean h^2 + eps) * gain in float32 and its bf16 copy b (the
+// experts' input); router logits W_router x from the float32 x; top-k (value desc, index asc);
+// softmax gates over the k picks.  With w_router_packed (the launch_router_pack copy, when
+// router_mfma_path holds) the logits run on MFMA as W (hi + lo), hi = bf16(x), lo = bf16(x - hi),
+// float32 accumulation; otherwise on the vector ALUs in float32.
+bool router_mfma_path(int d, int n_exp);
+void launch_router_pack(const uint16_t* w_router, int n_exp, int d, uint16_t* out, hipStream_t s);
 void launch_norm_router(float* h, const float* part, int n_part, long part_stride,
-                        const float* gain, float eps, const uint16_t* w_router, int rows, int d,
-                        int n_exp, int top_k, uint16_t* b_out, int32_t* idx, float* gates,
-                        hipStream_t s);
+                        const float* gain, float eps, const uint16_t* w_router,
+                        const uint16_t* w_router_packed, int rows, int d, int n_exp, int top_k,
+                        uint16_t* b_out, int32_t* idx, float* gates, hipStream_t s);
 
 // Destination of the fused QKV projection (EPI_ROPE_QKV): q heads and k heads rotated with
 // the table (rotate-half; null table = no rotation), q -> q [rows][Hq*D] bf16, k / v ->

@@ -14,67 +14,69 @@ namespace dg {
 namespace {
 
 // ------------------------------------------------------------------------------ permute
-// One 1024-thread work-group.  Routes r = t*top_k + j are ranked by (expert, r): counts per
-// expert (LDS integer atomics; the totals are order-independent), exclusive scan, then per
-// 1024-route chunk each wave finds equal-expert lanes with 7 ballots, ranks within the wave
-// by popcount, and offsets by the earlier waves' counts and the earlier chunks' totals.
-__global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __restrict__ idx,
-                                                           int n, int n_exp,
-                                                           int32_t* __restrict__ offs,
-                                                           int32_t* __restrict__ perm,
-                                                           int32_t* __restrict__ inv) {
-  __shared__ int cnt[64];
-  __shared__ int base[64];
-  __shared__ int wcnt[16][64];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid < 64) cnt[tid] = 0;
-  __syncthreads();
-  for (int r = tid; r < n; r += 1024) atomicAdd(&cnt[idx[r]], 1);
-  __syncthreads();
-  if (tid < 64) {
-    // exclusive scan over 64 experts in one wave
-    int c = (tid < n_exp) ? cnt[tid] : 0;
-    int incl = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    const int excl = incl - c;
-    base[tid] = excl;
-    if (tid < n_exp) offs[tid] = excl;
-    if (tid == 0) offs[n_exp] = n;
-  }
+// Stable sort of the routes r = t*top_k + j by (expert, r), one work-group of 8 waves per expert
+// e.  Wave w owns the contiguous routes [w S, (w + 1) S) (S a multiple of 64): in a first
+// sweep it counts, with two ballots per 64 routes, the routes of expert e and of lower experts;
+// one barrier shares the eight counts, which give offs[e] (all routes of lower experts) and
+// the routes of e in earlier waves; a second sweep places the wave's routes of e in route
+// order.  Each sweep requests up to kPermBatch groups of 64 routes at once.
+constexpr int kPermWaves = 8, kPermBatch = 16;
+__global__ __launch_bounds__(64 * kPermWaves) void moe_permute_kernel(const int32_t* __restrict__ idx,
+                                                                     int n, int n_exp,
+                                                                     int32_t* __restrict__ offs,
+                                                                     int32_t* __restrict__ perm,
+                                                                     int32_t* __restrict__ inv) {
+  __shared__ int wc[2][kPermWaves];
+  const int e = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int per = (n + 64 * kPermWaves - 1) / (64 * kPermWaves);  // groups of 64 per wave
+  const int g0 = w * per;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < n; c0 += 1024) {
-    wcnt[w][lane] = 0;
-    __syncthreads();
-    const int r = c0 + tid;
-    const int e = (r < n) ? idx[r] : 127;
-    unsigned long long match = ~0ull;
+  int c_eq = 0, c_lt = 0;
+  for (int gb = 0; gb < per; gb += kPermBatch) {
+    int ex[kPermBatch];
 #pragma unroll
-    for (int bit = 0; bit < 7; ++bit) {
-      const bool set = (e >> bit) & 1;
-      const unsigned long long bal = __ballot(set);
-      match &= set ? bal : ~bal;
+    for (int i = 0; i < kPermBatch; ++i) {
+      const int r = (g0 + gb + i) * 64 + lane;
+      ex[i] = (gb + i < per && r < n) ? idx[r] : 0x7fffffff;
     }
-    const int rank = __popcll(match & below);
-    if (r < n && rank == 0) wcnt[w][e] = __popcll(match);
-    __syncthreads();
-    if (r < n) {
-      int pre = 0;
-      for (int v = 0; v < w; ++v) pre += wcnt[v][e];
-      const int p = base[e] + pre + rank;
-      perm[p] = r;
-      inv[r] = p;
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i) {
+      c_eq += __popcll(__ballot(ex[i] == e));
+      c_lt += __popcll(__ballot(ex[i] < e));
     }
-    __syncthreads();
-    if (tid < 64) {
-      int tot = 0;
-      for (int v = 0; v < 16; ++v) tot += wcnt[v][tid];
-      base[tid] += tot;
+  }
+  if (lane == 0) {
+    wc[0][w] = c_eq;
+    wc[1][w] = c_lt;
+  }
+  __syncthreads();
+  int run = 0, p0 = 0;
+  for (int v = 0; v < kPermWaves; ++v) {
+    if (v < w) run += wc[0][v];
+    p0 += wc[1][v];
+  }
+  if (threadIdx.x == 0) {
+    offs[e] = p0;
+    if (e == n_exp - 1) offs[n_exp] = n;
+  }
+  for (int gb = 0; gb < per; gb += kPermBatch) {
+    int ex[kPermBatch];
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i) {
+      const int r = (g0 + gb + i) * 64 + lane;
+      ex[i] = (gb + i < per && r < n) ? idx[r] : 0x7fffffff;
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i) {
+      const unsigned long long eq = __ballot(ex[i] == e);
+      if (ex[i] == e) {
+        const int r = (g0 + gb + i) * 64 + lane;
+        const int p = p0 + run + __popcll(eq & below);
+        perm[p] = r;
+        inv[r] = p;
+      }
+      run += __popcll(eq);
+    }
   }
 }
 
@@ -480,8 +482,8 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
 
 void launch_moe_permute(const int32_t* idx, int n_routes, int n_exp, int32_t* offs, int32_t* perm,
                         int32_t* inv, hipStream_t s) {
-  hipLaunchKernelGGL(moe_permute_kernel, dim3(1), dim3(1024), 0, s, idx, n_routes, n_exp, offs,
-                     perm, inv);
+  hipLaunchKernelGGL(moe_permute_kernel, dim3(n_exp), dim3(64 * kPermWaves), 0, s, idx, n_routes,
+                     n_exp, offs, perm, inv);
 }
 
 // Row tiles per pass from the mean routed rows per expert, sized so that the busiest expert
