@@ -70,10 +70,14 @@ struct philox_out { uint32_t x[4]; };
 
 DG_DEVICE philox_out philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                    uint32_t k0, uint32_t k1) {
+  // each 32x32->64 product as one 64-bit multiply: one v_mad_u64_u32 instead of a low and a
+  // high multiply
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint64_t p0 = static_cast<uint64_t>(c0) * 0xD2511F53u;
+    const uint64_t p1 = static_cast<uint64_t>(c2) * 0xCD9E8D57u;
+    const uint32_t lo0 = static_cast<uint32_t>(p0), hi0 = static_cast<uint32_t>(p0 >> 32);
+    const uint32_t lo1 = static_cast<uint32_t>(p1), hi1 = static_cast<uint32_t>(p1 >> 32);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
     k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
@@ -86,7 +90,12 @@ enum : uint32_t { kStreamGumbel = 0, kStreamRenoise = 1, kStreamInit = 2 };
 
 // Uniform in (0,1): ((w >> 9) + 0.5) * 2^-23, exact in fp32.
 DG_DEVICE float u01(uint32_t w) { return (static_cast<float>(w >> 9) + 0.5f) * 0x1p-23f; }
-DG_DEVICE float gumbel(uint32_t w) { return -logf(-logf(u01(w))); }
+// Gumbel(0,1) = -ln(-ln u) with the hardware base-2 logarithm (about one ulp; u >= 2^-24 and
+// -ln u >= 2^-24 keep both arguments normal): -ln2 log2(-ln2 log2 u).
+DG_DEVICE float gumbel(uint32_t w) {
+  constexpr float kLn2 = 0.69314718055994531f;
+  return -kLn2 * __log2f(-kLn2 * __log2f(u01(w)));
+}
 // Uniform token in [0, V): multiply-shift.
 DG_DEVICE int32_t token_from_word(uint32_t w, uint32_t vocab) {
   return static_cast<int32_t>((static_cast<uint64_t>(w) * vocab) >> 32);

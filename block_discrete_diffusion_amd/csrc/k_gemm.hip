@@ -430,10 +430,12 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restr
 
 // ------------------------------------------------------------------------------------------
 // Fused vocab head.  Per lane and token: the four logits z of vocab entries v0..v0+3 (v0 a
-// multiple of 4) give t = z / T, Gumbel noise from one Philox call (counter v0>>2, position,
-// step, request), and running max / sum(exp) / sum(exp*t) / best (score, index, t).  Lanes of
-// the same token merge with two butterfly steps; one record per (token, wave slice of BF/2
-// vocab entries) goes to `part`.
+// multiple of 4) give t = z * (1 / T), Gumbel noise from one Philox call (counter v0>>2,
+// position, step, request), and running max / sum(exp) / sum(exp*t) / best (score, index, t).
+// Lanes of the same token merge with two butterfly steps; one record per (token, wave slice of
+// BF/2 vocab entries) goes to `part`.  The exponentials and the noise's logarithms use the
+// hardware base-2 instructions (about one ulp each): the statistics are float32 sums either
+// way, and the Gumbel-max pick only depends on them at ties closer than that.
 // ------------------------------------------------------------------------------------------
 struct Stat {
   float m, s, st, bs, bt, tc;
@@ -448,7 +450,7 @@ DG_DEVICE Stat merge_stat(const Stat& a, const Stat& b) {
     r = a;
   } else {
     r.m = fmaxf(a.m, b.m);
-    const float ea = expf(a.m - r.m), eb = expf(b.m - r.m);
+    const float ea = __expf(a.m - r.m), eb = __expf(b.m - r.m);
     r.s = a.s * ea + b.s * eb;
     r.st = a.st * ea + b.st * eb;
   }
@@ -486,7 +488,7 @@ DG_DEVICE void head_stats(const HeadArgs& a, const floatx4_t (&acc)[FM][TN], int
     const int b = tc / a.map.rows_per_req;
     const int pos = a.map.pos0[b] + (tc - b * a.map.rows_per_req);
     const int cur = ok ? a.cur_tok[tc] : -1;
-    const float temp_b = a.temp[b];
+    const float inv_temp = 1.0f / a.temp[b];
     float tv[FM][4];
     Stat st;
     st.m = -INFINITY; st.s = 0.f; st.st = 0.f; st.bs = -INFINITY; st.bt = 0.f; st.tc = NAN;
@@ -500,7 +502,7 @@ DG_DEVICE void head_stats(const HeadArgs& a, const floatx4_t (&acc)[FM][TN], int
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float z = acc[fm][tn][i];
-        const float t_ = z / temp_b;
+        const float t_ = z * inv_temp;
         tv[fm][i] = t_;
         const float sc = t_ + gumbel(rnd.x[i]);
         if (sc > st.bs) { st.bs = sc; st.bi = v0 + i; st.bt = t_; }
@@ -513,7 +515,7 @@ DG_DEVICE void head_stats(const HeadArgs& a, const floatx4_t (&acc)[FM][TN], int
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = expf(tv[fm][i] - st.m);
+        const float e = __expf(tv[fm][i] - st.m);
         st.s += e;
         st.st += e * tv[fm][i];
       }
