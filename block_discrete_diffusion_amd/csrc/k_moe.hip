@@ -95,24 +95,31 @@ __global__ __launch_bounds__(64 * kPermWaves) void moe_permute_kernel(const int3
 // issue the loads of chunk c+2; barrier.  Loads are unconditional (clamped chunk and row
 // indices) and the loop body is the same on every trip, so the compiler's wait counts leave
 // the younger chunks in flight.
-template <bool GATED, int TT, int KS, int FPW, bool F8>
-__global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
+template <bool GATED, int TT, int KS, int FPW, bool F8, bool FUSED, int SG>
+__global__ __launch_bounds__(256 * SG) void expert_stream_kernel(MoeArgs a) {
+  static_assert(!FUSED || GATED, "only the gate/up projection ranks the routes itself");
+  static_assert(!FUSED || SG == 1, "the route ranking assumes four waves");
   constexpr int NA = GATED ? 2 : 1;
-  constexpr int GT = 4 * FPW;  // tiles per work-group = tiles per packed group
+  constexpr int GT = 4 * FPW;  // tiles per packed group = tiles of one four-wave subgroup
   static_assert(!F8 || KS == 2, "E4M3 fragments come in pairs of k-steps");
+  constexpr int NTH = 256 * SG;
   constexpr int KC = 32 * KS, ROWS = TT * 16, LDX = KC + 8, CPR = KC / 8;
-  constexpr int PIECES = ROWS * CPR, PPT = (PIECES + 255) / 256;
+  constexpr int PIECES = ROWS * CPR, PPT = (PIECES + NTH - 1) / NTH;
   __shared__ uint16_t xs[2][ROWS * LDX];
-  __shared__ int rl[GATED ? kFusedRoutes : 1];  // this expert's routes, in route order
+  // this expert's routes, in route order (only when the kernel ranks them itself: the array
+  // would otherwise cost a work-group slot per CU at the largest row tiles)
+  __shared__ int rl[FUSED ? kFusedRoutes : 1];
   __shared__ int wc[2][4];
   const int e = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wq = w & 3, sg = w >> 2;  // wave of subgroup sg, which streams packed group G SG + sg
   const int j4 = lane >> 4, l16 = lane & 15;
-  const int ft0 = blockIdx.x * GT + w * FPW;
+  const int grp = blockIdx.x * SG + sg;
+  const int ft0 = grp * GT + wq * FPW;
   const int S = a.K / 32, nch = S / KS;
-  const long wgrp = static_cast<long>(e) * (a.N / (16 * GT)) + blockIdx.x;  // packed tile group
-  const uint16_t* wp = F8 ? nullptr : a.wp + (wgrp * S * GT + w * FPW) * NA * 512 + lane * 8;
-  const uint8_t* wp8 = F8 ? a.wp8 + ((wgrp * (S / 2) * GT + w * FPW) * NA * 64 + lane) * 16 : nullptr;
+  const long wgrp = static_cast<long>(e) * (a.N / (16 * GT)) + grp;  // packed tile group
+  const uint16_t* wp = F8 ? nullptr : a.wp + (wgrp * S * GT + wq * FPW) * NA * 512 + lane * 8;
+  const uint8_t* wp8 = F8 ? a.wp8 + ((wgrp * (S / 2) * GT + wq * FPW) * NA * 64 + lane) * 16 : nullptr;
   // bf16: one 16-byte fragment per (k-step, tile, matrix); E4M3: one 16-byte load holds the
   // fragments of both k-steps of the chunk, widened to bf16 (exactly) right before the MFMA
   constexpr int WS = F8 ? 1 : KS;
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
         }
   };
   int p0, n_e;
-  const bool fused = GATED && a.idx != nullptr;  // uniform
+  constexpr bool fused = FUSED;  // the launch picks it when a.idx is set
   if (fused) {
     // rank this expert's routes from the router's choices: p0 = routes of lower experts, and
     // the routes of expert e in route order, i.e. the order of a stable sort by (expert,
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
     bool keep[PPT];
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-      const int piece = tid + 256 * j, pc = min(piece, PIECES - 1);
+      const int piece = tid + NTH * j, pc = min(piece, PIECES - 1);
       const int r = pc / CPR, col = (pc % CPR) * 8;
       const int rr = min(ps + r, n_e - 1);
       const long row = GATED ? ((fused ? rl[rr] : a.perm[p0 + rr]) / a.top_k) : static_cast<long>(p0 + rr);
@@ -238,6 +245,11 @@ __global__ __launch_bounds__(256) void expert_stream_kernel(MoeArgs a) {
           for (int f = 0; f < FPW; ++f)
 #pragma unroll
             for (int q = 0; q < NA; ++q) acc[f][q][t] = mfma16(frag(b, ks, f, q), xf, acc[f][q][t]);
+          // with several subgroups (fewer registers per wave) the fragment reads go in pairs
+          // of tiles instead of all ahead of the products
+          if constexpr (SG > 1) {
+            if (t % 2 == 1) sched_fence();
+          }
         }
     };
     load_x(0);
@@ -494,10 +506,33 @@ template <bool GATED, int FPW, bool F8>
 void launch_stream_t(const MoeArgs& a, int mean_rows, hipStream_t s) {
   const dim3 grid(a.N / (64 * FPW), a.n_exp, 2);
   constexpr int KS1 = F8 ? 2 : 1;  // E4M3 fragments come in pairs of k-steps
-  if (mean_rows <= 24) hipLaunchKernelGGL((expert_stream_kernel<GATED, 3, KS1, FPW, F8>), grid, dim3(256), 0, s, a);
-  else if (mean_rows <= 36) hipLaunchKernelGGL((expert_stream_kernel<GATED, 4, 2, FPW, F8>), grid, dim3(256), 0, s, a);
-  else if (mean_rows <= 84) hipLaunchKernelGGL((expert_stream_kernel<GATED, 8, 2, FPW, F8>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((expert_stream_kernel<GATED, 10, 2, FPW, F8>), grid, dim3(256), 0, s, a);
+  if (GATED && a.idx) {
+    constexpr bool FU = GATED;  // (the branch is only taken for the gate/up projection)
+    if (mean_rows <= 24) hipLaunchKernelGGL((expert_stream_kernel<GATED, 3, KS1, FPW, F8, FU, 1>), grid, dim3(256), 0, s, a);
+    else if (mean_rows <= 36) hipLaunchKernelGGL((expert_stream_kernel<GATED, 4, 2, FPW, F8, FU, 1>), grid, dim3(256), 0, s, a);
+    else if (mean_rows <= 84) hipLaunchKernelGGL((expert_stream_kernel<GATED, 8, 2, FPW, F8, FU, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((expert_stream_kernel<GATED, 10, 2, FPW, F8, FU, 1>), grid, dim3(256), 0, s, a);
+    return;
+  }
+  if (mean_rows <= 24) hipLaunchKernelGGL((expert_stream_kernel<GATED, 3, KS1, FPW, F8, false, 1>), grid, dim3(256), 0, s, a);
+  else if (mean_rows <= 36) hipLaunchKernelGGL((expert_stream_kernel<GATED, 4, 2, FPW, F8, false, 1>), grid, dim3(256), 0, s, a);
+  else if (mean_rows <= 84) hipLaunchKernelGGL((expert_stream_kernel<GATED, 8, 2, FPW, F8, false, 1>), grid, dim3(256), 0, s, a);
+  else {
+    // many rows per expert: every feature group re-reads the expert's staged rows, so the
+    // groups of one expert share a work-group (SG subgroups of four waves, one staging of the
+    // rows) while the grid still holds a work-group per CU.  With one work-group per CU an
+    // expert whose rows need a second pass would add a second round of work-groups, so a pass
+    // holds 192 rows here (a uniform router's 128 per expert plus five standard deviations;
+    // 32-column chunks for the gate/up pair, whose registers then fit 12 waves per CU)
+    constexpr int SG = GATED ? 3 : 2;
+    constexpr int KSG = (GATED && !F8) ? 1 : 2;  // registers: 12 waves per CU hold 170 each
+    if (!(GATED && F8) && (a.N / (64 * FPW)) % SG == 0 && (a.N / (64 * FPW * SG)) * a.n_exp >= 256) {
+      const dim3 g(a.N / (64 * FPW * SG), a.n_exp, 2);
+      hipLaunchKernelGGL((expert_stream_kernel<GATED, 12, KSG, FPW, F8, false, SG>), g, dim3(256 * SG), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((expert_stream_kernel<GATED, 10, 2, FPW, F8, false, 1>), grid, dim3(256), 0, s, a);
+    }
+  }
 }
 
 template <bool GATED, int FPW>
