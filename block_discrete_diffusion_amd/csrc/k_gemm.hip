@@ -374,6 +374,69 @@ struct DlMainloop {
   }
 };
 
+// Fused QKV epilogue through LDS (the large tiles): after the last k-step the ring is free; each
+// lane rotates its rotation pairs as rope_store does and writes the bf16 results into a
+// [token][feature] tile at their place in the head (d = j, j + 1 and j + D/2, j + D/2 + 1), then
+// every thread writes 16-byte pieces of whole head rows (16 consecutive threads cover one
+// 256-byte row of D = 128).  The per-lane stores of rope_store cover 32 bytes per token row
+// each; here each request stores whole rows.  Needs work-group tiles that hold whole heads of q,
+// k or v (RA a multiple of D at the q/k and k/v boundaries).  Row pitch 528 bytes: the 4-byte
+// writes of 16 tokens x 4 lanes and the 16-byte reads hit distinct banks.
+constexpr int kQkvPitch = 264;  // bf16 elements per staged token row (256 features + 8)
+template <class C, class Acc>
+DG_DEVICE void qkv_staged_store(const RopeArgs& r, uint16_t* tile, const Acc& acc, int n_tok, int t0,
+                                int f0, int wa, int wt) {
+  constexpr int FM = C::RA / C::NWA / 16, TN = C::WT / 16, WF = C::RA / C::NWA;
+  static_assert(C::RA == 256, "one staged row per token holds 256 features");
+  const int lane = threadIdx.x & 63, l16 = lane & 15, j4 = lane >> 4;
+  const int D = r.D, qk = (r.Hq + r.Hkv) * D;
+  __syncthreads();  // every wave has read its last fragments from the ring
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const int tl = wt * C::WT + tn * 16 + l16, fl = wa * WF + fm * 16 + 4 * j4;
+      const int t = min(t0 + tl, n_tok - 1);  // rows past n_tok are staged but never stored
+      const int f = f0 + fl;
+      const floatx4_t v = acc[fm][tn];
+      uint16_t* row = tile + tl * kQkvPitch;
+      if (f < qk) {
+        const int hb = ((f - f0) / D) * D, j = ((f - f0 - hb) >> 2) * 2;
+        float y0 = v[0], y1 = v[1], y2 = v[2], y3 = v[3];
+        if (r.table) {
+          const floatx4_t cs = *reinterpret_cast<const floatx4_t*>(r.table + (static_cast<long>(t) * (D / 2) + j) * 2);
+          y0 = v[0] * cs[0] - v[1] * cs[1];
+          y1 = v[1] * cs[0] + v[0] * cs[1];
+          y2 = v[2] * cs[2] - v[3] * cs[3];
+          y3 = v[3] * cs[2] + v[2] * cs[3];
+        }
+        *reinterpret_cast<uint32_t*>(row + hb + j) = pack_bf2(y0, y2);
+        *reinterpret_cast<uint32_t*>(row + hb + j + D / 2) = pack_bf2(y1, y3);
+      } else {
+        *reinterpret_cast<u32x2_t*>(row + fl) = u32x2_t{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+      }
+    }
+  __syncthreads();
+  constexpr int PIECES = C::BT * 32;  // 16-byte pieces of the staged tile
+  const int cpr = D / 8;               // pieces per head row
+#pragma unroll
+  for (int i = 0; i < (PIECES + 64 * C::NW - 1) / (64 * C::NW); ++i) {
+    const int c = threadIdx.x + 64 * C::NW * i;
+    if (c >= PIECES) break;
+    const int tl = c >> 5, pc = c & 31, t = t0 + tl;
+    if (t >= n_tok) continue;
+    const int f = f0 + pc * 8;                 // first feature of the piece
+    const int h = f / D, dd = f - h * D;       // head (q heads, then k, then v) and dim
+    const int b = t / r.map.rows_per_req, i_r = t - b * r.map.rows_per_req;
+    uint16_t* dst;
+    if (f < r.Hq * D) dst = r.q + static_cast<long>(t) * r.Hq * D + f;
+    else if (f < qk) dst = r.k_dst + ((static_cast<long>(b) * r.Hkv + (h - r.Hq)) * r.kv_cap + r.slot0[b] + i_r) * D + dd;
+    else dst = r.v_dst + ((static_cast<long>(b) * r.Hkv + (h - r.Hq - r.Hkv)) * r.kv_cap + r.slot0[b] + i_r) * D + dd;
+    (void)cpr;
+    st16(dst, ld16(tile + tl * kQkvPitch + pc * 8));
+  }
+}
+
 template <class C, int EPI>
 __global__ __launch_bounds__(64 * C::NW) void gemm_dl_kernel(GemmArgs a, int S) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
@@ -395,6 +458,13 @@ __global__ __launch_bounds__(64 * C::NW) void gemm_dl_kernel(GemmArgs a, int S) 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wa = wave % C::NWA, wt = wave / C::NWA;
   constexpr int NF = DUAL ? ML::FM / 2 : ML::FM;
+  if constexpr (EPI == EPI_ROPE_QKV && C::RA == 256 && sizeof(DlSmem<C>) >= C::BT * kQkvPitch * 2) {
+    const RopeArgs& r = a.rope;
+    if ((r.D == 64 || r.D == 128) && ((r.Hq + r.Hkv) * r.D) % BF == 0 && (r.Hkv * r.D) % BF == 0) {
+      qkv_staged_store<C>(r, reinterpret_cast<uint16_t*>(&sm), ml.acc, a.n_tok, t0, f0, wa, wt);
+      return;
+    }
+  }
 #pragma unroll
   for (int fm = 0; fm < NF; ++fm)
 #pragma unroll
