@@ -437,6 +437,37 @@ DG_DEVICE void qkv_staged_store(const RopeArgs& r, uint16_t* tile, const Acc& ac
   }
 }
 
+// Residual-adding epilogue through LDS (unsplit large tiles): the fp32 products go into a
+// [token][feature] tile in the freed ring (row pitch RA + 4 floats), then every thread adds
+// 16-byte pieces of whole output rows to h (one read and one write of 16 bytes each, 32
+// consecutive threads covering a 512-byte row at RA = 128) instead of each lane updating 16
+// bytes of 16 rows.
+template <class C, class Acc>
+DG_DEVICE void add_staged_store(const GemmArgs& a, float* tile, const Acc& acc, int t0, int f0, int wa,
+                                int wt) {
+  constexpr int FM = C::RA / C::NWA / 16, TN = C::WT / 16, WF = C::RA / C::NWA, P = C::RA + 4;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, j4 = lane >> 4;
+  __syncthreads();  // every wave has read its last fragments from the ring
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+      *reinterpret_cast<floatx4_t*>(tile + (wt * C::WT + tn * 16 + l16) * P + wa * WF + fm * 16 + 4 * j4) = acc[fm][tn];
+  __syncthreads();
+  constexpr int PR = C::RA / 4, PIECES = C::BT * PR;  // 16-byte pieces per row, per tile
+#pragma unroll
+  for (int i = 0; i < (PIECES + 64 * C::NW - 1) / (64 * C::NW); ++i) {
+    const int c = threadIdx.x + 64 * C::NW * i;
+    if (c >= PIECES) break;
+    const int tl = c / PR, pc = c % PR, t = t0 + tl;
+    if (t >= a.n_tok) continue;
+    floatx4_t* o = reinterpret_cast<floatx4_t*>(a.out_f32 + static_cast<long>(t) * a.ldo + f0 + pc * 4);
+    floatx4_t v = *o;
+    v += *reinterpret_cast<const floatx4_t*>(tile + tl * P + pc * 4);
+    *o = v;
+  }
+}
+
 template <class C, int EPI>
 __global__ __launch_bounds__(64 * C::NW) void gemm_dl_kernel(GemmArgs a, int S) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16);
@@ -458,6 +489,12 @@ __global__ __launch_bounds__(64 * C::NW) void gemm_dl_kernel(GemmArgs a, int S) 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wa = wave % C::NWA, wt = wave / C::NWA;
   constexpr int NF = DUAL ? ML::FM / 2 : ML::FM;
+  if constexpr (EPI == EPI_ADD_F32 && sizeof(DlSmem<C>) >= C::BT * (C::RA + 4) * 4) {
+    if (S == 1) {
+      add_staged_store<C>(a, reinterpret_cast<float*>(&sm), ml.acc, t0, f0, wa, wt);
+      return;
+    }
+  }
   if constexpr (EPI == EPI_ROPE_QKV && C::RA == 256 && sizeof(DlSmem<C>) >= C::BT * kQkvPitch * 2) {
     const RopeArgs& r = a.rope;
     if ((r.D == 64 || r.D == 128) && ((r.Hq + r.Hkv) * r.D) % BF == 0 && (r.Hkv * r.D) % BF == 0) {
