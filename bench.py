@@ -85,10 +85,16 @@ def causal_attention_flops(shape, n: int, chunk: int) -> float:
 # only for the kernel source it was taken on: a changed source reports traffic null.
 PMC_TRAFFIC = {
     "moe_gemm1_swiglu": {
-        "kernel": "expert_stream_kernel<true, 3, 1, 1, false>", "workload": "full_canvas_loop",
-        "source": "block_discrete_diffusion_amd/csrc/k_moe.hip", "sha": "b37d0147617978a9",
-        "fetch_kib": 202317.0, "fetch_scale": 1048576.0 / 524307.7,  # copy of 1 GiB reads 524308 KiB
-        "write_kib": 1550.0, "write_scale": 1048576.0 / 1048576.0,   # and writes 1048576 KiB
+        "kernel": "expert_stream_kernel<true, 3, 1, 1, false, true, 1>", "workload": "full_canvas_loop",
+        "source": "block_discrete_diffusion_amd/csrc/k_moe.hip", "sha": "40382b2f9f3106e9",
+        "fetch_kib": 202148.6, "fetch_scale": 1048576.0 / 524314.9,  # copy of 1 GiB reads 524315 KiB
+        "write_kib": 1487.8, "write_scale": 1048576.0 / 1048576.0,   # and writes 1048576 KiB
+    },
+    "attention": {
+        "kernel": "attention_pipe_kernel<8>", "workload": "batch8_ragged_32k",
+        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "581a6366ef07609a",
+        "fetch_kib": 571560.2, "fetch_scale": 1048576.0 / 524314.9,
+        "write_kib": 66735.8, "write_scale": 1048576.0 / 1048576.0,
     },
 }
 
