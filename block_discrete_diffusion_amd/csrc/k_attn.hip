@@ -330,17 +330,18 @@ void attention_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ pipelined canvas kernel
-// The canvas attention over long key ranges (no mask) at head_dim 128, 8 waves of two 16-row
-// query tiles each, built so that each wave keeps its matrix unit and its vector unit busy at
-// the same time:
+// Attention over long key ranges at head_dim 128 (the canvas, unmasked, and the causal
+// prefill, whose mask only touches the half blocks that cross a wave's diagonal), 8 waves of
+// two 16-row query tiles each, built so that each wave keeps its matrix unit and its vector unit
+// busy at the same time:
 //  * software pipeline: while the softmax of block n runs (scale, exp, pack to bf16), the
 //    QK^T products of block n + 1 are already issued; while P V of block n runs, the maximum of
 //    block n + 1 is taken.  Two score sets alternate;
 //  * K and V blocks go from global memory straight into LDS (global_load_lds_dwordx4) through
 //    a ring of PS stages, three blocks ahead, one barrier per block; no staging registers.  A
 //    1 KB load is four whole 256-byte key rows, so every instruction reads 1 KB of contiguous
-//    memory; inside a row the 16-byte chunk c is stored at chunk c ^ (row & 15), which makes
-//    both the 16-byte K fragment reads and the transposing 8-byte V reads conflict-free;
+//    memory; inside a row the 16-byte chunk c is stored at chunk c ^ swz(row) (below), which
+//    makes both the 16-byte K fragment reads and the transposing 8-byte V reads conflict-free;
 //  * lazy rescaling: the exponent reference of a query only moves when the block maximum
 //    exceeds it by more than kLazy (log2 units), so P stays below 2^kLazy and O and its row
 //    sum are rescaled a handful of times per range instead of whenever the maximum grows; the
@@ -430,7 +431,14 @@ void attention_pipe_kernel(AttnArgs a) {
   const int n_cache = a.n_cache[b];
   const int n_keys = n_cache + a.n_extra;
   const int k_lo = by * a.req_split_keys[b];
-  const int k_hi = min(n_keys, k_lo + a.req_split_keys[b]);
+  int k_hi = min(n_keys, k_lo + a.req_split_keys[b]);
+  // causal: the work-group's range ends after its last query (a split past it is empty)
+  const int qpos0 = a.q_pos0[b] + row0;  // position of the wave's first query row
+  if (a.causal) {
+    const int last_task = min(bx * NW + NW - 1, group * n_rb - 1);
+    const int last_row = min(rows - 1, (last_task / group) * RW + RW - 1);
+    k_hi = min(k_hi, a.q_pos0[b] + last_row + 1);
+  }
   const int hi0 = min(k_hi, n_cache), lo1 = max(k_lo, n_cache);
   const int nb0 = hi0 > k_lo ? (hi0 - k_lo + KB - 1) / KB : 0;
   const int nb = nb0 + (k_hi > lo1 ? (k_hi - lo1 + KB - 1) / KB : 0);
@@ -533,17 +541,20 @@ void attention_pipe_kernel(AttnArgs a) {
       }
   };
   // keys of a partial half past the range end get -inf (uniform branch, a few per range)
+  // scores of keys past the range end, and with a causal mask of keys after the lane's query,
+  // go to -inf (uniform test: only half blocks that cross the end or the wave's diagonal)
   auto mask = [&](floatx4_t (&sc)[2][QT], int bi, int h) {
     const int k0 = first_key(bi) + 32 * h, hi = end_key(bi);
-    if (k0 + 32 <= hi) return;
+    const bool diag = a.causal && k0 + 31 > qpos0;
+    if (k0 + 32 <= hi && !diag) return;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool out = k0 + t * 16 + 4 * j4 + i >= hi;
+        const int kk = k0 + t * 16 + 4 * j4 + i;
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          if (out) sc[t][qt][i] = -INFINITY;
+          if (kk >= hi || (a.causal && kk > qpos0 + qt * 16 + l16)) sc[t][qt][i] = -INFINITY;
       }
   };
   // maximum of a half per query; move the reference (and rescale O and its sum) only when it is
@@ -791,7 +802,7 @@ void launch_combine_d(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 bool attention_pipe_path(const AttnArgs& a) {
-  return a.D == 128 && a.n_waves == 8 && a.q_tiles != 1 && !a.causal;
+  return a.D == 128 && a.n_waves == 8 && a.q_tiles != 1;
 }
 
 int attention_waves(int max_keys, bool causal) { return max_keys >= (causal ? 8192 : 2048) ? 8 : 4; }

@@ -245,6 +245,37 @@ def test_long_causal_prefill(chunk):
         m.close()
 
 
+def test_causal_prefill_chunk_over_a_long_cache():
+    """A 2048-row causal prefill chunk over 8000 cached positions (N(0,1) bf16 K/V) at head dim
+    128: its attention runs on the long-range pipelined kernel, causal, with per-request splits
+    (a split past a work-group's last query is empty).  Two layers with every expert active
+    (top-k = E, so no router tie can move a row); layer 1's K/V of the chunk depend on layer 0's
+    attention and must equal the oracle's prefill of the chunk over the same cache."""
+    dg = need_gpu()
+    shape = dataclasses.replace(synth.MID_LAYER, n_layers=2, n_experts=4, top_k=4, vocab=1024)
+    w = synth.model_weights(shape, SEED + 9)
+    L0, n = 8000, 2048
+    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=n)
+    try:
+        k, v = random_cache(shape, L0, L0 + n + 256, SEED + 10)
+        kv = dg.KV(shape, 1, L0 + n + 256, fill=None)
+        load_cache(kv, k, v, [L0])
+        toks = synth.tokens(n, shape.vocab, SEED, 501)
+        m.prefill(torch.from_numpy(toks).cuda(), [n], kv)
+        torch.cuda.synchronize()
+        assert kv.lengths == [L0 + n]
+        ck = [k[l, 0].astype(np.float64) for l in range(shape.n_layers)]
+        cv = [v[l, 0].astype(np.float64) for l in range(shape.n_layers)]
+        omodel.prefill(w, shape, toks, ck, cv, L0)
+        for l in range(shape.n_layers):
+            close(bf16_to_np(kv.k[l, 0, :, L0:L0 + n]), ck[l][:, L0:L0 + n], what=f"chunk K layer {l}", bf16_out=True)
+            close(bf16_to_np(kv.v[l, 0, :, L0:L0 + n]), cv[l][:, L0:L0 + n], what=f"chunk V layer {l}", bf16_out=True)
+        # the cached positions before the chunk are untouched
+        assert torch.equal(kv.k[:, 0, :, :L0].float().cpu(), torch.from_numpy(k[:, 0, :, :L0]))
+    finally:
+        m.close()
+
+
 def test_prefill_2048_rows_on_the_large_tile_gemms():
     """A 2048-row causal prefill at width 2048 with the shared FFN 4096: the QKV projection (RoPE
     epilogue), the split O-projection, the shared gate/up pair and the split shared down
