@@ -488,7 +488,10 @@ int dg_create(const dg_model_desc* desc, const dg_weights* weights, int32_t max_
   c->max_prefill = max_prefill_rows;
   c->r_canvas = max_batch * desc->canvas;
   c->r_max = std::max(c->r_canvas, max_prefill_rows);
-  c->part_cap = c->r_canvas * desc->n_q_heads * kMaxSplit;
+  // split partials for every row a call can hold (canvas rows or a prefill chunk), up to 4
+  // splits per row at the largest count (the per-request plan asks for about two work-groups
+  // per CU), 16 below
+  c->part_cap = std::max(c->r_canvas * kMaxSplit, c->r_max * 4) * desc->n_q_heads;
   const dg_model_desc& m = c->m;
   const long R = c->r_max, d = m.d_model, HD = m.n_q_heads * m.head_dim;
   const long nqkv = (m.n_q_heads + 2L * m.n_kv_heads) * m.head_dim;
