@@ -418,7 +418,6 @@ DG_DEVICE void qkv_staged_store(const RopeArgs& r, uint16_t* tile, const Acc& ac
     }
   __syncthreads();
   constexpr int PIECES = C::BT * 32;  // 16-byte pieces of the staged tile
-  const int cpr = D / 8;               // pieces per head row
 #pragma unroll
   for (int i = 0; i < (PIECES + 64 * C::NW - 1) / (64 * C::NW); ++i) {
     const int c = threadIdx.x + 64 * C::NW * i;
@@ -432,7 +431,6 @@ DG_DEVICE void qkv_staged_store(const RopeArgs& r, uint16_t* tile, const Acc& ac
     if (f < r.Hq * D) dst = r.q + static_cast<long>(t) * r.Hq * D + f;
     else if (f < qk) dst = r.k_dst + ((static_cast<long>(b) * r.Hkv + (h - r.Hq)) * r.kv_cap + r.slot0[b] + i_r) * D + dd;
     else dst = r.v_dst + ((static_cast<long>(b) * r.Hkv + (h - r.Hq - r.Hkv)) * r.kv_cap + r.slot0[b] + i_r) * D + dd;
-    (void)cpr;
     st16(dst, ld16(tile + tl * kQkvPitch + pc * 8));
   }
 }
