@@ -98,7 +98,7 @@ struct dg_ctx {
   int32_t* perm = nullptr;     // [r_max*k]
   int32_t* inv = nullptr;      // [r_max*k]
   uint16_t* act = nullptr;     // [r_max*k][F]
-  float* y = nullptr;          // [r_max*k][d]
+  uint16_t* y = nullptr;       // [r_max*k][d] bf16 expert outputs
   uint16_t* sact = nullptr;    // [r_max][Fs]
   uint16_t* f = nullptr;       // [r_canvas][d]
   float* head_part = nullptr;  // [r_canvas][V/64][8]
@@ -391,7 +391,7 @@ void run_layer(dg_ctx* c, int l, int n_req, int rows_per_req, const int32_t* len
                          hipMemcpyDeviceToDevice, s);
   MoeArgs g2{};
   g2.x = c->act; g2.ldx = m.d_ff_expert; g2.perm = c->perm; g2.top_k = m.top_k; g2.offs = c->offs;
-  g2.wp = c->pk2[l]; g2.K = m.d_ff_expert; g2.N = d; g2.out_f32 = c->y; g2.ldo = d;
+  g2.wp = c->pk2[l]; g2.K = m.d_ff_expert; g2.N = d; g2.out_bf16 = c->y; g2.ldo = d;
   if (m.expert_fp8) { g2.wp8 = c->pk2_8[l]; g2.wscale0 = c->sc_down[l]; }
   g2.n_exp = m.n_experts;
   timed(c, "moe_gemm2", s, [&] { launch_moe_gemm2(g2, routes / m.n_experts, s); });

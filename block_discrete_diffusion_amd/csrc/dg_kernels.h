@@ -165,7 +165,7 @@ struct MoeArgs {
   const int32_t* offs;              // [E+1]
   const uint16_t* wp;               // expert weights in the packed fragment layout (below)
   int K; int N;                     // reduction length and output features per expert
-  uint16_t* out_bf16; float* out_f32; int ldo;
+  uint16_t* out_bf16; int ldo;      // GEMM1: bf16 SwiGLU; GEMM2: the bf16 products
   int n_exp;
   // E4M3 experts (instead of wp): packed bytes and per-channel scales [E][N] of matrix q
   const uint8_t* wp8; const float* wscale0; const float* wscale1;
@@ -196,9 +196,10 @@ void launch_moe_pack_fp8(const uint8_t* q0, const uint8_t* q1, uint8_t* out, int
 // mean_rows: routed rows per expert on average (selects the token-tile depth per pass)
 void launch_moe_gemm1(const MoeArgs& a, int mean_rows, hipStream_t s);
 void launch_moe_gemm2(const MoeArgs& a, int mean_rows, hipStream_t s);
-// h[t] += sum_z part_z[t] (n_part residual slices, z order) + sum_j gate[t][j] * y[inv[t][j]];
-// with a gain also out[t] = bf16(rmsnorm(h[t]) * gain) (the next block's input)
-void launch_moe_combine(float* h, const float* part, int n_part, long part_stride, const float* y,
+// h[t] += sum_z part_z[t] (n_part residual slices, z order) + sum_j gate[t][j] * y[inv[t][j]]
+// (y: the down projection's bf16 outputs, widened exactly); with a gain also
+// out[t] = bf16(rmsnorm(h[t]) * gain) (the next block's input)
+void launch_moe_combine(float* h, const float* part, int n_part, long part_stride, const uint16_t* y,
                         const int32_t* inv, const float* gates, int rows, int d, int top_k,
                         const float* gain, float eps, uint16_t* out, hipStream_t s);
 

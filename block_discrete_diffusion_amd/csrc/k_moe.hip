@@ -303,7 +303,8 @@ __global__ __launch_bounds__(256 * SG) void expert_stream_kernel(MoeArgs a) {
             y[i] = acc[f][0][t][i] / (1.0f + expf(-acc[f][0][t][i])) * acc[f][NA - 1][t][i];
           *reinterpret_cast<u32x2_t*>(a.out_bf16 + orow) = u32x2_t{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
         } else {
-          *reinterpret_cast<floatx4_t*>(a.out_f32 + orow) = acc[f][0][t];
+          const floatx4_t v = acc[f][0][t];
+          *reinterpret_cast<u32x2_t*>(a.out_bf16 + orow) = u32x2_t{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
         }
       }
     }
@@ -406,6 +407,12 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const uint16_t* __re
   for (int c = tid; c < cols; c += 256) q[r * cols + c] = static_cast<uint8_t>(e4m3_encode(bf2f(wr[c]) / sc));
 }
 
+// Four bf16 values (two packed pairs) widened to float32, exactly.
+DG_DEVICE floatx4_t bf4(const u32x2_t& p) {
+  return floatx4_t{__uint_as_float(p[0] << 16), __uint_as_float(p[0] & 0xffff0000u),
+                   __uint_as_float(p[1] << 16), __uint_as_float(p[1] & 0xffff0000u)};
+}
+
 // Un-permute + residual, one work-group (8 waves) per row t:
 // h[t] += sum_z part_z[t] + sum_j gate[t][j] * y[inv[t*k+j]]   (z then j in order);
 // with a gain it also writes the next block's normed input out = bf16(rmsnorm(h[t]) * gain),
@@ -416,7 +423,7 @@ template <int NCH>  // 4-element chunks per thread: ceil(d / 2048)
 __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
                                                           const float* __restrict__ part,
                                                           int n_part, long part_stride,
-                                                          const float* __restrict__ y,
+                                                          const uint16_t* __restrict__ y,
                                                           const int32_t* __restrict__ inv,
                                                           const float* __restrict__ gates, int d,
                                                           int top_k, const float* __restrict__ gain,
@@ -440,7 +447,8 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
   for (int z = 0; z < kMaxParts; ++z)
     zp[z] = n_part > 0 ? part + min(z, n_part - 1) * part_stride + static_cast<long>(t) * d : hr;
   const float* gsrc = gain ? gain : hr;
-  floatx4_t v[NCH], pz[kMaxParts][NCH], yj[KJ][NCH], gv[NCH];
+  floatx4_t v[NCH], pz[kMaxParts][NCH], gv[NCH];
+  u32x2_t yj[KJ][NCH];  // four bf16 expert outputs each
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = min((tid + 512 * i) * 4, d - 4);  // clamped; chunks past d are not stored
@@ -449,7 +457,7 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
 #pragma unroll
     for (int z = 0; z < kMaxParts; ++z) pz[z][i] = *reinterpret_cast<const floatx4_t*>(zp[z] + c);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) yj[j][i] = *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(pj[j]) * d + c);
+    for (int j = 0; j < KJ; ++j) yj[j][i] = *reinterpret_cast<const u32x2_t*>(y + static_cast<long>(pj[j]) * d + c);
   }
   float ss = 0.f;
 #pragma unroll
@@ -461,11 +469,11 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
       if (z < n_part) acc += pz[z][i];
 #pragma unroll
     for (int j = 0; j < KJ; ++j)
-      if (j < top_k) acc += gj[j] * yj[j][i];
+      if (j < top_k) acc += gj[j] * bf4(yj[j][i]);
     for (int j = KJ; j < top_k; ++j) {
       const float g = gates[static_cast<long>(t) * top_k + j];
       const int p = inv[static_cast<long>(t) * top_k + j];
-      acc += g * *reinterpret_cast<const floatx4_t*>(y + static_cast<long>(p) * d + min(c, d - 4));
+      acc += g * bf4(*reinterpret_cast<const u32x2_t*>(y + static_cast<long>(p) * d + min(c, d - 4)));
     }
     v[i] += acc;
     if (c < d) {
@@ -566,7 +574,7 @@ void launch_moe_pack(const uint16_t* w0, const uint16_t* w1, uint16_t* out, int 
                      N, K, na, group_tiles);
 }
 
-void launch_moe_combine(float* h, const float* part, int n_part, long part_stride, const float* y,
+void launch_moe_combine(float* h, const float* part, int n_part, long part_stride, const uint16_t* y,
                         const int32_t* inv, const float* gates, int rows, int d, int top_k,
                         const float* gain, float eps, uint16_t* out, hipStream_t s) {
   const int nch = (d + 2047) / 2048;
