@@ -685,33 +685,43 @@ void attention_pipe_kernel(AttnArgs a) {
     wait_vm_lgkm0<0>();  // no load may still be writing this work-group's LDS at exit
   }
 
+  // Output through LDS (the ring is free once every wave has read its last stage): each wave
+  // writes its 32 rows of O / l as bf16 into [row][D + 8] rows of the ring, then stores whole
+  // 256-byte rows as 16-byte pieces (16 lanes per row), to the output when the request has one
+  // split, else to the split's partial slot; the split's exponent reference and row sum go
+  // next to it.  (Per-lane 8-byte stores would cover 32 bytes of 16 rows each.)
+  __syncthreads();
   if (!active) return;
-  // write: lane owns query qt*16+l16, dims dt*16 + 4*j4 + i; partial references in log2 units
+  constexpr int OP = D + 8;  // staged row pitch (elements): 272 bytes
+  uint16_t* ob = (wave < 3 ? st0 : wave < 6 ? st1 : st2) + (wave % 3) * 32 * OP;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
+    const float l_run = l_acc[qt][0];
+    const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const floatx4_t v = o[dt][qt];
+      *reinterpret_cast<u32x2_t*>(ob + (qt * 16 + l16) * OP + dt * 16 + 4 * j4) =
+          u32x2_t{pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv)};
+    }
     const int qr = row0 + qt * 16 + l16;
+    if (n_split_b > 1 && j4 == 0 && qr < rows) {
+      const long slot = ((qrow_base + qr) * a.Hq + hq) * a.n_split + by;
+      a.part_ml[slot * 2] = m_ref[qt];
+      a.part_ml[slot * 2 + 1] = l_run;
+    }
+  }
+  // the wave reads back only its own rows (LDS operations of a wave complete in order)
+  uint16_t* part16 = reinterpret_cast<uint16_t*>(a.part_o);
+#pragma unroll
+  for (int k = 0; k < 32 / 4; ++k) {
+    const int r = k * 4 + (lane >> 4), c = lane & 15;
+    const int qr = row0 + r;
     if (qr >= rows) continue;
     const long orow = qrow_base + qr;
-    const float l_run = l_acc[qt][0];
-    if (n_split_b == 1) {
-      const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
-      uint16_t* op = a.out + orow * a.Hq * D + hq * D;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const floatx4_t v = o[dt][qt];
-        *reinterpret_cast<u32x2_t*>(op + dt * 16 + 4 * j4) =
-            u32x2_t{pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv)};
-      }
-    } else {
-      const long slot = (orow * a.Hq + hq) * a.n_split + by;
-      float* po = a.part_o + slot * D;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<floatx4_t*>(po + dt * 16 + 4 * j4) = o[dt][qt];
-      if (j4 == 0) {
-        a.part_ml[slot * 2] = m_ref[qt];
-        a.part_ml[slot * 2 + 1] = l_run;
-      }
-    }
+    uint16_t* dst = (n_split_b == 1) ? a.out + orow * a.Hq * D + hq * D
+                                     : part16 + (((orow * a.Hq + hq) * a.n_split + by) * D);
+    st16(dst + c * 8, ld16(ob + r * OP + c * 8));
   }
 }
 
@@ -720,11 +730,13 @@ struct SplitCounts {
   int32_t n[kMaxBatch];
 };
 
-// Merge split partials in split order: O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
-// Every (max, sum) pair and every partial row of a thread is requested before any arithmetic.
-// With per-request splits a row of request b merges its own req_split[b] partials; a request
-// with one split was written by the attention kernel itself.
-template <int D>
+// Merge split partials in split order: O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, with O_s
+// the split's unnormalised fp32 output, or, from the pipelined kernel (NORM16), its normalised
+// bf16 output O_s / l_s, weighted by 2^(m_s - m) l_s.  Every (max, sum) pair and every partial
+// row of a thread is requested before any arithmetic.  With per-request splits a row of
+// request b merges its own req_split[b] partials; a request with one split was written by the
+// attention kernel itself.
+template <int D, bool NORM16>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            uint16_t* __restrict__ out, int n_rh,
@@ -737,13 +749,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   if (n_split <= 1) return;
   const int d0 = (threadIdx.x % TPR) * 4;
   const long base = static_cast<long>(rh) * stride;
+  const uint16_t* part16 = reinterpret_cast<const uint16_t*>(part_o);
   float2 ml[MS];
   floatx4_t po[MS];
+  u32x2_t ph[MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s)
     if (s < n_split) {
       ml[s] = *reinterpret_cast<const float2*>(part_ml + (base + s) * 2);
-      po[s] = *reinterpret_cast<const floatx4_t*>(part_o + (base + s) * D + d0);
+      if constexpr (NORM16) ph[s] = *reinterpret_cast<const u32x2_t*>(part16 + (base + s) * D + d0);
+      else po[s] = *reinterpret_cast<const floatx4_t*>(part_o + (base + s) * D + d0);
     }
   float m = -INFINITY;
 #pragma unroll
@@ -755,8 +770,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   for (int s = 0; s < MS; ++s) {
     if (s >= n_split || ml[s].x == -INFINITY) continue;
     const float w = exp2f(ml[s].x - m);
-    l += w * ml[s].y;
-    acc += w * po[s];
+    if constexpr (NORM16) {
+      const float wl = w * ml[s].y;
+      l += wl;
+      const u32x2_t p = ph[s];
+      acc += wl * floatx4_t{__uint_as_float(p[0] << 16), __uint_as_float(p[0] & 0xffff0000u),
+                            __uint_as_float(p[1] << 16), __uint_as_float(p[1] & 0xffff0000u)};
+    } else {
+      l += w * ml[s].y;
+      acc += w * po[s];
+    }
   }
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
   *reinterpret_cast<u32x2_t*>(out + static_cast<long>(rh) * D + d0) =
@@ -795,8 +818,12 @@ void launch_combine_d(const AttnArgs& a, hipStream_t s) {
   sc.Hq = a.Hq;
   sc.rows_per_req = a.rows_per_req;
   for (int b = 0; b < a.n_req; ++b) sc.n[b] = a.req_split[b];
-  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((n_rh + per - 1) / per), dim3(256), 0, s,
-                     a.part_o, a.part_ml, a.out, n_rh, a.n_split, sc);
+  if (a.balanced)
+    hipLaunchKernelGGL((attn_combine_kernel<D, true>), dim3((n_rh + per - 1) / per), dim3(256), 0, s,
+                       a.part_o, a.part_ml, a.out, n_rh, a.n_split, sc);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<D, false>), dim3((n_rh + per - 1) / per), dim3(256), 0, s,
+                       a.part_o, a.part_ml, a.out, n_rh, a.n_split, sc);
 }
 
 }  // namespace
