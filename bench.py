@@ -92,9 +92,9 @@ PMC_TRAFFIC = {
     },
     "attention": {
         "kernel": "attention_pipe_kernel<8>", "workload": "batch8_ragged_32k",
-        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "c10e5277fb64b811",
-        "fetch_kib": 571444.4, "fetch_scale": 1048576.0 / 524315.2,
-        "write_kib": 33840.3, "write_scale": 1048576.0 / 1048576.0,
+        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "c4dde5f338b92d7c",
+        "fetch_kib": 571461.8, "fetch_scale": 1048576.0 / 524315.2,
+        "write_kib": 33837.4, "write_scale": 1048576.0 / 1048576.0,
     },
 }
 

@@ -511,6 +511,14 @@ void attention_pipe_kernel(AttnArgs a) {
   }
   const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const float sl2 = a.scale * 1.4426950408889634f;
+  // per query tile: the exponent offset -m_ref (0 while no key has been seen), and the raw
+  // score (m_ref + kLazy) / (scale log2 e) above which the reference has to move (the scale is
+  // positive); both change only where the reference does, so a half costs one FMA per score
+  // and one compare per query tile on top of the exponentials
+  const float inv_sl2 = 1.f / sl2;
+  float neg_mu[QT], thr[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) { neg_mu[qt] = 0.f; thr[qt] = -INFINITY; }
 
   // fragment read offsets (elements) inside a stage's K and V arrays
   // row l16 of a 16-key tile, chunk (4 ks + j4) ^ f = 4 (ks ^ (f / 4)) + (j4 ^ (f % 4)), f = swz(l16)
@@ -557,32 +565,33 @@ void attention_pipe_kernel(AttnArgs a) {
           if (kk >= hi || (a.causal && kk > qpos0 + qt * 16 + l16)) sc[t][qt][i] = -INFINITY;
       }
   };
-  // maximum of a half per query; move the reference (and rescale O and its sum) only when it is
-  // exceeded by more than kLazy
-  // The check uses each lane's own maximum (no lane can exceed the reference by more than kLazy
-  // unless some lane's own maximum does); only then are the query maxima formed across the four
-  // lanes of each query and the references that must move moved.
-  auto rebase = [&](const floatx4_t (&sc)[2][QT]) {
-    float mx[QT];
+  // A half's maximum per query moves the reference (and rescales O and its sum) only when it
+  // exceeds the reference by more than kLazy.  The check takes each lane's own raw maximum (no
+  // query's maximum can pass the threshold unless one of its lanes' does); only then are the
+  // query maxima formed across the four lanes of each query and the references that must move
+  // moved.  (Scaling by a positive constant and rounding are monotonic: the maximum of the scaled
+  // scores is the scaled maximum.)
+  auto lane_max = [&](const floatx4_t (&sc)[2][QT], int qt) {
+    return fmaxf(fmaxf(fmaxf(sc[0][qt][0], sc[0][qt][1]), fmaxf(sc[0][qt][2], sc[0][qt][3])),
+                 fmaxf(fmaxf(sc[1][qt][0], sc[1][qt][1]), fmaxf(sc[1][qt][2], sc[1][qt][3])));
+  };
+  auto rebase = [&](const float (&mx)[QT]) {
     bool need = false;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float v = fmaxf(fmaxf(fmaxf(sc[0][qt][0], sc[0][qt][1]), fmaxf(sc[0][qt][2], sc[0][qt][3])),
-                            fmaxf(fmaxf(sc[1][qt][0], sc[1][qt][1]), fmaxf(sc[1][qt][2], sc[1][qt][3])));
-      mx[qt] = v * sl2;
-      need |= mx[qt] > m_ref[qt] + kLazy;
-    }
+    for (int qt = 0; qt < QT; ++qt) need |= mx[qt] > thr[qt];
     if (__any(need)) {  // uniform: every lane takes part in the cross-lane maximum
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        mx[qt] = group_max(mx[qt]);
-        const bool up = mx[qt] > m_ref[qt] + kLazy;
-        const float m_new = up ? mx[qt] : m_ref[qt];
+        const float ms = group_max(mx[qt]) * sl2;
+        const bool up = ms > m_ref[qt] + kLazy;
+        const float m_new = up ? ms : m_ref[qt];
         const float alpha = up ? fast_exp2(m_ref[qt] - m_new) : 1.f;  // 0 from -inf
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha;
         l_acc[qt] *= alpha;
         m_ref[qt] = m_new;
+        neg_mu[qt] = (m_new == -INFINITY) ? 0.f : -m_new;
+        thr[qt] = (m_new + kLazy) * inv_sl2;
       }
     }
   };
@@ -600,7 +609,9 @@ void attention_pipe_kernel(AttnArgs a) {
   // between the next half's QK^T products:
   //   QK group g (8):  the two MFMAs of K fragment g; scale, exp and pack of two P values;
   //                    request of K fragment g + 3
-  //   PV group dt (8): the two MFMAs of V^T fragment dt; request of V^T fragment dt + 3
+  //   PV group dt (8): the two MFMAs of V^T fragment dt; request of V^T fragment dt + 3; in
+  //                    groups 0-5 a piece of the next half's per-lane maxima (the vector unit
+  //                    is otherwise idle there)
   auto step = [&](auto R, auto H, floatx4_t (&cur)[2][QT], floatx4_t (&nxt)[2][QT], int n) {
     constexpr int r = decltype(R)::value, h = decltype(H)::value;
     if constexpr (h == 0) {
@@ -612,9 +623,6 @@ void attention_pipe_kernel(AttnArgs a) {
       // past the last block the next half's K is a copy whose scores are never used
       const uint16_t* kb = h == 0 ? stage(Stage<r>{}) + 32 * D : stage(Stage<r + 1>{});
       const uint16_t* vb = stage(Stage<r>{}) + KB * D + h * 32 * D;
-      float mu[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) mu[qt] = (m_ref[qt] == -INFINITY) ? 0.f : m_ref[qt];  // no key seen yet
       u32x4_t pf[QT];
       u32x4_t kf[3] = {kread(kb, 0), kread(kb, 1), kread(kb, 2)};
       sched_fence();
@@ -626,8 +634,8 @@ void attention_pipe_kernel(AttnArgs a) {
           nxt[t][qt] = mfma16(kf[g % 3], qf[qt][ks], ks == 0 ? floatx4_t{0.f, 0.f, 0.f, 0.f} : nxt[t][qt]);
         // P values 2 j, 2 j + 1 (of the 8 = keys {16 t' + 4 j4 + i}) of query tile qt
         const int qt = g >> 2, j = g & 3;
-        const float p0 = fast_exp2(fmaf(cur[j >> 1][qt][2 * (j & 1)], sl2, -mu[qt]));
-        const float p1 = fast_exp2(fmaf(cur[j >> 1][qt][2 * (j & 1) + 1], sl2, -mu[qt]));
+        const float p0 = fast_exp2(fmaf(cur[j >> 1][qt][2 * (j & 1)], sl2, neg_mu[qt]));
+        const float p1 = fast_exp2(fmaf(cur[j >> 1][qt][2 * (j & 1) + 1], sl2, neg_mu[qt]));
         uint32_t pk = pack_bf2(p0, p1);
         asm volatile("" : "+v"(pk));  // computed here, in this group (not sunk to its first use)
         pf[qt][j] = pk;
@@ -637,17 +645,34 @@ void attention_pipe_kernel(AttnArgs a) {
       const bool has_next = (h == 0) || (n + 1 < nb);
       if (has_next) mask(nxt, h == 0 ? n : n + 1, 1 - h);
       u32x4_t vf[3] = {vread(vb, 0), vread(vb, 1), vread(vb, 2)};
+      float pa[QT], pb[QT], mx[QT];
       sched_fence();
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16(vf[dt % 3], pf[qt], o[dt][qt]);
         if (dt + 3 < NDT) vf[dt % 3] = vread(vb, dt + 3);
+        // the next half's per-lane maxima, a piece per group (pinned there: not sunk to the use)
+        if (dt == 0 || dt == 3) {
+          const int qt = dt / 3;
+          pa[qt] = fmaxf(fmaxf(nxt[0][qt][0], nxt[0][qt][1]), nxt[0][qt][2]);
+          asm volatile("" : "+v"(pa[qt]));
+        }
+        if (dt == 1 || dt == 4) {
+          const int qt = dt / 3;
+          pb[qt] = fmaxf(fmaxf(nxt[0][qt][3], nxt[1][qt][0]), nxt[1][qt][1]);
+          asm volatile("" : "+v"(pb[qt]));
+        }
+        if (dt == 2 || dt == 5) {
+          const int qt = dt / 3;
+          mx[qt] = fmaxf(fmaxf(pa[qt], pb[qt]), fmaxf(nxt[1][qt][2], nxt[1][qt][3]));
+          asm volatile("" : "+v"(mx[qt]));
+        }
         sched_fence();
       }
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) l_acc[qt] = mfma16(ones, pf[qt], l_acc[qt]);
-      if (has_next) rebase(nxt);
+      if (has_next) rebase(mx);
     }
   };
 
@@ -664,7 +689,10 @@ void attention_pipe_kernel(AttnArgs a) {
     if (active) {
       qk(sa, Stage<0>{}, 0);
       mask(sa, 0, 0);
-      rebase(sa);
+      float mx[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) mx[qt] = lane_max(sa, qt);
+      rebase(mx);
     }
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
