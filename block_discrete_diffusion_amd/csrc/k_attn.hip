@@ -331,36 +331,76 @@ void attention_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ pipelined canvas kernel
 // Attention over long key ranges at head_dim 128 (the canvas, unmasked, and the causal
-// prefill, whose mask only touches the half blocks that cross a wave's diagonal), 8 waves of
-// two 16-row query tiles each, built so that each wave keeps its matrix unit and its vector unit
-// busy at the same time:
-//  * software pipeline: while the softmax of block n runs (scale, exp, pack to bf16), the
-//    QK^T products of block n + 1 are already issued; while P V of block n runs, the maximum of
-//    block n + 1 is taken.  Two score sets alternate;
+// prefill, whose mask only touches the half blocks that cross a wave's diagonal), 8 waves of one
+// 32-row query tile each, on the 32 x 32 x 16 matrix instruction:
+//  * one 32 x 32 MFMA does the work of two 16 x 16 x 32 ones but holds the SIMD's issue for
+//    about as long as one of them (measured on gfx950: each MFMA blocks vector issue for ~11
+//    cycles, whatever its size), so the softmax's vector work (an FMA, an exponential and half a
+//    pack per score) fits beside the matrix work instead of queueing behind it;
+//  * software pipeline: while the softmax of half block n runs (scale, exp, pack to bf16, row
+//    sum), the QK^T products of the next half are already issued; while P V of half n runs, the
+//    maximum of the next half is taken.  Two score tiles alternate;
 //  * K and V blocks go from global memory straight into LDS (global_load_lds_dwordx4) through
 //    a ring of PS stages, three blocks ahead, one barrier per block; no staging registers.  A
 //    1 KB load is four whole 256-byte key rows, so every instruction reads 1 KB of contiguous
-//    memory; inside a row the 16-byte chunk c is stored at chunk c ^ swz(row) (below), which
-//    makes both the 16-byte K fragment reads and the transposing 8-byte V reads conflict-free;
+//    memory; inside a row the 16-byte chunk c is stored at chunk c ^ swz_k(row) (K) or
+//    c ^ swz_v(row) (V), below, which keeps the 16-byte K fragment reads and the transposing
+//    8-byte V reads free of bank conflicts;
 //  * lazy rescaling: the exponent reference of a query only moves when the block maximum
 //    exceeds it by more than kLazy (log2 units), so P stays below 2^kLazy and O and its row
 //    sum are rescaled a handful of times per range instead of whenever the maximum grows; the
 //    result is unchanged (O and the row sum share the reference, which cancels);
 //  * the work-groups that share one (request, KV head, split) range are numbered so that they
 //    land on the same XCD, whose L2 then serves the second reader.
+//
+// Lane layouts of the 32 x 32 x 16 bf16 MFMA (D = A B): lane l holds A[l % 32][8 (l / 32) ..
+// + 8], B[8 (l / 32) .. + 8][l % 32] and D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32], i = 0..15.
+// Scores are S^T = K Q^T (keys x queries): lane l holds 16 keys of query l % 32.  P^T feeds
+// O^T += V^T P^T as the B operand in the same registers, so the keys of a 16-key chunk are taken
+// in the order that layout gives: slot s of lane half hh = l / 32 is key 8 (s / 4) + 4 hh + s % 4;
+// V^T (the A operand) is read in the same key order.
 constexpr int PS = 4;          // LDS ring stages (3 blocks in flight)
 constexpr float kLazy = 8.f;   // lazy-rescale margin, log2 units
 
 template <int S>
 using Stage = std::integral_constant<int, S % PS>;
 
-// Chunk swizzle of an LDS key row (16 chunks of 16 bytes): chunk c of row r is stored at
-// c ^ swz(r).  Measured on gfx950 with 8 waves per CU: the 16-byte K fragment reads (rows 0..15
-// of a tile, one chunk each) run at the full LDS rate when eight consecutive rows hit eight
-// distinct chunk pairs, and the transposing 8-byte V reads (two adjacent chunks 2 m, 2 m + 1 of
-// eight rows per 32 lanes) need the same; swz(r) = 2 (r % 8) gives both (K 253 B per tick and
-// CU, V 208; r itself, the plain diagonal: K 253, V 155).
-DG_DEVICE int swz(int r) { return (r & 7) << 1; }
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+DG_DEVICE floatx16_t mfma32(const u32x4_t& a, const u32x4_t& b, const floatx16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+// acc + the two bf16 values of pk (v_dot2 with (1, 1)): the row sum of the rounded P
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+DG_DEVICE float add_bf2(uint32_t pk, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
+}
+// Sum and maximum of lanes l and l ^ 32 (gfx950 permlane32 swap, no trip through LDS): called
+// with the same value in both operands the swap returns v[l] and v[l ^ 32] to every lane, as
+// (low lane, high lane) in both, so both lanes add the same two numbers in the same order.
+DG_DEVICE float pair_sum(float v) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+DG_DEVICE float pair_max(float v) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Chunk swizzles of the LDS key rows (16 chunks of 16 bytes): chunk c of K row r is stored at
+// c ^ swz_k(r), of V row r at c ^ swz_v(r).
+//  * A K fragment read takes one 16-byte chunk (2 k + hh) of 32 consecutive rows per lane half:
+//    swz_k(r) = r % 16 puts the rows on all sixteen chunk positions, two rows each (512 bytes
+//    over the 256 bytes of banks: the fewest passes there can be).  An even swizzle leaves only
+//    eight positions, four rows each (counters: a third of the LDS cycles went to conflicts).
+//  * A transposing V read takes the 32-byte pairs 2 dt and 2 dt + 1 of the four rows 4 hh .. + 3
+//    per lane half.  swz_v(r) is even, so a pair stays together and pair p goes to
+//    p ^ (swz_v(r) / 2); with swz_v(r) / 2 = 2 (r % 4) + (r / 4) % 2 the four rows' swizzles
+//    differ above the lowest pair bit, and rows r and r + 4 take opposite parities, so the
+//    eight pairs a lane half reads are distinct.
+DG_DEVICE int swz_k(int r) { return r & 15; }
+DG_DEVICE int swz_v(int r) { return ((r & 3) << 2) | ((r >> 1) & 2); }
 
 // One global_load_lds_dwordx4: lane l's 16 bytes at g land at LDS address lds + 16 l.  Issued
 // from inline assembly so that the compiler does not track it: its own tracking of such loads
@@ -384,7 +424,7 @@ DG_DEVICE void dma16(const uint16_t* base, uint32_t lane_ofs, const uint16_t* ld
 template <int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_pipe_kernel(AttnArgs a) {
-  constexpr int D = 128, QT = 2, NKS = D / 32, NDT = D / 16;
+  constexpr int D = 128, NKC = D / 16, NDT = D / 32;  // 16-dim k-chunks of QK^T; 32-dim O tiles
   constexpr int SEG = 2 * KB * D * 2 / 1024;  // 1 KB segments per stage (K then V)
   constexpr int LPW = SEG / NW;               // segments each wave loads per stage
   static_assert(SEG % NW == 0 && LPW * NW == SEG, "segments split evenly over the waves");
@@ -403,7 +443,8 @@ void attention_pipe_kernel(AttnArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
-  const int j4 = lane >> 4, l16 = lane & 15;
+  const int l32 = lane & 31, hh = lane >> 5;  // query column of the tile; lane half
+  const int l16 = lane & 15, g4 = lane >> 4;  // lane in, and index of, its 16-lane group
   // work-group -> (task group bx, unit u); unit u = (pair p, KV head g) and pair p = (request
   // b, split by), pairs longest first.  The dispatcher places work-group lin on XCD lin % 8 and
   // hands each XCD its work-groups in order, so unit u goes to XCD u % 8 with its task groups
@@ -411,7 +452,7 @@ void attention_pipe_kernel(AttnArgs a) {
   // XCD starts on the longest ranges.
   const int group = a.Hq / a.Hkv;
   const int rows = a.rows_per_req;
-  constexpr int RW = 16 * QT;
+  constexpr int RW = 32;
   const int n_rb = (rows + RW - 1) / RW;
   const int nx = (group * n_rb + NW - 1) / NW;
   const int lin = blockIdx.x;
@@ -453,7 +494,7 @@ void attention_pipe_kernel(AttnArgs a) {
 
   // this lane's part of the wave's LPW segments: segment s of a stage holds key rows
   // 4 (s % 16) .. + 3 of K (s < 16) or V; lane i fills LDS chunk i % 16 of row i / 16 with the
-  // global chunk (i % 16) ^ swz(row)
+  // global chunk (i % 16) ^ swz_k(row) (K) or ^ swz_v(row) (V)
   // (segment bases are wave-uniform: the cache and canvas arrays of K or V, the canvas one
   // offset so that both are indexed by the key's position in the request)
   int seg_row[LPW], seg_chunk[LPW];
@@ -463,7 +504,7 @@ void attention_pipe_kernel(AttnArgs a) {
   for (int i = 0; i < LPW; ++i) {
     const int s = wave * LPW + i, r = 4 * (s & 15) + (lane >> 4);
     seg_row[i] = r;
-    seg_chunk[i] = ((lane & 15) ^ swz(r)) * 8;
+    seg_chunk[i] = ((lane & 15) ^ (s < 16 ? swz_k(r) : swz_v(r))) * 8;
     seg_cb[i] = s < 16 ? kc : vc;
     seg_xb[i] = (s < 16 ? kx : vx) - static_cast<long>(n_cache) * D;
   }
@@ -483,136 +524,108 @@ void attention_pipe_kernel(AttnArgs a) {
     }
   };
 
-  // queries (B operand): lane holds Q[qt*16 + l16][ks*32 + 8*j4 .. +8]
-  u32x4_t qf[QT][NKS];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int qr = row0 + qt * 16 + l16;
+  // queries (B operand of S^T = K Q^T): lane holds Q[row0 + l32][16 c + 8 hh .. + 8]
+  u32x4_t qf[NKC];
+  {
+    const int qr = row0 + l32;
     const bool ok = active && qr < rows;
     const uint16_t* qp = a.q + (qrow_base + qr) * a.Hq * D + hq * D;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[qt][ks] = ok ? ld16(qp + ks * 32 + 8 * j4) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int c = 0; c < NKC; ++c) qf[c] = ok ? ld16(qp + 16 * c + 8 * hh) : u32x4_t{0u, 0u, 0u, 0u};
   }
   // the queries have landed before the first stage load is issued: the compiler does not see
   // those loads, so a wait it placed for a query register inside the loop would also wait for
   // the stage loads issued after it
   wait_vm_lgkm0<0>();
-  floatx4_t o[NDT][QT];
+  floatx16_t o[NDT];  // O^T tile dt: lane holds d = 32 dt + 8 (i / 4) + 4 hh + i % 4 of its query
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) o[dt][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  floatx4_t l_acc[QT];
-  float m_ref[QT];  // exponent reference (log2 units, scale folded in) of o and l_acc
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    l_acc[qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    m_ref[qt] = -INFINITY;
-  }
-  const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  // per query (each lane pair l, l ^ 32 holds the same values): exponent reference (log2
+  // units, scale folded in) of O and the row sum; the offset -m_ref (0 while no key has been
+  // seen); the raw score (m_ref + kLazy) / (scale log2 e) above which the reference has to move
+  // (the scale is positive).  All three change only where the reference does.  The row sum is
+  // this lane's keys only; the two halves are added at the end.
+  float m_ref = -INFINITY, neg_mu = 0.f, thr = -INFINITY, l_acc = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;
-  // per query tile: the exponent offset -m_ref (0 while no key has been seen), and the raw
-  // score (m_ref + kLazy) / (scale log2 e) above which the reference has to move (the scale is
-  // positive); both change only where the reference does, so a half costs one FMA per score
-  // and one compare per query tile on top of the exponentials
   const float inv_sl2 = 1.f / sl2;
-  float neg_mu[QT], thr[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) { neg_mu[qt] = 0.f; thr[qt] = -INFINITY; }
 
-  // fragment read offsets (elements) inside a stage's K and V arrays
-  // row l16 of a 16-key tile, chunk (4 ks + j4) ^ f = 4 (ks ^ (f / 4)) + (j4 ^ (f % 4)), f = swz(l16)
-  const int kf0 = swz(l16);
-  const int kofs0 = l16 * D + 8 * (j4 ^ (kf0 & 3)), kq = kf0 >> 2;  // + kt * 16 * D + 32 (ks ^ kq)
-  // transposing V reads: rows 32 h + 4 j4 + l16 / 4 (+ 16), columns dt * 16 + 4 (l16 % 4)
-  const int vr = 4 * j4 + (l16 >> 2);
-  int vofs[NDT];  // + h * 32 * D (+ 16 * D for the second tile; swz depends on row % 16 only)
+  // K fragment c of a half (A operand: key row l32, dims 16 c + 8 hh .. + 8, i.e. 16-byte chunk
+  // 2 c + hh): element offsets inside the half, one register each (the swizzle is per row; the
+  // second half's rows, 32 further, have the same swizzles)
+  int kofs[NKC];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) vofs[dt] = vr * D + (((2 * dt + ((l16 & 3) >> 1)) ^ swz(vr)) * 8) + 4 * (l16 & 1);
-
-  // The pipeline runs over half blocks of 32 keys (two 16-key tiles t of the stage's block):
-  // scores of one half are sc[t][qt], 16 registers, so two of them (the half being turned into
-  // P and the next half being multiplied) fit next to O.
-  auto qk = [&](floatx4_t (&sc)[2][QT], auto S, int h) {
+  for (int c = 0; c < NKC; ++c) kofs[c] = l32 * D + 8 * ((2 * c + hh) ^ swz_k(l32));
+  // V^T fragment (16-key chunk c, 32-dim tile dt): A operand, lane holds d = 32 dt + l32 and the
+  // keys of P's slots, 4 hh + 0..3 (lo) and 8 + 4 hh + 0..3 (hi) of the chunk.  In a transposing
+  // read, lane s of 16-lane group g4 points at row 4 hh + s / 4 (+ 8 for hi) and columns
+  // 32 dt + 16 (g4 % 2) + 4 (s % 4) .. + 4, and receives column 32 dt + l32 of those four rows.
+  // Rows 16 c + vr and 16 c + 8 + vr (and the second half's, 32 further) share vr's swizzle.
+  const int vr = 4 * hh + (l16 >> 2);
+  int vofs[NDT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) sc[t][qt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* kb = stage(S) + h * 32 * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4_t kf = ld16(kb + t * 16 * D + kofs0 + 32 * (ks ^ kq));
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) sc[t][qt] = mfma16(kf, qf[qt][ks], sc[t][qt]);
-      }
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int col = 32 * dt + 16 * (g4 & 1) + 4 * (l16 & 3);
+    vofs[dt] = vr * D + (((col >> 3) ^ swz_v(vr)) << 3) + (col & 7);
+  }
+  auto kread = [&](const uint16_t* kb, int c) { return ld16(kb + kofs[c]); };
+  auto vread = [&](const uint16_t* vb, int c, int dt) {
+    const u32x2_t lo = read_tr16(vb + 16 * c * D + vofs[dt]);
+    const u32x2_t hi = read_tr16(vb + (16 * c + 8) * D + vofs[dt]);
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   };
-  // keys of a partial half past the range end get -inf (uniform branch, a few per range)
+
   // scores of keys past the range end, and with a causal mask of keys after the lane's query,
   // go to -inf (uniform test: only half blocks that cross the end or the wave's diagonal)
-  auto mask = [&](floatx4_t (&sc)[2][QT], int bi, int h) {
+  auto mask = [&](floatx16_t& sc, int bi, int h) {
     const int k0 = first_key(bi) + 32 * h, hi = end_key(bi);
     const bool diag = a.causal && k0 + 31 > qpos0;
     if (k0 + 32 <= hi && !diag) return;
+    const int qp = qpos0 + l32;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = k0 + t * 16 + 4 * j4 + i;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          if (kk >= hi || (a.causal && kk > qpos0 + qt * 16 + l16)) sc[t][qt][i] = -INFINITY;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int kk = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      if (kk >= hi || (a.causal && kk > qp)) sc[i] = -INFINITY;
+    }
   };
   // A half's maximum per query moves the reference (and rescales O and its sum) only when it
   // exceeds the reference by more than kLazy.  The check takes each lane's own raw maximum (no
   // query's maximum can pass the threshold unless one of its lanes' does); only then are the
-  // query maxima formed across the four lanes of each query and the references that must move
-  // moved.  (Scaling by a positive constant and rounding are monotonic: the maximum of the scaled
-  // scores is the scaled maximum.)
-  auto lane_max = [&](const floatx4_t (&sc)[2][QT], int qt) {
-    return fmaxf(fmaxf(fmaxf(sc[0][qt][0], sc[0][qt][1]), fmaxf(sc[0][qt][2], sc[0][qt][3])),
-                 fmaxf(fmaxf(sc[1][qt][0], sc[1][qt][1]), fmaxf(sc[1][qt][2], sc[1][qt][3])));
+  // two lanes of each query combined and the references that must move moved.  (Scaling by a
+  // positive constant and rounding are monotonic: the maximum of the scaled scores is the
+  // scaled maximum.)
+  auto lane_max = [&](const floatx16_t& sc) {
+    float m = sc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, sc[i]);
+    return m;
   };
-  auto rebase = [&](const float (&mx)[QT]) {
-    bool need = false;
+  auto rebase = [&](float mx) {
+    if (__any(mx > thr)) {  // uniform: every lane takes part in the cross-lane maximum
+      const float ms = pair_max(mx) * sl2;
+      const bool up = ms > m_ref + kLazy;
+      const float m_new = up ? ms : m_ref;
+      const float alpha = up ? fast_exp2(m_ref - m_new) : 1.f;  // 0 from -inf
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) need |= mx[qt] > thr[qt];
-    if (__any(need)) {  // uniform: every lane takes part in the cross-lane maximum
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float ms = group_max(mx[qt]) * sl2;
-        const bool up = ms > m_ref[qt] + kLazy;
-        const float m_new = up ? ms : m_ref[qt];
-        const float alpha = up ? fast_exp2(m_ref[qt] - m_new) : 1.f;  // 0 from -inf
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha;
-        l_acc[qt] *= alpha;
-        m_ref[qt] = m_new;
-        neg_mu[qt] = (m_new == -INFINITY) ? 0.f : -m_new;
-        thr[qt] = (m_new + kLazy) * inv_sl2;
-      }
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      l_acc *= alpha;
+      m_ref = m_new;
+      neg_mu = (m_new == -INFINITY) ? 0.f : -m_new;
+      thr = (m_new + kLazy) * inv_sl2;
     }
-  };
-  // K fragment g of a half (tile g % 2, k-step g / 2), and V^T fragment dt of a half
-  auto kread = [&](const uint16_t* kb, int g) { return ld16(kb + (g & 1) * 16 * D + kofs0 + 32 * ((g >> 1) ^ kq)); };
-  auto vread = [&](const uint16_t* vb, int dt) {
-    const u32x2_t lo = read_tr16(vb + vofs[dt]);
-    const u32x2_t hi = read_tr16(vb + 16 * D + vofs[dt]);
-    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   };
   // One pipeline step on half H of block n (n % PS == R): its scores are in cur; the next half
   // ((n, 1), or (n + 1, 0) in the next stage) is multiplied into nxt meanwhile.  The step is
   // written as groups with scheduling fences between them, so that every LDS fragment is
-  // requested three groups before the MFMAs that use it and the current half's softmax sits
+  // requested three groups before the MFMA that uses it and the current half's softmax sits
   // between the next half's QK^T products:
-  //   QK group g (8):  the two MFMAs of K fragment g; scale, exp and pack of two P values;
-  //                    request of K fragment g + 3
-  //   PV group dt (8): the two MFMAs of V^T fragment dt; request of V^T fragment dt + 3; in
-  //                    groups 0-5 a piece of the next half's per-lane maxima (the vector unit
-  //                    is otherwise idle there)
-  auto step = [&](auto R, auto H, floatx4_t (&cur)[2][QT], floatx4_t (&nxt)[2][QT], int n) {
+  //   QK group c (8):  the MFMA of K chunk c; scale, exp, pack and row sum of two P values;
+  //                    request of K chunk c + 3
+  //   PV group q (8):  the MFMA of key chunk q / 4 and O tile q % 4; request of V^T fragment
+  //                    q + 3; a piece of the next half's per-lane maximum (the vector unit is
+  //                    otherwise idle there)
+  auto step = [&](auto R, auto H, floatx16_t& cur, floatx16_t& nxt, int n) {
     constexpr int r = decltype(R)::value, h = decltype(H)::value;
     if constexpr (h == 0) {
       wait_vm_lgkm0<LPW>();  // this wave's loads of block n + 1 have landed
@@ -623,56 +636,42 @@ void attention_pipe_kernel(AttnArgs a) {
       // past the last block the next half's K is a copy whose scores are never used
       const uint16_t* kb = h == 0 ? stage(Stage<r>{}) + 32 * D : stage(Stage<r + 1>{});
       const uint16_t* vb = stage(Stage<r>{}) + KB * D + h * 32 * D;
-      u32x4_t pf[QT];
+      u32x4_t pf[2];
       u32x4_t kf[3] = {kread(kb, 0), kread(kb, 1), kread(kb, 2)};
       sched_fence();
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const int t = g & 1, ks = g >> 1;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          nxt[t][qt] = mfma16(kf[g % 3], qf[qt][ks], ks == 0 ? floatx4_t{0.f, 0.f, 0.f, 0.f} : nxt[t][qt]);
-        // P values 2 j, 2 j + 1 (of the 8 = keys {16 t' + 4 j4 + i}) of query tile qt
-        const int qt = g >> 2, j = g & 3;
-        const float p0 = fast_exp2(fmaf(cur[j >> 1][qt][2 * (j & 1)], sl2, neg_mu[qt]));
-        const float p1 = fast_exp2(fmaf(cur[j >> 1][qt][2 * (j & 1) + 1], sl2, neg_mu[qt]));
+      for (int c = 0; c < NKC; ++c) {
+        nxt = mfma32(kf[c % 3], qf[c], c == 0 ? floatx16_t{} : nxt);
+        // P slots 2 c, 2 c + 1 (of the 16 = P chunk c / 4, slots 2 (c % 4) .. + 1)
+        const float p0 = fast_exp2(fmaf(cur[2 * c], sl2, neg_mu));
+        const float p1 = fast_exp2(fmaf(cur[2 * c + 1], sl2, neg_mu));
         uint32_t pk = pack_bf2(p0, p1);
         asm volatile("" : "+v"(pk));  // computed here, in this group (not sunk to its first use)
-        pf[qt][j] = pk;
-        if (g + 3 < 8) kf[g % 3] = kread(kb, g + 3);
+        pf[c >> 2][c & 3] = pk;
+        l_acc = add_bf2(pk, l_acc);
+        if (c + 3 < NKC) kf[c % 3] = kread(kb, c + 3);
         sched_fence();
       }
       const bool has_next = (h == 0) || (n + 1 < nb);
       if (has_next) mask(nxt, h == 0 ? n : n + 1, 1 - h);
-      u32x4_t vf[3] = {vread(vb, 0), vread(vb, 1), vread(vb, 2)};
-      float pa[QT], pb[QT], mx[QT];
+      u32x4_t vf[3] = {vread(vb, 0, 0), vread(vb, 0, 1), vread(vb, 0, 2)};
+      float ma, mb;
       sched_fence();
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16(vf[dt % 3], pf[qt], o[dt][qt]);
-        if (dt + 3 < NDT) vf[dt % 3] = vread(vb, dt + 3);
-        // the next half's per-lane maxima, a piece per group (pinned there: not sunk to the use)
-        if (dt == 0 || dt == 3) {
-          const int qt = dt / 3;
-          pa[qt] = fmaxf(fmaxf(nxt[0][qt][0], nxt[0][qt][1]), nxt[0][qt][2]);
-          asm volatile("" : "+v"(pa[qt]));
-        }
-        if (dt == 1 || dt == 4) {
-          const int qt = dt / 3;
-          pb[qt] = fmaxf(fmaxf(nxt[0][qt][3], nxt[1][qt][0]), nxt[1][qt][1]);
-          asm volatile("" : "+v"(pb[qt]));
-        }
-        if (dt == 2 || dt == 5) {
-          const int qt = dt / 3;
-          mx[qt] = fmaxf(fmaxf(pa[qt], pb[qt]), fmaxf(nxt[1][qt][2], nxt[1][qt][3]));
-          asm volatile("" : "+v"(mx[qt]));
-        }
+      for (int q = 0; q < 2 * NDT; ++q) {
+        o[q % NDT] = mfma32(vf[q % 3], pf[q / NDT], o[q % NDT]);
+        if (q + 3 < 2 * NDT) vf[q % 3] = vread(vb, (q + 3) / NDT, (q + 3) % NDT);
+        // the next half's per-lane maximum, a piece per group (pinned there: not sunk to the use)
+        // (scores 0-2, 3-5, then two more per group up to 14, 15 in group 6)
+        if (q == 0) ma = fmaxf(fmaxf(nxt[0], nxt[1]), nxt[2]);
+        if (q == 1) mb = fmaxf(fmaxf(nxt[3], nxt[4]), nxt[5]);
+        if (q >= 2 && q <= 6 && q % 2 == 0) ma = fmaxf(fmaxf(ma, nxt[2 * q + 2]), nxt[2 * q + 3]);
+        if (q >= 2 && q <= 6 && q % 2 == 1) mb = fmaxf(fmaxf(mb, nxt[2 * q + 2]), nxt[2 * q + 3]);
+        if (q <= 6 && q % 2 == 0) asm volatile("" : "+v"(ma));
+        if (q <= 6 && q % 2 == 1) asm volatile("" : "+v"(mb));
         sched_fence();
       }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) l_acc[qt] = mfma16(ones, pf[qt], l_acc[qt]);
-      if (has_next) rebase(mx);
+      if (has_next) rebase(fmaxf(ma, mb));
     }
   };
 
@@ -685,14 +684,14 @@ void attention_pipe_kernel(AttnArgs a) {
     issue(Stage<2>{}, 2);
     wait_vm_lgkm0<2 * LPW>();
     __builtin_amdgcn_s_barrier();
-    floatx4_t sa[2][QT], sb[2][QT];
+    floatx16_t sa, sb;
     if (active) {
-      qk(sa, Stage<0>{}, 0);
-      mask(sa, 0, 0);
-      float mx[QT];
+      const uint16_t* kb = stage(Stage<0>{});
+      sa = floatx16_t{};
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) mx[qt] = lane_max(sa, qt);
-      rebase(mx);
+      for (int c = 0; c < NKC; ++c) sa = mfma32(kread(kb, c), qf[c], sa);
+      mask(sa, 0, 0);
+      rebase(lane_max(sa));
     }
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
@@ -717,25 +716,26 @@ void attention_pipe_kernel(AttnArgs a) {
   // writes its 32 rows of O / l as bf16 into [row][D + 8] rows of the ring, then stores whole
   // 256-byte rows as 16-byte pieces (16 lanes per row), to the output when the request has one
   // split, else to the split's partial slot; the split's exponent reference and row sum go
-  // next to it.  (Per-lane 8-byte stores would cover 32 bytes of 16 rows each.)
+  // next to it.
+  const float l_run = pair_sum(l_acc);  // every lane: the whole row sum of its query
   __syncthreads();
   if (!active) return;
   constexpr int OP = D + 8;  // staged row pitch (elements): 272 bytes
   uint16_t* ob = (wave < 3 ? st0 : wave < 6 ? st1 : st2) + (wave % 3) * 32 * OP;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float l_run = l_acc[qt][0];
+  {
     const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const floatx4_t v = o[dt][qt];
-      *reinterpret_cast<u32x2_t*>(ob + (qt * 16 + l16) * OP + dt * 16 + 4 * j4) =
-          u32x2_t{pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv)};
-    }
-    const int qr = row0 + qt * 16 + l16;
-    if (n_split_b > 1 && j4 == 0 && qr < rows) {
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const floatx16_t& v = o[dt];
+        *reinterpret_cast<u32x2_t*>(ob + l32 * OP + 32 * dt + 8 * i4 + 4 * hh) =
+            u32x2_t{pack_bf2(v[4 * i4] * inv, v[4 * i4 + 1] * inv), pack_bf2(v[4 * i4 + 2] * inv, v[4 * i4 + 3] * inv)};
+      }
+    const int qr = row0 + l32;
+    if (n_split_b > 1 && hh == 0 && qr < rows) {
       const long slot = ((qrow_base + qr) * a.Hq + hq) * a.n_split + by;
-      a.part_ml[slot * 2] = m_ref[qt];
+      a.part_ml[slot * 2] = m_ref;
       a.part_ml[slot * 2 + 1] = l_run;
     }
   }
