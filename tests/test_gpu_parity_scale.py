@@ -276,6 +276,34 @@ def test_causal_prefill_chunk_over_a_long_cache():
         m.close()
 
 
+def test_short_causal_chunk_over_a_long_cache():
+    """A 70-row causal prefill chunk over 8200 cached positions at head dim 128: the long-range
+    kernel, causal, with 3 row blocks of 32 (the last one 6 rows) per head, so two of the eight
+    waves hold no query task, and the causal mask cuts the last key half block of every wave.
+    Two layers with every expert active; the chunk's K/V of both layers against the oracle."""
+    dg = need_gpu()
+    shape = dataclasses.replace(synth.MID_LAYER, n_layers=2, n_experts=4, top_k=4, vocab=1024)
+    w = synth.model_weights(shape, SEED + 13)
+    L0, n = 8200, 70
+    m = dg.Model(shape, w, max_batch=1, max_prefill_rows=256)
+    try:
+        k, v = random_cache(shape, L0, L0 + n + 256, SEED + 14)
+        kv = dg.KV(shape, 1, L0 + n + 256, fill=None)
+        load_cache(kv, k, v, [L0])
+        toks = synth.tokens(n, shape.vocab, SEED, 502)
+        m.prefill(torch.from_numpy(toks).cuda(), [n], kv)
+        torch.cuda.synchronize()
+        assert kv.lengths == [L0 + n]
+        ck = [k[l, 0].astype(np.float64) for l in range(shape.n_layers)]
+        cv = [v[l, 0].astype(np.float64) for l in range(shape.n_layers)]
+        omodel.prefill(w, shape, toks, ck, cv, L0)
+        for l in range(shape.n_layers):
+            close(bf16_to_np(kv.k[l, 0, :, L0:L0 + n]), ck[l][:, L0:L0 + n], what=f"chunk K layer {l}", bf16_out=True)
+            close(bf16_to_np(kv.v[l, 0, :, L0:L0 + n]), cv[l][:, L0:L0 + n], what=f"chunk V layer {l}", bf16_out=True)
+    finally:
+        m.close()
+
+
 def test_prefill_2048_rows_on_the_large_tile_gemms():
     """A 2048-row causal prefill at width 2048 with the shared FFN 4096: the QKV projection (RoPE
     epilogue), the split O-projection, the shared gate/up pair and the split shared down
