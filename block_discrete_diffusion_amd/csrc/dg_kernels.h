@@ -141,8 +141,8 @@ struct AttnArgs {
   int32_t n_pairs;
   uint16_t pair[kMaxPairs];
 };
-// True when launch_attention runs the pipelined canvas kernel for these arguments (head dim
-// 128, 8 waves, two query tiles per wave, no causal mask); it takes per-request splits.
+// True when launch_attention runs the pipelined kernel for these arguments (head dim 128, 8
+// waves, 32-row query tasks, with or without the causal mask); it takes per-request splits.
 bool attention_pipe_path(const AttnArgs& a);
 // Work-group shape for a key range of max_keys.  Waves: 8 from 2048 keys on the canvas path
 // and from 8192 in the causal prefill (each staged block serves more queries), else 4.  Query tiles per wave: 2 (32 rows) for long ranges and the
