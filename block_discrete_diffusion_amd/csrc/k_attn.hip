@@ -769,30 +769,31 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
                                                            const float* __restrict__ part_ml,
                                                            uint16_t* __restrict__ out, int n_rh,
                                                            int stride, SplitCounts sc) {
-  constexpr int TPR = D / 4;  // threads per (row, head): 4 dims each
-  constexpr int MS = 16;      // most splits a launch uses
+  constexpr int DPT = NORM16 ? 8 : 4;  // dims per thread: one 16-byte load per split
+  constexpr int TPR = D / DPT;         // threads per (row, head)
+  constexpr int MS = 16;               // most splits a launch uses
   const int rh = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (rh >= n_rh) return;
   const int n_split = sc.balanced ? sc.n[rh / sc.Hq / sc.rows_per_req] : stride;
   if (n_split <= 1) return;
-  const int d0 = (threadIdx.x % TPR) * 4;
+  const int d0 = (threadIdx.x % TPR) * DPT;
   const long base = static_cast<long>(rh) * stride;
   const uint16_t* part16 = reinterpret_cast<const uint16_t*>(part_o);
   float2 ml[MS];
   floatx4_t po[MS];
-  u32x2_t ph[MS];
+  u32x4_t ph[MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s)
     if (s < n_split) {
       ml[s] = *reinterpret_cast<const float2*>(part_ml + (base + s) * 2);
-      if constexpr (NORM16) ph[s] = *reinterpret_cast<const u32x2_t*>(part16 + (base + s) * D + d0);
+      if constexpr (NORM16) ph[s] = ld16(part16 + (base + s) * D + d0);
       else po[s] = *reinterpret_cast<const floatx4_t*>(part_o + (base + s) * D + d0);
     }
   float m = -INFINITY;
 #pragma unroll
   for (int s = 0; s < MS; ++s)
     if (s < n_split) m = fmaxf(m, ml[s].x);
-  floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f}, acc1 = acc;  // dims d0 .. + 3, d0 + 4 .. + 7
   float l = 0.f;
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
@@ -801,17 +802,24 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     if constexpr (NORM16) {
       const float wl = w * ml[s].y;
       l += wl;
-      const u32x2_t p = ph[s];
+      const u32x4_t p = ph[s];
       acc += wl * floatx4_t{__uint_as_float(p[0] << 16), __uint_as_float(p[0] & 0xffff0000u),
                             __uint_as_float(p[1] << 16), __uint_as_float(p[1] & 0xffff0000u)};
+      acc1 += wl * floatx4_t{__uint_as_float(p[2] << 16), __uint_as_float(p[2] & 0xffff0000u),
+                             __uint_as_float(p[3] << 16), __uint_as_float(p[3] & 0xffff0000u)};
     } else {
       l += w * ml[s].y;
       acc += w * po[s];
     }
   }
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
-  *reinterpret_cast<u32x2_t*>(out + static_cast<long>(rh) * D + d0) =
-      u32x2_t{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
+  if constexpr (NORM16)
+    st16(out + static_cast<long>(rh) * D + d0,
+         u32x4_t{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv),
+                 pack_bf2(acc1[0] * inv, acc1[1] * inv), pack_bf2(acc1[2] * inv, acc1[3] * inv)});
+  else
+    *reinterpret_cast<u32x2_t*>(out + static_cast<long>(rh) * D + d0) =
+        u32x2_t{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
 }
 
 template <int D, int NW>
@@ -840,7 +848,7 @@ void launch_attn_d(const AttnArgs& a, hipStream_t s) {
 template <int D>
 void launch_combine_d(const AttnArgs& a, hipStream_t s) {
   const int n_rh = a.n_req * a.rows_per_req * a.Hq;
-  const int per = 256 / (D / 4);
+  const int per = 256 / (D / (a.balanced ? 8 : 4));  // (row, head) pairs per work-group
   SplitCounts sc{};
   sc.balanced = a.balanced;
   sc.Hq = a.Hq;
