@@ -359,8 +359,11 @@ __global__ __launch_bounds__(256) void router_pack_kernel(const uint16_t* __rest
 }
 
 // The same step (residual update, FFN norm, router, top-k, gates) with the router logits on
-// MFMA, for d = 32 NW SPW, one work-group of NW waves per 16 rows.  Lane (l16, j4) of wave w
-// owns row l16 of the group and, in each of its SPW 32-column k-steps s, the columns
+// MFMA, for d = 32 NW SPW, one work-group of NW waves per RW = 16 or 8 rows (8 where 16-row groups
+// would leave CUs idle: every group reads the whole router matrix, so the CUs' load rate, not
+// HBM, sets the pace).  The MFMA tiles stay 16 rows wide; with RW = 8, lanes l16 >= 8 repeat
+// the rows of lanes l16 - 8 (the same addresses: no extra traffic) and store nothing.  Lane
+// (l16, j4) of wave w takes row l16 % RW of the group and, in each of its SPW 32-column k-steps s, the columns
 // 32 (w SPW + s) + 8 j4 .. + 8: exactly the MFMA B-operand fragment of those rows, so the normed
 // row never goes through LDS.  The normed float32 x is split into bf16 hi = bf16(x) (the copy
 // the experts read) and lo = bf16(x - hi), and each 16 x 16 logit tile is W hi + W lo with
@@ -383,23 +386,24 @@ DG_DEVICE float wave_tree_sum(const float* v, int stride) {  // v[i * stride], i
   else return wave_tree_sum<NW / 2>(v, stride) + wave_tree_sum<NW / 2>(v + (NW / 2) * stride, stride);
 }
 
-template <int NW, int SPW, int WH>  // WH: the weights come in WH parts (2: the second after the rows)
+template <int NW, int SPW, int WH, int RW>  // WH: the weights come in WH parts (2: the second after the rows)
 __global__ __launch_bounds__(64 * NW) void norm_router_mfma_kernel(
     float* __restrict__ h, const float* __restrict__ part, int n_part, long part_stride,
     const float* __restrict__ gain, float eps, const uint16_t* __restrict__ wp, int d, int n_exp,
     int top_k, int rows, uint16_t* __restrict__ bout, int32_t* __restrict__ idx,
     float* __restrict__ gates) {
-  constexpr int R = 16, NT = 4;  // rows per work-group, 16-expert tiles
+  constexpr int R = 16, NT = 4;  // rows of an MFMA tile, 16-expert tiles
   static_assert(R % NW == 0 || NW % R == 0, "rows split over the waves");
+  static_assert(RW == 16 || RW == 8, "rows per work-group");
   __shared__ float red[NW][R];
   __shared__ float plg[NW][NT * 16][R + 1];
   __shared__ __align__(16) float lg[R][64];
   __shared__ __align__(16) float gs[NW * SPW * 32];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, j4 = lane >> 4;
-  const int r0 = blockIdx.x * R;
-  const bool own = r0 + l16 < rows;
-  const long row = min(r0 + l16, rows - 1);  // rows past the end re-read the last one
+  const int r0 = blockIdx.x * RW;
+  const bool own = l16 < RW && r0 + l16 < rows;
+  const long row = min(r0 + l16 % RW, rows - 1);  // rows past the end re-read the last one
   const int kc0 = w * SPW * 32 + 8 * j4;     // this lane's first column; k-step s adds 32 s
 
   constexpr int SH = SPW / WH;  // k-steps per part of the weights
@@ -509,7 +513,7 @@ __global__ __launch_bounds__(64 * NW) void norm_router_mfma_kernel(
 #pragma unroll
   for (int k = 0; k < RPW; ++k) {
     const int rr = w + NW * k;
-    if (rr >= R || r0 + rr >= rows) break;  // uniform
+    if (rr >= RW || r0 + rr >= rows) break;  // uniform
     const float mine = lg[rr][lane];
     float top = -INFINITY;
     int rank = 0;
@@ -570,10 +574,14 @@ void launch_norm_router(float* h, const float* part, int n_part, long part_strid
                         const float* gain, float eps, const uint16_t* w_router,
                         const uint16_t* w_router_packed, int rows, int d, int n_exp, int top_k,
                         uint16_t* b_out, int32_t* idx, float* gates, hipStream_t s) {
-#define DG_NRM(NW, SPW, WH)                                                                         \
-  hipLaunchKernelGGL((norm_router_mfma_kernel<NW, SPW, WH>), dim3((rows + 15) / 16), dim3(64 * NW), 0, s, h, \
-                     part, n_part, part_stride, gain, eps, w_router_packed, d, n_exp, top_k, rows, b_out,  \
-                     idx, gates)
+#define DG_NRM_R(NW, SPW, WH, RW)                                                                   \
+  hipLaunchKernelGGL((norm_router_mfma_kernel<NW, SPW, WH, RW>), dim3((rows + RW - 1) / RW), dim3(64 * NW), 0, \
+                     s, h, part, n_part, part_stride, gain, eps, w_router_packed, d, n_exp, top_k, rows,    \
+                     b_out, idx, gates)
+  // 8 rows per work-group while 16-row groups would not give every CU one
+#define DG_NRM(NW, SPW, WH)                                  \
+  if ((rows + 15) / 16 < 256) DG_NRM_R(NW, SPW, WH, 8);      \
+  else DG_NRM_R(NW, SPW, WH, 16)
   // the MFMA router from 1024 rows (64 work-groups and more); below that a work-group per row
   if (w_router_packed && rows >= 1024 && router_mfma_path(d, n_exp)) {
     switch (d / 256) {  // 16 waves at 512 and 1024 columns, else 8 (registers)
@@ -585,6 +593,7 @@ void launch_norm_router(float* h, const float* part, int n_part, long part_strid
     }
   }
 #undef DG_NRM
+#undef DG_NRM_R
   const int nch = (d + 2047) / 2048;
   // several rows per work-group once there are enough rows to fill the chip: the router
   // weights are then read once per group instead of once per row
