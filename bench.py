@@ -92,9 +92,9 @@ PMC_TRAFFIC = {
     },
     "attention": {
         "kernel": "attention_pipe_kernel<8>", "workload": "batch8_ragged_32k",
-        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "c27b1b937c56be40",
-        "fetch_kib": 571364.5, "fetch_scale": 1048576.0 / 524315.2,
-        "write_kib": 33837.5, "write_scale": 1048576.0 / 1048576.0,
+        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "70e51fb387a5ecc6",
+        "fetch_kib": 571364.8, "fetch_scale": 1048576.0 / 524315.2,
+        "write_kib": 33836.3, "write_scale": 1048576.0 / 1048576.0,
     },
 }
 
