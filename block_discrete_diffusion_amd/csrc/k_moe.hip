@@ -418,8 +418,10 @@ DG_DEVICE floatx4_t bf4(const u32x2_t& p) {
 // with a gain it also writes the next block's normed input out = bf16(rmsnorm(h[t]) * gain),
 // which saves a pass over h.  All of a thread's loads (the gain too) are issued before any
 // arithmetic, and with a gain h is stored after the norm's barrier: a barrier after a global
-// store waits for that store.
-template <int NCH>  // 4-element chunks per thread: ceil(d / 2048)
+// store waits for that store.  KJ routed slots (>= top_k up to 8) and NP slices (>= n_part) are
+// loaded; the launch picks the smallest that hold the call's, so no load is made only to be
+// dropped.
+template <int NCH, int KJ, int NP>  // NCH: 4-element chunks per thread, ceil(d / 2048)
 __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
                                                           const float* __restrict__ part,
                                                           int n_part, long part_stride,
@@ -431,7 +433,8 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
   __shared__ float red[8];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float* hr = h + static_cast<long>(t) * d;
-  constexpr int KJ = 8;  // routed slots held in registers; more are read in the second loop
+  static_assert(KJ == 4 || KJ == 8, "routed slots held in registers; more are read in the second loop");
+  static_assert(NP >= 0 && NP <= kMaxParts, "split slices");
   // every load is unconditional (slots past top_k and slices past n_part re-read the last
   // valid one and are not added): loads under a condition would each get a wait of their own
   const int kl = min(top_k, KJ) - 1;
@@ -442,12 +445,13 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
     pj[j] = inv[static_cast<long>(t) * top_k + min(j, kl)];
     gj[j] = gates[static_cast<long>(t) * top_k + min(j, kl)];
   }
-  const float* zp[kMaxParts];
+  constexpr int NPA = NP > 0 ? NP : 1;
+  const float* zp[NPA];
 #pragma unroll
-  for (int z = 0; z < kMaxParts; ++z)
+  for (int z = 0; z < NPA; ++z)
     zp[z] = n_part > 0 ? part + min(z, n_part - 1) * part_stride + static_cast<long>(t) * d : hr;
   const float* gsrc = gain ? gain : hr;
-  floatx4_t v[NCH], pz[kMaxParts][NCH], gv[NCH];
+  floatx4_t v[NCH], pz[NPA][NCH], gv[NCH];
   u32x2_t yj[KJ][NCH];  // four bf16 expert outputs each
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
     v[i] = *reinterpret_cast<const floatx4_t*>(hr + c);
     gv[i] = *reinterpret_cast<const floatx4_t*>(gsrc + c);
 #pragma unroll
-    for (int z = 0; z < kMaxParts; ++z) pz[z][i] = *reinterpret_cast<const floatx4_t*>(zp[z] + c);
+    for (int z = 0; z < NP; ++z) pz[z][i] = *reinterpret_cast<const floatx4_t*>(zp[z] + c);
 #pragma unroll
     for (int j = 0; j < KJ; ++j) yj[j][i] = *reinterpret_cast<const u32x2_t*>(y + static_cast<long>(pj[j]) * d + c);
   }
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(512) void moe_combine_kernel(float* __restrict__ h,
     const int c = (tid + 512 * i) * 4;
     floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int z = 0; z < kMaxParts; ++z)
+    for (int z = 0; z < NP; ++z)
       if (z < n_part) acc += pz[z][i];
 #pragma unroll
     for (int j = 0; j < KJ; ++j)
@@ -578,12 +582,21 @@ void launch_moe_combine(float* h, const float* part, int n_part, long part_strid
                         const int32_t* inv, const float* gates, int rows, int d, int top_k,
                         const float* gain, float eps, uint16_t* out, hipStream_t s) {
   const int nch = (d + 2047) / 2048;
-#define DG_MC(N)                                                                              \
-  hipLaunchKernelGGL(moe_combine_kernel<N>, dim3(rows), dim3(512), 0, s, h, part, n_part,         \
+#define DG_MC(N, KJ, NP)                                                                          \
+  hipLaunchKernelGGL((moe_combine_kernel<N, KJ, NP>), dim3(rows), dim3(512), 0, s, h, part, n_part,  \
                      part_stride, y, inv, gates, d, top_k, gain, eps, out)
-  if (nch <= 1) DG_MC(1);
-  else if (nch <= 2) DG_MC(2);
-  else DG_MC(4);
+#define DG_MC_P(N, KJ)                    \
+  if (n_part <= 0) DG_MC(N, KJ, 0);       \
+  else if (n_part <= 2) DG_MC(N, KJ, 2);  \
+  else DG_MC(N, KJ, 4)
+#define DG_MC_K(N)                  \
+  if (top_k <= 4) { DG_MC_P(N, 4); } \
+  else { DG_MC_P(N, 8); }
+  if (nch <= 1) { DG_MC_K(1); }
+  else if (nch <= 2) { DG_MC_K(2); }
+  else { DG_MC_K(4); }
+#undef DG_MC_K
+#undef DG_MC_P
 #undef DG_MC
 }
 
