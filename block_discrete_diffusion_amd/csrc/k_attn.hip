@@ -335,8 +335,8 @@ void attention_kernel(AttnArgs a) {
 // 32-row query tile each, on the 32 x 32 x 16 matrix instruction:
 //  * one 32 x 32 MFMA does the work of two 16 x 16 x 32 ones but holds the SIMD's issue for
 //    about as long as one of them (measured on gfx950: each MFMA blocks vector issue for ~11
-//    cycles, whatever its size), so the softmax's vector work (an FMA, an exponential and half a
-//    pack per score) fits beside the matrix work instead of queueing behind it;
+//    cycles, whatever its size), which leaves more issue cycles to the softmax's vector work
+//    (an FMA, an exponential and half a pack per score): 16 MFMAs per 32-key half instead of 34;
 //  * software pipeline: while the softmax of half block n runs (scale, exp, pack to bf16, row
 //    sum), the QK^T products of the next half are already issued; while P V of half n runs, the
 //    maximum of the next half is taken.  Two score tiles alternate;
