@@ -86,15 +86,15 @@ def causal_attention_flops(shape, n: int, chunk: int) -> float:
 PMC_TRAFFIC = {
     "moe_gemm1_swiglu": {
         "kernel": "expert_stream_kernel<true, 3, 1, 1, false, true, 1>", "workload": "full_canvas_loop",
-        "source": "block_discrete_diffusion_amd/csrc/k_moe.hip", "sha": "a1f02f99820d951d",
-        "fetch_kib": 202175.9, "fetch_scale": 1048576.0 / 524315.2,  # copy of 1 GiB reads 524315 KiB
+        "source": "block_discrete_diffusion_amd/csrc/k_moe.hip", "sha": "929cf7488c01e500",
+        "fetch_kib": 202120.2, "fetch_scale": 1048576.0 / 524315.2,  # copy of 1 GiB reads 524315 KiB
         "write_kib": 1487.8, "write_scale": 1048576.0 / 1048576.0,   # and writes 1048576 KiB
     },
     "attention": {
         "kernel": "attention_pipe_kernel<8>", "workload": "batch8_ragged_32k",
-        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "70e51fb387a5ecc6",
-        "fetch_kib": 571364.8, "fetch_scale": 1048576.0 / 524315.2,
-        "write_kib": 33836.3, "write_scale": 1048576.0 / 1048576.0,
+        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "8ba4e9606d5362de",
+        "fetch_kib": 571376.1, "fetch_scale": 1048576.0 / 524315.2,
+        "write_kib": 33836.6, "write_scale": 1048576.0 / 1048576.0,
     },
 }
 
