@@ -336,9 +336,13 @@ void attention_kernel(AttnArgs a) {
 //  * one 32 x 32 MFMA does the work of two 16 x 16 x 32 ones but holds the SIMD's issue for
 //    about as long as one of them (measured on gfx950: each MFMA blocks vector issue for ~11
 //    cycles, whatever its size), which leaves more issue cycles to the softmax's vector work
-//    (an FMA, an exponential and half a pack per score): 16 MFMAs per 32-key half instead of 34;
-//  * software pipeline: while the softmax of half block n runs (scale, exp, pack to bf16, row
-//    sum), the QK^T products of the next half are already issued; while P V of half n runs, the
+//    (an exponential and half a pack per score): 17 MFMAs per 32-key half instead of 34;
+//  * the scores leave the MFMAs ready for the exponential: the queries are multiplied by
+//    scale * log2 e once (and rounded to bf16 again), and each QK^T chain starts with one more
+//    MFMA that adds the query's exponent offset -m_ref (a ones column of K times an offset row of
+//    Q^T), which replaces an FMA per score with one MFMA per 1024 scores;
+//  * software pipeline: while the softmax of half block n runs (exp, pack to bf16, row sum),
+//    the QK^T products of the next half are already issued; while P V of half n runs, the
 //    maximum of the next half is taken.  Two score tiles alternate;
 //  * K and V blocks go from global memory straight into LDS (global_load_lds_dwordx4) through
 //    a ring of PS stages, three blocks ahead, one barrier per block; no staging registers.  A
@@ -533,6 +537,15 @@ void attention_pipe_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < NKC; ++c) qf[c] = ok ? ld16(qp + 16 * c + 8 * hh) : u32x4_t{0u, 0u, 0u, 0u};
   }
+  // scores in log2 units: Q <- bf16(Q * scale * log2 e)
+  const float sl2 = a.scale * 1.4426950408889634f;
+#pragma unroll
+  for (int c = 0; c < NKC; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = qf[c][w];
+      qf[c][w] = pack_bf2(__uint_as_float(x << 16) * sl2, __uint_as_float(x & 0xffff0000u) * sl2);
+    }
   // the queries have landed before the first stage load is issued: the compiler does not see
   // those loads, so a wait it placed for a query register inside the loop would also wait for
   // the stage loads issued after it
@@ -542,14 +555,17 @@ void attention_pipe_kernel(AttnArgs a) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  // per query (each lane pair l, l ^ 32 holds the same values): exponent reference (log2
-  // units, scale folded in) of O and the row sum; the offset -m_ref (0 while no key has been
-  // seen); the raw score (m_ref + kLazy) / (scale log2 e) above which the reference has to move
-  // (the scale is positive).  All three change only where the reference does.  The row sum is
-  // this lane's keys only; the two halves are added at the end.
+  // per query (each lane pair l, l ^ 32 holds the same values): exponent reference m_ref (log2
+  // units, a bf16 value) of O and the row sum; the offset -m_ref (0 while no key has been seen)
+  // that the scores come out with; the offset score above which the reference has to move
+  // (kLazy, or -inf while no key has been seen).  All three change only where the reference
+  // does.  The row sum is this lane's keys only; the two halves are added at the end.
   float m_ref = -INFINITY, neg_mu = 0.f, thr = -INFINITY, l_acc = 0.f;
-  const float sl2 = a.scale * 1.4426950408889634f;
-  const float inv_sl2 = 1.f / sl2;
+  // the offset MFMA's operands: A = a ones column (dim 0 of every key), B = the offset row
+  // (dim 0 of every query: bf16(-m_ref), exact since m_ref is a bf16 value); lanes of half 1
+  // hold dims 8..15, all zero
+  const u32x4_t ones = {hh == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};
+  u32x4_t qb = {0u, 0u, 0u, 0u};
 
   // K fragment c of a half (A operand: key row l32, dims 16 c + 8 hh .. + 8, i.e. 16-byte chunk
   // 2 c + hh): element offsets inside the half, one register each (the swizzle is per row; the
@@ -590,29 +606,35 @@ void attention_pipe_kernel(AttnArgs a) {
     }
   };
   // A half's maximum per query moves the reference (and rescales O and its sum) only when it
-  // exceeds the reference by more than kLazy.  The check takes each lane's own raw maximum (no
-  // query's maximum can pass the threshold unless one of its lanes' does); only then are the
-  // two lanes of each query combined and the references that must move moved.  (Scaling by a
-  // positive constant and rounding are monotonic: the maximum of the scaled scores is the
-  // scaled maximum.)
+  // exceeds the reference by more than kLazy.  The check takes each lane's own maximum of the
+  // offset scores (no query's maximum can pass the threshold unless one of its lanes' does);
+  // only then are the two lanes of each query combined and the references that must move
+  // moved: to the half's maximum rounded to bf16 (P then stays below about 2^kLazy), with the
+  // already computed scores of that half shifted to the new offset.
   auto lane_max = [&](const floatx16_t& sc) {
     float m = sc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) m = fmaxf(m, sc[i]);
     return m;
   };
-  auto rebase = [&](float mx) {
+  auto rebase = [&](float mx, floatx16_t& sc) {
     if (__any(mx > thr)) {  // uniform: every lane takes part in the cross-lane maximum
-      const float ms = pair_max(mx) * sl2;
+      const float ms = pair_max(mx) - neg_mu;
       const bool up = ms > m_ref + kLazy;
-      const float m_new = up ? ms : m_ref;
+      const uint32_t mb = pack_bf2(ms, 0.f) & 0xffffu;
+      const float m_new = up ? __uint_as_float(mb << 16) : m_ref;
       const float alpha = up ? fast_exp2(m_ref - m_new) : 1.f;  // 0 from -inf
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
       l_acc *= alpha;
       m_ref = m_new;
-      neg_mu = (m_new == -INFINITY) ? 0.f : -m_new;
-      thr = (m_new + kLazy) * inv_sl2;
+      const float nm = (m_new == -INFINITY) ? 0.f : -m_new;
+      const float shift = nm - neg_mu;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] += shift;
+      neg_mu = nm;
+      qb[0] = hh == 0 ? (pack_bf2(nm, 0.f) & 0xffffu) : 0u;
+      thr = (m_new == -INFINITY) ? -INFINITY : kLazy;
     }
   };
   // One pipeline step on half H of block n (n % PS == R): its scores are in cur; the next half
@@ -620,7 +642,8 @@ void attention_pipe_kernel(AttnArgs a) {
   // written as groups with scheduling fences between them, so that every LDS fragment is
   // requested three groups before the MFMA that uses it and the current half's softmax sits
   // between the next half's QK^T products:
-  //   QK group c (8):  the MFMA of K chunk c; scale, exp, pack and row sum of two P values;
+  //   QK group c (8):  the MFMA of K chunk c (after the offset MFMA in group 0); exp, pack and
+  //                    row sum of two P values;
   //                    request of K chunk c + 3
   //   PV group q (8):  the MFMA of key chunk q / 4 and O tile q % 4; request of V^T fragment
   //                    q + 3; a piece of the next half's per-lane maximum (the vector unit is
@@ -641,10 +664,11 @@ void attention_pipe_kernel(AttnArgs a) {
       sched_fence();
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
-        nxt = mfma32(kf[c % 3], qf[c], c == 0 ? floatx16_t{} : nxt);
+        if (c == 0) nxt = mfma32(ones, qb, floatx16_t{});
+        nxt = mfma32(kf[c % 3], qf[c], nxt);
         // P slots 2 c, 2 c + 1 (of the 16 = P chunk c / 4, slots 2 (c % 4) .. + 1)
-        const float p0 = fast_exp2(fmaf(cur[2 * c], sl2, neg_mu));
-        const float p1 = fast_exp2(fmaf(cur[2 * c + 1], sl2, neg_mu));
+        const float p0 = fast_exp2(cur[2 * c]);
+        const float p1 = fast_exp2(cur[2 * c + 1]);
         uint32_t pk = pack_bf2(p0, p1);
         asm volatile("" : "+v"(pk));  // computed here, in this group (not sunk to its first use)
         pf[c >> 2][c & 3] = pk;
@@ -671,7 +695,7 @@ void attention_pipe_kernel(AttnArgs a) {
         if (q <= 6 && q % 2 == 1) asm volatile("" : "+v"(mb));
         sched_fence();
       }
-      if (has_next) rebase(fmaxf(ma, mb));
+      if (has_next) rebase(fmaxf(ma, mb), nxt);
     }
   };
 
@@ -691,7 +715,7 @@ void attention_pipe_kernel(AttnArgs a) {
 #pragma unroll
       for (int c = 0; c < NKC; ++c) sa = mfma32(kread(kb, c), qf[c], sa);
       mask(sa, 0, 0);
-      rebase(lane_max(sa));
+      rebase(lane_max(sa), sa);
     }
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
