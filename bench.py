@@ -92,9 +92,9 @@ PMC_TRAFFIC = {
     },
     "attention": {
         "kernel": "attention_pipe_kernel<8>", "workload": "batch8_ragged_32k",
-        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "763c0b91f2f6a2fe",
-        "fetch_kib": 571275.1, "fetch_scale": 1048576.0 / 524315.2,
-        "write_kib": 33844.1, "write_scale": 1048576.0 / 1048576.0,
+        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "e18dfdd9162edf2e",
+        "fetch_kib": 571288.7, "fetch_scale": 1048576.0 / 524315.2,
+        "write_kib": 33826.4, "write_scale": 1048576.0 / 1048576.0,
     },
 }
 

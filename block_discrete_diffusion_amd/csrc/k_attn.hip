@@ -344,6 +344,10 @@ void attention_kernel(AttnArgs a) {
 //  * software pipeline: while the softmax of half block n runs (exp, pack to bf16, row sum),
 //    the QK^T products of the next half are already issued; while P V of half n runs, the
 //    maximum of the next half is taken.  Two score tiles alternate;
+//  * a wave raises its issue priority for its P V groups: of the two waves of a SIMD, the one
+//    with only matrix work queued then keeps the MFMA unit fed, while the other's softmax takes
+//    the vector issue slots in between (measured 2.9 % faster than equal priorities, 1.7 % faster
+//    than raising it for the softmax groups instead);
 //  * K and V blocks go from global memory straight into LDS (global_load_lds_dwordx4) through
 //    a ring of PS stages, three blocks ahead, one barrier per block; no staging registers.  A
 //    1 KB load is four whole 256-byte key rows, so every instruction reads 1 KB of contiguous
@@ -681,6 +685,8 @@ void attention_pipe_kernel(AttnArgs a) {
       u32x4_t vf[3] = {vread(vb, 0, 0), vread(vb, 0, 1), vread(vb, 0, 2)};
       float ma, mb;
       sched_fence();
+      __builtin_amdgcn_s_setprio(1);  // P V groups: matrix work first (see above)
+      sched_fence();
 #pragma unroll
       for (int q = 0; q < 2 * NDT; ++q) {
         o[q % NDT] = mfma32(vf[q % 3], pf[q / NDT], o[q % NDT]);
@@ -695,6 +701,9 @@ void attention_pipe_kernel(AttnArgs a) {
         if (q <= 6 && q % 2 == 1) asm volatile("" : "+v"(mb));
         sched_fence();
       }
+      sched_fence();
+      __builtin_amdgcn_s_setprio(0);
+      sched_fence();
       if (has_next) rebase(fmaxf(ma, mb), nxt);
     }
   };

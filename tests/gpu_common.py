@@ -139,12 +139,13 @@ def check_ffn_teacher_forced(lw, shape, h_mid, gpu_idx, gpu_gates, gpu_out, tag=
     return clear
 
 
-def check_layer(dg, m, w, shape, Lp, seed, cap):
+def check_layer(dg, m, w, shape, Lp, seed, cap, cache=None):
     """One layer from a synthetic residual state: attention, canvas K/V and the residual after
     attention against the oracle layer on the same input; the FFN sub-block teacher-forced on the
-    GPU's residual after attention (every row outside the router's tie gap)."""
+    GPU's residual after attention (every row outside the router's tie gap).  cache: the prefix
+    (k, v) as numpy [n_layers, 1, Hkv, cap, D] bf16 values (default: random_cache)."""
     kv = dg.KV(shape, 1, cap)
-    k, v = random_cache(shape, Lp, cap, seed)
+    k, v = random_cache(shape, Lp, cap, seed) if cache is None else cache
     load_cache(kv, k, v, [Lp])
     h = synth.hidden(256, shape.d_model, seed, 5)
     dbg = layer_debug(dg, m, shape, 256, shape.n_layers)

@@ -45,6 +45,22 @@ def test_full_shape_layer_with_shared_ffn(full_env, prefix):
     check_layer(dg, m, host, FULL1, prefix, SEED + prefix, prefix + 256)
 
 
+def test_long_range_attention_moving_reference(full_env):
+    """Scores that climb inside every key range, so that the pipelined kernel's exponent
+    reference moves during a split: the 9000 cached keys are scaled by a sawtooth from 0.05 to 3
+    over each 1024 keys.  Each split then starts low and its running maximum passes the
+    reference by more than the lazy-rescale margin (8 in log2 units) about 1.5 times per query
+    (emulated on the host: maxima up to ~19 log2 units); every such move rescales O and the row
+    sum and shifts the already computed scores of the next half to the new offset.  All 256 rows
+    against the oracle, as the other full-shape layers."""
+    dg, w, m, host = full_env
+    Lp, seed = 9000, SEED + 9000
+    k, v = random_cache(FULL1, Lp, Lp + 256, seed)
+    ramp = 0.05 + 2.95 * ((np.arange(Lp) % 1024) / 1023.0)
+    k[:, :, :, :Lp] = synth.bf16_round(k[:, :, :, :Lp] * ramp[None, None, None, :, None].astype(np.float32))
+    check_layer(dg, m, host, FULL1, Lp, seed, Lp + 256, cache=(k, v))
+
+
 def test_full_shape_layer_without_shared_ffn(full_env):
     """The single-layer shape of the mid configuration: no shared FFN, prefix 4096."""
     dg, w, _, host = full_env
