@@ -624,11 +624,25 @@ def long_generation(args, dg, shape, w, cfg):
     t_wall = time.perf_counter() - t_wall
     total_ms = e0.elapsed_time(e1)
     n_steps = sum(steps)
+    final_len = kv.lengths[0]
+    extra = {}
+    if not args.no_kernel_timing:
+        # per-kernel timing of the last canvas again (outside the timed region): its cache is
+        # rolled back to the last block's prefix and the block re-run with the events on
+        L_last = L0 + (n_blocks - 1) * shape.canvas
+        kv.set_lengths([L_last])
+        m.timing(True)
+        one_block()
+        torch.cuda.synchronize()
+        kt = m.timing_read()
+        m.timing(False)
+        extra["attention_roofline"] = roofline_entry("mfma", "attention", kt, attention_flops(shape, [L_last]),
+                                                     "flops", "long_generation", {"prefix": L_last})
     out = base_line("canvas positions/s (block-autoregressive generation, 1 GPU)",
                     n_blocks * shape.canvas / (total_ms * 1e-3), "finalised canvas positions/s", n_steps, 1,
                     total_ms / n_steps, "bf16", "long_generation", 1, L0 + n_blocks * shape.canvas,
-                    steps_per_canvas=steps, canvas_ms=round(total_ms / n_blocks, 3), final_kv_len=kv.lengths[0],
-                    roofline=None, cpu_baseline=None, wall_s_timed=round(t_wall, 3))
+                    steps_per_canvas=steps, canvas_ms=round(total_ms / n_blocks, 3), final_kv_len=final_len,
+                    roofline=None, cpu_baseline=None, wall_s_timed=round(t_wall, 3), **extra)
     print(json.dumps(out), flush=True)
     m.close()
 
