@@ -638,11 +638,28 @@ def long_generation(args, dg, shape, w, cfg):
         m.timing(False)
         extra["attention_roofline"] = roofline_entry("mfma", "attention", kt, attention_flops(shape, [L_last]),
                                                      "flops", "long_generation", {"prefix": L_last})
+        roofline = roofline_entry("hbm", "moe_gemm1_swiglu", kt,
+                                  expert_gemm1_bytes(shape, shape.canvas * shape.top_k, shape.n_experts), "bytes",
+                                  "long_generation")
+    else:
+        roofline = None
+    cpu = None
+    if not args.no_cpu_baseline:
+        # one denoise step of the oracle over the last canvas's prefix (its GPU-filled bf16 K/V),
+        # as for the batched workload with one request, then per finalised position: a canvas
+        # took the mean steps per canvas of the GPU run
+        log("CPU oracle baseline (bounded sample)")
+        L_last = L0 + (n_blocks - 1) * shape.canvas
+        cpu = cpu_baseline_batch(shape, w, kv, [L_last], args.cpu_sample_rows)
+        spc = n_steps / n_blocks
+        cpu["value"] = round(cpu["value"] / spc, 4)
+        cpu["unit"] = "finalised canvas positions/s"
+        cpu["sample"] += f"; per finalised position: divided by the {spc:g} steps per canvas of the GPU run"
     out = base_line("canvas positions/s (block-autoregressive generation, 1 GPU)",
                     n_blocks * shape.canvas / (total_ms * 1e-3), "finalised canvas positions/s", n_steps, 1,
                     total_ms / n_steps, "bf16", "long_generation", 1, L0 + n_blocks * shape.canvas,
                     steps_per_canvas=steps, canvas_ms=round(total_ms / n_blocks, 3), final_kv_len=final_len,
-                    roofline=None, cpu_baseline=None, wall_s_timed=round(t_wall, 3), **extra)
+                    roofline=roofline, cpu_baseline=cpu, wall_s_timed=round(t_wall, 3), **extra)
     print(json.dumps(out), flush=True)
     m.close()
 
