@@ -92,7 +92,7 @@ PMC_TRAFFIC = {
     },
     "attention": {
         "kernel": "attention_pipe_kernel<8>", "workload": "batch8_ragged_32k",
-        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "e18dfdd9162edf2e",
+        "source": "block_discrete_diffusion_amd/csrc/k_attn.hip", "sha": "c847875a1b63d4d7",
         "fetch_kib": 571288.7, "fetch_scale": 1048576.0 / 524315.2,
         "write_kib": 33826.4, "write_scale": 1048576.0 / 1048576.0,
     },

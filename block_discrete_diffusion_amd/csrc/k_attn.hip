@@ -336,7 +336,8 @@ void attention_kernel(AttnArgs a) {
 //  * one 32 x 32 MFMA does the work of two 16 x 16 x 32 ones but holds the SIMD's issue for
 //    about as long as one of them (measured on gfx950: each MFMA blocks vector issue for ~11
 //    cycles, whatever its size), which leaves more issue cycles to the softmax's vector work
-//    (an exponential and half a pack per score): 17 MFMAs per 32-key half instead of 34;
+//    (an exponential and half a pack per score): 17 MFMAs per 32-key half (one of them the
+//    offset below), where the 16 x 16 x 32 kernel issues 34;
 //  * the scores leave the MFMAs ready for the exponential: the queries are multiplied by
 //    scale * log2 e once (and rounded to bf16 again), and each QK^T chain starts with one more
 //    MFMA that adds the query's exponent offset -m_ref (a ones column of K times an offset row of
@@ -355,7 +356,7 @@ void attention_kernel(AttnArgs a) {
 //    c ^ swz_v(row) (V), below, which keeps the 16-byte K fragment reads and the transposing
 //    8-byte V reads free of bank conflicts;
 //  * lazy rescaling: the exponent reference of a query only moves when the block maximum
-//    exceeds it by more than kLazy (log2 units), so P stays below 2^kLazy and O and its row
+//    exceeds it by more than kLazy (log2 units), so P stays below about 2^kLazy and O and its row
 //    sum are rescaled a handful of times per range instead of whenever the maximum grows; the
 //    result is unchanged (O and the row sum share the reference, which cancels);
 //  * the work-groups that share one (request, KV head, split) range are numbered so that they
