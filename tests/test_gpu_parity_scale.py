@@ -261,12 +261,15 @@ def test_long_causal_prefill(chunk):
         m.close()
 
 
-def test_causal_prefill_chunk_over_a_long_cache():
+@pytest.mark.parametrize("sawtooth", [False, True])
+def test_causal_prefill_chunk_over_a_long_cache(sawtooth):
     """A 2048-row causal prefill chunk over 8000 cached positions (N(0,1) bf16 K/V) at head dim
     128: its attention runs on the long-range pipelined kernel, causal, with per-request splits
     (a split past a work-group's last query is empty).  Two layers with every expert active
     (top-k = E, so no router tie can move a row); layer 1's K/V of the chunk depend on layer 0's
-    attention and must equal the oracle's prefill of the chunk over the same cache."""
+    attention and must equal the oracle's prefill of the chunk over the same cache.  With
+    `sawtooth` the cached keys are scaled by 0.05 -> 3 over each 1024 positions, so that the
+    exponent reference of the causal kernel moves inside its splits as well."""
     dg = need_gpu()
     shape = dataclasses.replace(synth.MID_LAYER, n_layers=2, n_experts=4, top_k=4, vocab=1024)
     w = synth.model_weights(shape, SEED + 9)
@@ -274,6 +277,9 @@ def test_causal_prefill_chunk_over_a_long_cache():
     m = dg.Model(shape, w, max_batch=1, max_prefill_rows=n)
     try:
         k, v = random_cache(shape, L0, L0 + n + 256, SEED + 10)
+        if sawtooth:
+            ramp = (0.05 + 2.95 * ((np.arange(L0) % 1024) / 1023.0)).astype(np.float32)
+            k[:, :, :, :L0] = synth.bf16_round(k[:, :, :, :L0] * ramp[None, None, None, :, None])
         kv = dg.KV(shape, 1, L0 + n + 256, fill=None)
         load_cache(kv, k, v, [L0])
         toks = synth.tokens(n, shape.vocab, SEED, 501)
